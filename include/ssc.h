@@ -1,0 +1,168 @@
+/*
+ * ssc.h -- single-pass scan, stream compaction and stable partition on
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The method: evaluate a predicate on every element (a 0/1 flag), take the
+ * exclusive scan of the flags, and scatter every survivor x[i] to
+ * out[rank[i]]. Input order is kept, the survivor count is the top of the
+ * scan, and a stable partition addresses its second half with i - rank[i]
+ * from the same scan ("Day 33 compaction.cu", header comment and
+ * scatterCompact / scatterPartition). The scan runs in one pass over the
+ * input with per-tile descriptors and a decoupled look-back over earlier
+ * tiles, tile numbers being taken from an atomic counter ("CUDA Handbook
+ * ch. 13, Stream Compaction", Listings 13-17 and 13-18).
+ *
+ * Conventions shared by every call:
+ *   - All array, count and scratch pointers are DEVICE pointers (hipMalloc
+ *     or equivalent) owned by the caller. The library never allocates and
+ *     never frees.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); it
+ *     must belong to the current device. Calls only enqueue work on it and
+ *     never synchronise; counts and totals stay in device memory.
+ *   - Scratch: a caller-provided device buffer of at least
+ *     ssc_scratch_bytes(n) bytes (ssc_radix_sort_scratch_bytes(n) for the
+ *     sort), 8-byte aligned. The library clears what it needs on `stream`
+ *     at the start of each call. One scratch buffer must not serve two calls
+ *     that may run at the same time. After a call completes, 32-bit word 1
+ *     of the scratch (word 64 for the sort) is 1 if a look-back wait gave up
+ *     after its bounded spin (results then invalid), else 0; nothing else in
+ *     it is meaningful to the caller.
+ *   - Element pointers must be 4-byte aligned. 16-byte aligned arrays take
+ *     the 128-bit load/store path; other arrays take a 32-bit path with the
+ *     same results.
+ *   - Sizes: n is an element count, 0 <= n <= INT32_MAX (ranks and counts are
+ *     int32). n == 0 writes 0 to `count` / `total` and returns SSC_OK; array
+ *     pointers may then be NULL (count/total may not be, where required).
+ *   - Errors: every call returns an ssc_status; arguments are checked before
+ *     anything is enqueued, and on an argument error nothing is enqueued. A
+ *     failed launch gives SSC_ERR_HIP (ssc_last_hip_error() has the code).
+ *     The library never exits or aborts.
+ *   - Only the elements out[0 .. count) of a compaction are written; the rest
+ *     of `out` is left as it was.
+ */
+#ifndef SSC_H
+#define SSC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssc_status {
+    SSC_OK = 0,
+    SSC_ERR_ARG = 1,     /* null pointer, n < 0, bad predicate or predicate argument, misalignment */
+    SSC_ERR_SIZE = 2,    /* n > INT32_MAX */
+    SSC_ERR_ALIAS = 3,   /* buffers overlap where they must not */
+    SSC_ERR_SCRATCH = 4, /* scratch too small or not 8-byte aligned */
+    SSC_ERR_HIP = 5,     /* a HIP call or kernel launch failed */
+    SSC_ERR_DEVICE = 6   /* current device is not gfx950 with 64-wide wavefronts */
+} ssc_status;
+
+/* Predicate kinds. pa/pb are ignored where not listed.
+ *   NONZERO    x != 0              zero removal ("Day 33 compaction.cu", markNonZero)
+ *   ODD        (x & 1) == 1        ("CUDA Handbook ch. 13", Listing 13-17, isOdd)
+ *   EVEN       (x & 1) == 0        ("Day 33 compaction.cu", markEven)
+ *   BIT_SET    bit pa of x is 1    0 <= pa <= 31 (one split of an LSD radix sort,
+ *   BIT_CLEAR  bit pa of x is 0      "CIS 565 Project 2: Stream Compaction")
+ *   MOD_LT     r < pb where r is the non-negative residue of x modulo pa, pa >= 1
+ * Bit tests use the two's-complement bits, so -3 is odd. */
+typedef enum ssc_pred {
+    SSC_PRED_NONZERO = 0,
+    SSC_PRED_ODD = 1,
+    SSC_PRED_EVEN = 2,
+    SSC_PRED_BIT_SET = 3,
+    SSC_PRED_BIT_CLEAR = 4,
+    SSC_PRED_MOD_LT = 5
+} ssc_pred;
+
+/* Elements per tile (one workgroup's share of the single pass). */
+int64_t ssc_tile_elems(void);
+
+/* Scratch bytes needed by the scan, compaction and partition calls for n
+ * elements: a tile counter plus one 8-byte descriptor per tile. */
+size_t ssc_scratch_bytes(int64_t n);
+
+/* Scratch bytes needed by ssc_radix_sort_u32 for n keys. */
+size_t ssc_radix_sort_scratch_bytes(int64_t n);
+
+/* Exclusive scan of int32 values: out[0] = 0, out[i] = in[0] + ... + in[i-1],
+ * with two's-complement wrap (sums taken modulo 2^32). `total` (nullable)
+ * receives the sum of all n values. out == in is allowed (in place); any
+ * other overlap of in/out/total is SSC_ERR_ALIAS.
+ * Source: "Day 32 scan_2.cu" (scanExclusiveCpu) and the exclusive
+ * convention of the "CIS 565 Project 2" transcript (0 13 50 ... for 13 37 15 ...). */
+int ssc_exclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
+                           void *scratch, size_t scratch_bytes, void *stream);
+
+/* Exclusive scan of fp32 values, accumulated in fp32 in a tiled order (not
+ * the sequential order): every output is within a relative error of about
+ * 1e-5 of the exactly accumulated prefix for the inputs this library is
+ * tested on (non-negative values, n up to 10^7). Aliasing rules as above. */
+int ssc_exclusive_scan_f32(const float *in, float *out, int64_t n, float *total,
+                           void *scratch, size_t scratch_bytes, void *stream);
+
+/* Order-preserving compaction: out[0 .. count) = the elements x with P(x)
+ * true, in input order; *count = their number (the top of the scan of the
+ * flags). `ranks` (nullable) receives the exclusive scan of the flags for
+ * every i: the output slot of in[i] when it survives. No overlap between
+ * in, out, count and ranks is allowed.
+ * Source: "Day 33 compaction.cu" (compactCpu, scatterCompact) and
+ * "CUDA Handbook ch. 13" (Listing 13-17: survivors scattered to
+ * base + index within the tile; the last tile writes the total). */
+int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
+                    int32_t pb, int32_t *count, int32_t *ranks, void *scratch,
+                    size_t scratch_bytes, void *stream);
+
+/* Stable partition: out[0 .. K) = the elements with P true, out[K .. n) =
+ * the elements with P false, both in input order; *count = K. Kept x[i]
+ * goes to out[rank[i]], rejected x[i] to out[K + i - rank[i]], where rank
+ * is the exclusive scan of the flags. K is counted first by a reduction
+ * pass over the input (written to *count), then one single pass scans and
+ * scatters. No overlap between in, out and count is allowed.
+ * Source: "Day 33 compaction.cu" (partitionCpu, scatterPartition). */
+int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
+                      int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
+                      void *stream);
+
+/* *count = number of elements with P true (a reduction of the flags). */
+int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t pb,
+                     int32_t *count, void *stream);
+
+/* Unordered compaction by atomic counter, kept only for comparison:
+ * out[0 .. count) holds the same multiset as ssc_compact_i32's output, in
+ * an order the hardware scheduler decides. variant 0: one atomicAdd per
+ * 64-lane wavefront and 1024-element chunk; variant 1: one atomicAdd per
+ * survivor (the form of "Day 33 compaction.cu", compactAtomic). *count is
+ * cleared and used as the counter. No overlap between in, out and count. */
+int ssc_compact_atomic_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
+                           int32_t pb, int32_t *count, int variant, void *stream);
+
+/* LSD radix sort of uint32 keys as 32 chained stable 1-bit partitions,
+ * pass b keeping keys whose bit b is clear first (bit 0 first), leaving
+ * out[] ascending. One counting pass over the input gives the size of the
+ * first half for every bit at once (a permutation does not change how many
+ * keys have bit b clear). tmp is n words of caller workspace; in is not
+ * modified. out == in is allowed; tmp must not overlap in or out.
+ * Source: "CIS 565 Project 2: Stream Compaction" (radix sort built on the
+ * compaction primitives, checked against std::sort). */
+int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t n,
+                       void *scratch, size_t scratch_bytes, void *stream);
+
+/* out[i] = in[i]: the copy kernel with the same tile and load/store width as
+ * the single pass, the practical bandwidth ceiling ("Day 33 compaction.cu",
+ * copyInts; "Day 32 scan_2.cu", copyFloats). No overlap allowed. */
+int ssc_copy_i32(const int32_t *in, int32_t *out, int64_t n, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *ssc_status_str(int status);
+
+/* The hipError_t of the last SSC_ERR_HIP on the calling thread (0 if none). */
+int ssc_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSC_H */

@@ -1,1 +1,237 @@
-"""MI355X-native single-pass scan, stream compaction and stable partition."""
+"""MI355X-native single-pass scan, stream compaction and stable partition.
+
+A thin ctypes binding over ``libssc.so`` (the C ABI in ``include/ssc.h``).
+This module only marshals arguments: every step of the computation runs in
+the library's HIP kernels. PyTorch provides device memory and the current
+stream. There is no CPU fallback: if the library is missing or the device is
+not a gfx950 GPU, the calls raise.
+
+Names follow the pages' vocabulary: predicate flags, exclusive scan, rank,
+count (the top of the scan), compact, partition.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssc.so")
+
+PRED = {"nonzero": 0, "odd": 1, "even": 2, "bit_set": 3, "bit_clear": 4, "mod_lt": 5}
+STATUS = {0: "SSC_OK", 1: "SSC_ERR_ARG", 2: "SSC_ERR_SIZE", 3: "SSC_ERR_ALIAS",
+          4: "SSC_ERR_SCRATCH", 5: "SSC_ERR_HIP", 6: "SSC_ERR_DEVICE"}
+
+# Every symbol include/ssc.h declares, with (restype, argtypes).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "ssc_tile_elems": (_I64, []),
+    "ssc_scratch_bytes": (_SZ, [_I64]),
+    "ssc_radix_sort_scratch_bytes": (_SZ, [_I64]),
+    "ssc_exclusive_scan_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_exclusive_scan_f32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_compact_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "ssc_partition_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
+    "ssc_count_if_i32": (_INT, [_P, _I64, _INT, _I32, _I32, _P, _P]),
+    "ssc_compact_atomic_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _INT, _P]),
+    "ssc_radix_sort_u32": (_INT, [_P, _P, _P, _I64, _P, _SZ, _P]),
+    "ssc_copy_i32": (_INT, [_P, _P, _I64, _P]),
+    "ssc_status_str": (ctypes.c_char_p, [_INT]),
+    "ssc_last_hip_error": (_INT, []),
+}
+
+
+class SSCError(RuntimeError):
+    def __init__(self, call: str, status: int, detail: str):
+        super().__init__(f"{call} failed: {STATUS.get(status, status)} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssc.so (built in-tree by ``python -m scan_stream_compaction_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m scan_stream_compaction_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(call: str, rc: int) -> None:
+    if rc != 0:
+        L = lib()
+        detail = L.ssc_status_str(rc).decode()
+        if rc == 5:
+            detail += f", hipError {L.ssc_last_hip_error()}"
+        raise SSCError(call, rc, detail)
+
+
+def _pred(p) -> int:
+    return PRED[p] if isinstance(p, str) else int(p)
+
+
+def _dev(t: torch.Tensor) -> None:
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU (no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def tile_elems() -> int:
+    return int(lib().ssc_tile_elems())
+
+
+def scratch_bytes(n: int) -> int:
+    return int(lib().ssc_scratch_bytes(n))
+
+
+def radix_sort_scratch_bytes(n: int) -> int:
+    return int(lib().ssc_radix_sort_scratch_bytes(n))
+
+
+def new_scratch(n: int, device, radix: bool = False) -> torch.Tensor:
+    nbytes = radix_sort_scratch_bytes(n) if radix else scratch_bytes(n)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def exclusive_scan(x: torch.Tensor, out: torch.Tensor | None = None,
+                   total: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """(out, total): exclusive scan of int32 (wrapping) or float32 values."""
+    _dev(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if total is None:
+        total = torch.empty(1, dtype=x.dtype, device=x.device)
+    if scratch is None:
+        scratch = new_scratch(x.numel(), x.device)
+    fn = {torch.int32: ("ssc_exclusive_scan_i32", lib().ssc_exclusive_scan_i32),
+          torch.float32: ("ssc_exclusive_scan_f32", lib().ssc_exclusive_scan_f32)}.get(x.dtype)
+    if fn is None or out.dtype != x.dtype or total.dtype != x.dtype:
+        raise TypeError("exclusive_scan takes int32 or float32 tensors of one dtype")
+    _dev(out)
+    _check(fn[0], fn[1](x.data_ptr(), out.data_ptr(), x.numel(), _ptr(total), scratch.data_ptr(),
+                        scratch.numel(), _stream(x)))
+    return out, total
+
+
+def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+            out: torch.Tensor | None = None, count: torch.Tensor | None = None,
+            ranks=False, scratch: torch.Tensor | None = None):
+    """(out, count[, ranks]): order-preserving compaction of int32 values.
+
+    out[:count] holds the survivors; entries past count are not written.
+    ranks=True (or a tensor) also returns the exclusive scan of the flags.
+    """
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("compact takes int32")
+    n = x.numel()
+    if out is None:
+        out = torch.empty_like(x)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    rk = None
+    if ranks is True:
+        rk = torch.empty_like(x)
+    elif isinstance(ranks, torch.Tensor):
+        rk = ranks
+    if scratch is None:
+        scratch = new_scratch(n, x.device)
+    _check("ssc_compact_i32", lib().ssc_compact_i32(
+        x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), _ptr(rk),
+        scratch.data_ptr(), scratch.numel(), _stream(x)))
+    return (out, count, rk) if rk is not None else (out, count)
+
+
+def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,
+              out: torch.Tensor | None = None, count: torch.Tensor | None = None,
+              scratch: torch.Tensor | None = None):
+    """(out, count): stable partition, predicate-true elements first; count = K."""
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("partition takes int32")
+    n = x.numel()
+    if out is None:
+        out = torch.empty_like(x)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if scratch is None:
+        scratch = new_scratch(n, x.device)
+    _check("ssc_partition_i32", lib().ssc_partition_i32(
+        x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
+        scratch.data_ptr(), scratch.numel(), _stream(x)))
+    return out, count
+
+
+def count_if(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+             count: torch.Tensor | None = None) -> torch.Tensor:
+    _dev(x)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    _check("ssc_count_if_i32", lib().ssc_count_if_i32(
+        x.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(), _stream(x)))
+    return count
+
+
+def compact_atomic(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+                   variant: int = 0, out: torch.Tensor | None = None,
+                   count: torch.Tensor | None = None):
+    """(out, count): unordered compaction by atomic counter (comparison only)."""
+    _dev(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    _check("ssc_compact_atomic_i32", lib().ssc_compact_atomic_i32(
+        x.data_ptr(), out.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(),
+        variant, _stream(x)))
+    return out, count
+
+
+def radix_sort(x: torch.Tensor, *, out: torch.Tensor | None = None,
+               tmp: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """Ascending sort of 32-bit keys taken as unsigned (int32 storage)."""
+    _dev(x)
+    n = x.numel()
+    if out is None:
+        out = torch.empty_like(x)
+    if tmp is None:
+        tmp = torch.empty_like(x)
+    if scratch is None:
+        scratch = new_scratch(n, x.device, radix=True)
+    _check("ssc_radix_sort_u32", lib().ssc_radix_sort_u32(
+        x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, scratch.data_ptr(), scratch.numel(),
+        _stream(x)))
+    return out
+
+
+def copy(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    _dev(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _check("ssc_copy_i32", lib().ssc_copy_i32(x.data_ptr(), out.data_ptr(), x.numel(),
+                                              _stream(x)))
+    return out

@@ -1,0 +1,184 @@
+// Device-side building blocks for the single-pass kernels on gfx950 (CDNA4):
+// wave64 lane helpers, ballot/mbcnt ranks, DPP wave scans, predicates, the
+// packed tile descriptor and the decoupled look-back.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssc {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- lanes ---
+
+__device__ __forceinline__ int lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+__device__ __forceinline__ uint32_t uniform(uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(x)));
+}
+
+// ------------------------------------------------------------ value ops ---
+// Sum over uint32 (wraps modulo 2^32, which also serves int32 scans) and
+// over fp32. `bits`/`from_bits` move values through 32-bit descriptors.
+
+struct SumU32 {
+    using T = uint32_t;
+    __device__ static T zero() { return 0u; }
+    __device__ static T add(T a, T b) { return a + b; }
+    __device__ static uint32_t bits(T a) { return a; }
+    __device__ static T from_bits(uint32_t b) { return b; }
+};
+
+struct SumF32 {
+    using T = float;
+    __device__ static T zero() { return 0.0f; }
+    __device__ static T add(T a, T b) { return a + b; }
+    __device__ static uint32_t bits(T a) { return __float_as_uint(a); }
+    __device__ static T from_bits(uint32_t b) { return __uint_as_float(b); }
+};
+
+// DPP move with the identity (all-zero bits) written where the source lane
+// is outside the pattern or the row is masked off.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive scan across the 64 lanes of a wavefront: a Hillis-Steele scan
+// inside each 16-lane row (row_shr 1, 2, 4, 8), then row 15's total is carried
+// into the next row (row_bcast:15) and lane 31's into rows 2-3 (row_bcast:31).
+template <class Op>
+__device__ __forceinline__ typename Op::T wave_inclusive_scan(typename Op::T v) {
+    uint32_t x = Op::bits(v);
+    x = Op::bits(Op::add(Op::from_bits(x), Op::from_bits(dpp_move<0x111, 0xf>(x))));
+    x = Op::bits(Op::add(Op::from_bits(x), Op::from_bits(dpp_move<0x112, 0xf>(x))));
+    x = Op::bits(Op::add(Op::from_bits(x), Op::from_bits(dpp_move<0x114, 0xf>(x))));
+    x = Op::bits(Op::add(Op::from_bits(x), Op::from_bits(dpp_move<0x118, 0xf>(x))));
+    x = Op::bits(Op::add(Op::from_bits(x), Op::from_bits(dpp_move<0x142, 0xa>(x))));
+    x = Op::bits(Op::add(Op::from_bits(x), Op::from_bits(dpp_move<0x143, 0xc>(x))));
+    return Op::from_bits(x);
+}
+
+// Sum over all 64 lanes, result in every lane (butterfly through ds_swizzle-free
+// lane shuffles; used only on the look-back path).
+template <class Op>
+__device__ __forceinline__ typename Op::T wave_sum(typename Op::T v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = Op::add(v, __shfl_xor(v, off));
+    return v;
+}
+
+// ----------------------------------------------------------- predicates ---
+// Numbering matches ssc_pred in ssc.h.
+
+template <int P>
+__device__ __forceinline__ bool pred_eval(int32_t x, int32_t pa, int32_t pb) {
+    const uint32_t u = static_cast<uint32_t>(x);
+    if constexpr (P == 0) {
+        return x != 0;
+    } else if constexpr (P == 1) {
+        return (u & 1u) != 0u;
+    } else if constexpr (P == 2) {
+        return (u & 1u) == 0u;
+    } else if constexpr (P == 3) {
+        return ((u >> pa) & 1u) != 0u;
+    } else if constexpr (P == 4) {
+        return ((u >> pa) & 1u) == 0u;
+    } else {
+        // Non-negative residue: C's % truncates toward zero, so a negative
+        // remainder is moved up by the modulus (pa >= 1, no overflow).
+        int32_t r = x % pa;
+        if (r < 0) r += pa;
+        return r < pb;
+    }
+}
+
+// ------------------------------------------------------ tile descriptors ---
+// One 64-bit word per tile: status in the high half, a 32-bit value (count,
+// int sum or fp32 bits) in the low half, written and read as a single
+// agent-scope atomic so status and value always travel together. All-zero
+// is "no information yet", which is what clearing the scratch produces.
+
+constexpr uint32_t kStatusNone = 0;       // nothing published
+constexpr uint32_t kStatusAggregate = 1;  // value = this tile's own total
+constexpr uint32_t kStatusInclusive = 2;  // value = total of tiles 0..t
+
+__device__ __forceinline__ void publish(uint64_t *desc, uint32_t status, uint32_t value) {
+    const uint64_t word = (static_cast<uint64_t>(status) << 32) | value;
+    __hip_atomic_store(desc, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t peek(uint64_t *desc) {
+    return __hip_atomic_load(desc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t claim_tile(uint32_t *counter) {
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Decoupled look-back, run by one whole wavefront of the tile's workgroup.
+// Reads the descriptors of the 64 tiles just below `tile` at once; while any
+// of them has published nothing it sleeps and reads again. Once all 64 have
+// published, the nearest inclusive one ends the walk: the result is its value
+// plus the aggregates above it. With no inclusive value in the window all 64
+// aggregates are added and the window moves 64 tiles down. Tiles below 0
+// count as inclusive with value 0. Returns the exclusive prefix of `tile`
+// (the total of tiles 0..tile-1) in every lane.
+//
+// Forward progress: a tile only waits on lower-numbered tiles, whose numbers
+// were claimed earlier by workgroups that are already running, and tile 0
+// never waits.
+//
+// The wait is bounded: after kSpinLimit re-reads without progress (seconds,
+// far beyond any legitimate wait) the walk stops, *timed_out is set to 1 and
+// the partial prefix is returned, so a fault elsewhere can corrupt results
+// but can never leave the kernel spinning.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+template <class Op>
+__device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t *timed_out) {
+    using T = typename Op::T;
+    const int lane = lane_id();
+    T prefix = Op::zero();
+    int64_t end = static_cast<int64_t>(tile);
+    uint32_t spins = 0;
+    while (true) {
+        const int64_t idx = end - kWave + lane;
+        uint64_t word;
+        while (true) {
+            word = idx >= 0 ? peek(desc + idx)
+                            : (static_cast<uint64_t>(kStatusInclusive) << 32);
+            const bool ready = (word >> 32) != kStatusNone;
+            if (ballot(!ready) == 0) break;
+            if (++spins > kSpinLimit) {
+                if (lane == 0)
+                    __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return prefix;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const uint64_t inclusive = ballot((word >> 32) == kStatusInclusive);
+        const T value = Op::from_bits(static_cast<uint32_t>(word));
+        if (inclusive != 0) {
+            const int top = 63 - __builtin_clzll(inclusive);
+            prefix = Op::add(prefix, wave_sum<Op>(lane >= top ? value : Op::zero()));
+            return prefix;
+        }
+        prefix = Op::add(prefix, wave_sum<Op>(value));
+        end -= kWave;
+    }
+}
+
+}  // namespace ssc

@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI, runnable without a GPU.
+
+The library must load and export every function include/ssc.h declares, the
+enum numbering must agree with the oracle's and the binding's, and every
+argument error must be reported before the library touches HIP. The pointer
+values used here are never dereferenced: each call is rejected by the argument
+checks that run before anything is enqueued.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import scan_stream_compaction_amd as ssc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssc.h")
+
+OK, ARG, SIZE, ALIAS, SCRATCH, HIP, DEVICE = range(7)
+INT32_MAX = 2**31 - 1
+
+# Fake, never-dereferenced device addresses, 256-byte aligned and far apart.
+A = 0x7F0000000000
+B = 0x7F1000000000
+C = 0x7F2000000000
+S = 0x7F3000000000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(ssc_[a-z0-9_]+)\s*\(", text))
+
+
+def _enum(name):
+    text = open(HEADER).read()
+    body = re.search(r"typedef enum %s \{(.*?)\}" % name, text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return {k: int(v) for k, v in re.findall(r"(\w+)\s*=\s*(\d+)", body)}
+
+
+def test_library_exports_every_declared_symbol():
+    L = ssc.lib()
+    declared = _declared()
+    assert declared == set(ssc.SIGNATURES), declared ^ set(ssc.SIGNATURES)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_enum_numbering_agrees_with_oracle_and_binding():
+    preds = _enum("ssc_pred")
+    assert preds == {"SSC_PRED_NONZERO": 0, "SSC_PRED_ODD": 1, "SSC_PRED_EVEN": 2,
+                     "SSC_PRED_BIT_SET": 3, "SSC_PRED_BIT_CLEAR": 4, "SSC_PRED_MOD_LT": 5}
+    for k, v in preds.items():
+        assert ssc.PRED[k[len("SSC_PRED_"):].lower()] == v
+        assert oracle.lib().orc_pred_id(v) == v
+    assert (oracle.PRED_NONZERO, oracle.PRED_ODD, oracle.PRED_EVEN, oracle.PRED_BIT_SET,
+            oracle.PRED_BIT_CLEAR, oracle.PRED_MOD_LT) == tuple(range(6))
+    st = _enum("ssc_status")
+    assert {v: k for k, v in st.items()} == ssc.STATUS
+
+
+def test_tile_and_scratch_sizes():
+    L = ssc.lib()
+    T = L.ssc_tile_elems()
+    assert T == 4096
+    for n in (0, 1, T - 1, T, T + 1, 2**28, INT32_MAX):
+        tiles = (n + T - 1) // T
+        assert L.ssc_scratch_bytes(n) == 256 + 8 * tiles
+        assert L.ssc_radix_sort_scratch_bytes(n) == 512 + 32 * 8 * tiles
+    assert L.ssc_scratch_bytes(-5) == 256
+
+
+def test_status_strings():
+    L = ssc.lib()
+    for s in range(7):
+        assert L.ssc_status_str(s)
+    assert L.ssc_status_str(99) == b"unknown status"
+    assert L.ssc_last_hip_error() == 0
+
+
+def _compact(**kw):
+    a = dict(inp=A, out=B, n=1000, pred=1, pa=0, pb=0, count=C, ranks=None, scratch=S,
+             sbytes=1 << 20, stream=None)
+    a.update(kw)
+    return ssc.lib().ssc_compact_i32(a["inp"], a["out"], a["n"], a["pred"], a["pa"], a["pb"],
+                                     a["count"], a["ranks"], a["scratch"], a["sbytes"],
+                                     a["stream"])
+
+
+def test_compact_argument_errors():
+    assert _compact(inp=None) == ARG
+    assert _compact(out=None) == ARG
+    assert _compact(count=None) == ARG
+    assert _compact(n=-1) == ARG
+    assert _compact(n=INT32_MAX + 1) == SIZE
+    assert _compact(pred=6) == ARG
+    assert _compact(pred=-1) == ARG
+    assert _compact(pred=3, pa=32) == ARG
+    assert _compact(pred=4, pa=-1) == ARG
+    assert _compact(pred=5, pa=0) == ARG
+    assert _compact(inp=A + 2) == ARG          # not 4-byte aligned
+    assert _compact(count=C + 1) == ARG
+    assert _compact(out=A + 400) == ALIAS      # out overlaps in
+    assert _compact(count=A + 4) == ALIAS
+    assert _compact(ranks=B + 8) == ALIAS
+    assert _compact(scratch=None) == SCRATCH
+    assert _compact(scratch=S + 4) == SCRATCH  # not 8-byte aligned
+    assert _compact(sbytes=255) == SCRATCH
+    assert _compact(n=5000, sbytes=256 + 8) == SCRATCH  # needs two descriptors
+    assert _compact(scratch=A) == ALIAS
+
+
+def test_scan_partition_atomic_sort_copy_argument_errors():
+    L = ssc.lib()
+    big = 1 << 20
+    # scan: exact in-place is legal (checked later on the GPU); partial overlap is not
+    assert L.ssc_exclusive_scan_i32(A, A + 4, 100, None, S, big, None) == ALIAS
+    assert L.ssc_exclusive_scan_f32(A, B, 100, A + 8, S, big, None) == ALIAS
+    assert L.ssc_exclusive_scan_i32(None, B, 100, None, S, big, None) == ARG
+    assert L.ssc_exclusive_scan_i32(A, B, -3, None, S, big, None) == ARG
+    assert L.ssc_exclusive_scan_i32(A, B, INT32_MAX + 1, None, S, big, None) == SIZE
+    assert L.ssc_exclusive_scan_f32(A, B, 100, None, S, 100, None) == SCRATCH
+    assert L.ssc_exclusive_scan_f32(A, B + 2, 100, None, S, big, None) == ARG
+    # partition: in-place is not allowed
+    assert L.ssc_partition_i32(A, A, 100, 2, 0, 0, C, S, big, None) == ALIAS
+    assert L.ssc_partition_i32(A, B, 100, 9, 0, 0, C, S, big, None) == ARG
+    assert L.ssc_partition_i32(A, B, 100, 2, 0, 0, None, S, big, None) == ARG
+    assert L.ssc_partition_i32(A, B, 100, 2, 0, 0, C, S, 8, None) == SCRATCH
+    # count_if
+    assert L.ssc_count_if_i32(A, 100, 0, 0, 0, A + 8, None) == ALIAS
+    assert L.ssc_count_if_i32(A, 100, 5, 0, 0, C, None) == ARG
+    # atomic
+    assert L.ssc_compact_atomic_i32(A, B, 100, 1, 0, 0, C, 2, None) == ARG
+    assert L.ssc_compact_atomic_i32(A, A + 8, 100, 1, 0, 0, C, 0, None) == ALIAS
+    # radix sort: tmp must not overlap; scratch must hold 32 descriptor arrays
+    assert L.ssc_radix_sort_u32(A, B, B + 64, 100, S, big, None) == ALIAS
+    assert L.ssc_radix_sort_u32(A, B, C, 100, S, 512 + 8, None) == SCRATCH
+    assert L.ssc_radix_sort_u32(A, B, None, 100, S, big, None) == ARG
+    # copy
+    assert L.ssc_copy_i32(A, A + 4, 100, None) == ALIAS
+    assert L.ssc_copy_i32(A, B, -1, None) == ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(16, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        ssc.compact(x, "odd")
+    with pytest.raises(ValueError):
+        ssc.exclusive_scan(x)
