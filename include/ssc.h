@@ -20,13 +20,15 @@
  *     must belong to the current device. Calls only enqueue work on it and
  *     never synchronise; counts and totals stay in device memory.
  *   - Scratch: a caller-provided device buffer of at least
- *     ssc_scratch_bytes(n) bytes (ssc_radix_sort_scratch_bytes(n) for the
- *     sort), 8-byte aligned. The library clears what it needs on `stream`
- *     at the start of each call. One scratch buffer must not serve two calls
- *     that may run at the same time. After a call completes, 32-bit word 1
- *     of the scratch (word 64 for the sort) is 1 if a look-back wait gave up
- *     after its bounded spin (results then invalid), else 0; nothing else in
- *     it is meaningful to the caller.
+ *     ssc_scratch_bytes(n) bytes, 8-byte aligned, ZERO-FILLED BEFORE ITS
+ *     FIRST USE (ssc_scratch_init, or any memset to 0). The library keeps it
+ *     ready for the next call by itself: no clearing between calls, so a
+ *     call is a single kernel launch (two for a partition). Pass the same
+ *     scratch_bytes every time a buffer is used. One scratch buffer must not
+ *     serve two calls that may run at the same time (the calls race).
+ *     Diagnostic: after a call completes, 32-bit word 2 of the scratch is 1
+ *     if a look-back wait gave up after its bounded spin (results invalid;
+ *     only possible on misuse such as an uninitialised scratch).
  *   - Element pointers must be 4-byte aligned. 16-byte aligned arrays take
  *     the 128-bit load/store path; other arrays take a 32-bit path with the
  *     same results.
@@ -77,15 +79,20 @@ typedef enum ssc_pred {
     SSC_PRED_MOD_LT = 5
 } ssc_pred;
 
-/* Elements per tile (one workgroup's share of the single pass). */
+/* Elements per tile (one workgroup's share of the single pass, one tile
+ * number claimed from the atomic counter). */
 int64_t ssc_tile_elems(void);
 
-/* Scratch bytes needed by the scan, compaction and partition calls for n
- * elements: a tile counter plus one 8-byte descriptor per tile. */
+/* Scratch bytes needed by the scan, compaction, partition and counting calls
+ * for n elements: a 512-byte header (tile counter and epoch, counting-pass
+ * accumulators) plus one 8-byte descriptor per tile. */
 size_t ssc_scratch_bytes(int64_t n);
 
 /* Scratch bytes needed by ssc_radix_sort_u32 for n keys. */
 size_t ssc_radix_sort_scratch_bytes(int64_t n);
+
+/* Zero-fills a scratch buffer on `stream` (needed once, before first use). */
+int ssc_scratch_init(void *scratch, size_t scratch_bytes, void *stream);
 
 /* Exclusive scan of int32 values: out[0] = 0, out[i] = in[0] + ... + in[i-1],
  * with two's-complement wrap (sums taken modulo 2^32). `total` (nullable)
@@ -120,15 +127,16 @@ int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_
  * goes to out[rank[i]], rejected x[i] to out[K + i - rank[i]], where rank
  * is the exclusive scan of the flags. K is counted first by a reduction
  * pass over the input (written to *count), then one single pass scans and
- * scatters. No overlap between in, out and count is allowed.
+ * scatters: two launches. No overlap between in, out and count is allowed.
  * Source: "Day 33 compaction.cu" (partitionCpu, scatterPartition). */
 int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
                       int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
                       void *stream);
 
-/* *count = number of elements with P true (a reduction of the flags). */
+/* *count = number of elements with P true (a reduction of the flags; one
+ * launch). Needs a scratch buffer of at least ssc_scratch_bytes(0) bytes. */
 int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t pb,
-                     int32_t *count, void *stream);
+                     int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
 
 /* Unordered compaction by atomic counter, kept only for comparison:
  * out[0 .. count) holds the same multiset as ssc_compact_i32's output, in

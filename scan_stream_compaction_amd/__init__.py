@@ -33,11 +33,12 @@ SIGNATURES = {
     "ssc_tile_elems": (_I64, []),
     "ssc_scratch_bytes": (_SZ, [_I64]),
     "ssc_radix_sort_scratch_bytes": (_SZ, [_I64]),
+    "ssc_scratch_init": (_INT, [_P, _SZ, _P]),
     "ssc_exclusive_scan_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_exclusive_scan_f32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_compact_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "ssc_partition_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
-    "ssc_count_if_i32": (_INT, [_P, _I64, _INT, _I32, _I32, _P, _P]),
+    "ssc_count_if_i32": (_INT, [_P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
     "ssc_compact_atomic_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _INT, _P]),
     "ssc_radix_sort_u32": (_INT, [_P, _P, _P, _I64, _P, _SZ, _P]),
     "ssc_copy_i32": (_INT, [_P, _P, _I64, _P]),
@@ -113,8 +114,10 @@ def radix_sort_scratch_bytes(n: int) -> int:
 
 
 def new_scratch(n: int, device, radix: bool = False) -> torch.Tensor:
+    """A zero-filled scratch buffer for calls on up to n elements. The library
+    keeps it ready between calls; reuse it for calls on one stream."""
     nbytes = radix_sort_scratch_bytes(n) if radix else scratch_bytes(n)
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def exclusive_scan(x: torch.Tensor, out: torch.Tensor | None = None,
@@ -187,12 +190,16 @@ def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,
 
 
 def count_if(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
-             count: torch.Tensor | None = None) -> torch.Tensor:
+             count: torch.Tensor | None = None,
+             scratch: torch.Tensor | None = None) -> torch.Tensor:
     _dev(x)
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if scratch is None:
+        scratch = new_scratch(0, x.device)
     _check("ssc_count_if_i32", lib().ssc_count_if_i32(
-        x.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(), _stream(x)))
+        x.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(), scratch.data_ptr(),
+        scratch.numel(), _stream(x)))
     return count
 
 

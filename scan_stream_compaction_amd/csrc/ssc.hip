@@ -5,18 +5,27 @@
 // Stream Compaction", Listings 13-17/13-18): flag each element with a
 // predicate, exclusive-scan the flags, scatter survivors to out[rank]; the
 // count is the top of the scan, and a partition sends rejected x[i] to
-// out[K + i - rank[i]]. Here the whole path is one kernel launch over tiles
-// whose numbers come from an atomic counter, each tile finding the number of
+// out[K + i - rank[i]]. The whole path is one kernel launch over tiles whose
+// numbers come from an atomic counter; each tile finds the number of
 // survivors before it by a decoupled look-back over per-tile descriptors.
 //
-// Tile shape (MI355X-first, not the pages' 256- or 1024-thread blocks):
-// a 256-thread workgroup = 4 wavefronts of 64 lanes; each wavefront owns a
-// contiguous chunk of 64 * E elements and reads it with 128-bit loads, E/4
-// per lane, every load instruction covering 1 KiB of consecutive bytes.
-// Element order inside the chunk is (load j, lane, component k). Ranks inside
-// a wavefront come from ballot + mbcnt (no shared-memory tree), wave totals
-// meet in LDS, survivors are staged in LDS at their tile rank and leave as
-// one contiguous run of coalesced stores.
+// MI355X-first tile shape. A same-address device-scope atomic is serialised
+// across the 8 XCDs at roughly 11-12 ns, so the tile number is claimed once
+// per 32768 elements (128 KiB), not per few thousand: a 512-thread workgroup
+// (8 wavefronts of 64 lanes) holds its whole tile in registers, 64 elements
+// per lane from sixteen 128-bit loads. The tile is 4 sub-tiles of 8192; in
+// each sub-tile every wavefront owns 1024 consecutive elements read by four
+// 128-bit loads per lane, each load instruction covering 1 KiB of contiguous
+// bytes. Element order inside a wavefront chunk is (load j, lane, component
+// k). Ranks inside a wavefront come from ballot + mbcnt, wavefront totals
+// meet in LDS, and survivors are staged in LDS one sub-tile at a time (32
+// KiB) and leave as one contiguous run of coalesced stores per sub-tile.
+//
+// Scratch needs no clearing between calls: tile numbers and an epoch come
+// from one 64-bit atomic word {epoch:32 | next tile:32}; the workgroup that
+// claims the last tile resets the counter and advances the epoch, and
+// descriptors carry the epoch as a tag. The counting passes reset their own
+// accumulators (the last workgroup to finish does it).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -27,16 +36,27 @@
 namespace ssc {
 
 // ------------------------------------------------------------ tile shape ---
-constexpr int kBlock = 256;               // threads per workgroup
-constexpr int kWaves = kBlock / kWave;    // 4 wavefronts
-constexpr int kLoads = 4;                 // 128-bit loads per lane
-constexpr int kItems = 4 * kLoads;        // 16 elements per lane
-constexpr int kChunk = kWave * kItems;    // 1024 elements per wavefront
-constexpr int kTile = kBlock * kItems;    // 4096 elements per tile
-constexpr int kReduceGrid = 2048;         // workgroups of the grid-stride counting kernels
+constexpr int kBlock = 512;                    // threads per workgroup
+constexpr int kWaves = kBlock / kWave;         // 8 wavefronts
+constexpr int kLoads = 4;                      // 128-bit loads per lane per sub-tile
+constexpr int kChunk = kWave * kLoads * 4;     // 1024 elements per wavefront per sub-tile
+constexpr int kSub = kBlock * kLoads * 4;      // 8192 elements per sub-tile
+constexpr int kRounds = 4;                     // sub-tiles per tile
+constexpr int kTile = kSub * kRounds;          // 32768 elements per tile
+constexpr uint32_t kMaxTiles = 1u << 16;       // tiles of the largest n (INT32_MAX)
+constexpr int kReduceGrid = 512;               // workgroups of the grid-stride counting kernels
+constexpr int kSpread = 16;                    // accumulators a counting pass spreads over
 
-constexpr size_t kHeaderBytes = 256;       // tile counter, time-out flag
-constexpr size_t kRadixHeaderBytes = 512;  // 32 tile counters, 32 bit counts, time-out flag
+static_assert(static_cast<int64_t>(kMaxTiles) * kTile >= 2147483647LL, "kMaxTiles");
+
+// Scratch header (bytes). Descriptors follow it, one 64-bit word per tile.
+constexpr size_t kHeaderBytes = 512;
+constexpr size_t kOffClaim = 0;      // uint64 {epoch:32 | next tile:32}
+constexpr size_t kOffTimedOut = 8;   // uint32 look-back time-out flag
+constexpr size_t kOffDone = 12;      // uint32 workgroups finished (counting passes)
+constexpr size_t kOffAcc = 64;       // uint32[kSpread] partial counts
+constexpr size_t kOffAcc32 = 128;    // uint32[32] per-bit clear counts being summed
+constexpr size_t kOffKept32 = 256;   // uint32[32] per-bit clear counts of the current sort
 
 __host__ __device__ constexpr int64_t tiles_for(int64_t n) { return (n + kTile - 1) / kTile; }
 
@@ -54,12 +74,34 @@ __device__ __forceinline__ uint32_t to_u32(T v) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+struct ScratchView {
+    uint64_t *claim;
+    uint32_t *timed_out;
+    uint32_t *done;
+    uint32_t *acc;
+    uint32_t *acc32;
+    uint32_t *kept32;
+    uint64_t *desc;
+};
+
+__host__ __device__ inline ScratchView view(void *scratch) {
+    char *b = static_cast<char *>(scratch);
+    ScratchView v;
+    v.claim = reinterpret_cast<uint64_t *>(b + kOffClaim);
+    v.timed_out = reinterpret_cast<uint32_t *>(b + kOffTimedOut);
+    v.done = reinterpret_cast<uint32_t *>(b + kOffDone);
+    v.acc = reinterpret_cast<uint32_t *>(b + kOffAcc);
+    v.acc32 = reinterpret_cast<uint32_t *>(b + kOffAcc32);
+    v.kept32 = reinterpret_cast<uint32_t *>(b + kOffKept32);
+    v.desc = reinterpret_cast<uint64_t *>(b + kHeaderBytes);
+    return v;
+}
+
 // --------------------------------------------------------------- loading ---
-// Loads this lane's kItems elements of the chunk starting at `chunk`:
-// v[j][k] = in[chunk + j*256 + lane*4 + k]. `full` (uniform) says the whole
-// tile is in range; otherwise each element is checked against n and missing
-// ones read as 0 with valid = false. VEC selects 128-bit loads (the array is
-// 16-byte aligned) or 32-bit loads.
+// Loads one wavefront chunk: v[j][k] = in[chunk + j*256 + lane*4 + k].
+// `full` (uniform) says the whole tile is in range; otherwise every element is
+// checked against n and missing ones read as 0. VEC selects 128-bit accesses
+// (the array is 16-byte aligned) or 32-bit ones.
 template <bool VEC, class T>
 __device__ __forceinline__ void load_chunk(const T *__restrict__ in, int64_t chunk, int lane,
                                            int64_t n, bool full, T (&v)[kLoads][4]) {
@@ -119,122 +161,173 @@ __device__ __forceinline__ void store_chunk(T *out, int64_t chunk, int lane, int
     }
 }
 
-// Flags and wavefront-local ranks for one chunk. On return:
-//   f[j][k]   = element valid and predicate true,
-//   kb[j][k]  = number of flagged elements before (j, lane, k) in the chunk,
-// and the chunk's flag total is returned (uniform).
+// Flag of one element: in range and predicate true.
+template <int P>
+__device__ __forceinline__ bool flag_of(int32_t x, int64_t at, int64_t n, bool full, int32_t pa,
+                                        int32_t pb) {
+    return (full || at < n) && pred_eval<P>(x, pa, pb);
+}
+
+// Wavefront-local ranks of one chunk. lead[j] = flagged elements in earlier
+// loads of the chunk plus those of load j in lower lanes; the element's rank
+// inside the chunk is lead[j] + (flagged components before k in its lane).
+// Returns the chunk's flag total (uniform).
 template <int P>
 __device__ __forceinline__ uint32_t chunk_ranks(const int32_t (&v)[kLoads][4], int64_t chunk,
                                                 int lane, int64_t n, bool full, int32_t pa,
-                                                int32_t pb, bool (&f)[kLoads][4],
-                                                uint32_t (&kb)[kLoads][4]) {
-    uint32_t running = 0;  // flagged elements in earlier loads of this chunk (uniform)
+                                                int32_t pb, uint32_t (&lead)[kLoads]) {
+    uint32_t running = 0;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
         const int64_t at = chunk + j * (kWave * 4) + lane * 4;
-        uint64_t m[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            f[j][k] = (full || at + k < n) && pred_eval<P>(v[j][k], pa, pb);
-            m[k] = ballot(f[j][k]);
-        }
-        uint32_t below = 0;  // flagged elements of load j in lower lanes
+        uint32_t below = 0;
         uint32_t total = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            below += mbcnt64(m[k]);
-            total += static_cast<uint32_t>(__builtin_popcountll(m[k]));
+            const uint64_t m = ballot(flag_of<P>(v[j][k], at + k, n, full, pa, pb));
+            below += mbcnt64(m);
+            total += static_cast<uint32_t>(__builtin_popcountll(m));
         }
-        uint32_t in_lane = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            kb[j][k] = running + below + in_lane;
-            in_lane += f[j][k] ? 1u : 0u;
-        }
+        lead[j] = running + below;
         running += total;
     }
     return running;
 }
 
-// Sum of the wave totals below `w` and of all waves, after the barrier that
-// published them in LDS.
-__device__ __forceinline__ void wave_offsets(const uint32_t *s_tot, int w, uint32_t &below,
-                                             uint32_t &all) {
-    below = 0;
-    all = 0;
+// Exclusive prefixes over the (sub-tile, wavefront) chunk totals in LDS,
+// read after the barrier that published them: for every sub-tile q,
+// chunk_before[q] = total of chunks before (q, w) in tile order, and
+// sub_before[q] = total of sub-tiles before q; sub_before[kRounds] is the
+// tile aggregate.
+__device__ __forceinline__ void tile_prefixes(const uint32_t *s_tot, int w,
+                                              uint32_t (&chunk_before)[kRounds],
+                                              uint32_t (&sub_before)[kRounds + 1]) {
+    uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        const uint32_t t = s_tot[i];
-        below += (i < w) ? t : 0u;
-        all += t;
+    for (int q = 0; q < kRounds; ++q) {
+        sub_before[q] = acc;
+        uint32_t mine = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            const uint32_t t = s_tot[q * kWaves + i];
+            mine += (i < w) ? t : 0u;
+            acc += t;
+        }
+        chunk_before[q] = sub_before[q] + mine;
     }
+    sub_before[kRounds] = acc;
+}
+
+// Claims the next tile for this workgroup (thread 0 only). Returns
+// {epoch:32 | tile:32}. The claimer of the last tile resets the counter,
+// advances the epoch, and clears one stale descriptor slot: slot
+// (epoch mod kMaxTiles) when this call does not use it. Over any kMaxTiles
+// consecutive calls every slot is thus rewritten or cleared, far within the
+// 2^30-call period of the tag, so no stale descriptor can match a later tag.
+__device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t num_tiles,
+                                               uint32_t capacity) {
+    const uint64_t c =
+        __hip_atomic_fetch_add(sv.claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t tile = static_cast<uint32_t>(c);
+    const uint32_t epoch = static_cast<uint32_t>(c >> 32);
+    if (tile == num_tiles - 1) {
+        __hip_atomic_store(sv.claim, static_cast<uint64_t>(epoch + 1u) << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t slot = epoch & (kMaxTiles - 1u);
+        if (slot >= num_tiles && slot < capacity)
+            __hip_atomic_store(sv.desc + slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return c;
 }
 
 // ===================================================== compaction kernel ---
-// One launch, one tile per workgroup (tile number from the atomic counter).
-//   1. claim a tile, load it (128-bit loads), flag it, rank it per wavefront;
-//   2. wave totals in LDS -> tile aggregate A and each wavefront's offset;
-//   3. publish {aggregate, A} (tile 0 publishes {inclusive, A});
-//   4. stage survivors in LDS at their tile rank (partition: rejected ones
-//      after them at A + local index - rank) while wavefront 0 looks back;
-//   5. publish {inclusive, base + A}; barrier; stream the staged run(s) out.
+// One tile per workgroup, tile number from the atomic counter.
+//   1. claim a tile; issue all sixteen 128-bit loads; flag and rank each
+//      wavefront chunk (ballot + mbcnt); chunk totals to LDS;
+//   2. tile aggregate A and chunk offsets from LDS; publish {aggregate, A}
+//      (tile 0 publishes {inclusive, A});
+//   3. stage sub-tile 0 in LDS while wavefront 0 looks back; publish
+//      {inclusive, base + A};
+//   4. per sub-tile: stage (survivors at their rank; for a partition the
+//      rejected ones after them), barrier, stream the run(s) out, barrier.
 // PARTITION reads K from *kept_total (written by the counting pass).
 template <int P, bool VEC, bool PARTITION>
 __global__ __launch_bounds__(kBlock) void select_kernel(
     const int32_t *__restrict__ in, int32_t *__restrict__ out, int64_t n, int32_t pa,
-    int32_t pb, uint64_t *__restrict__ desc, uint32_t *__restrict__ tile_counter,
-    uint32_t *__restrict__ timed_out, uint32_t num_tiles, int32_t *__restrict__ count,
-    int32_t *__restrict__ ranks, const int32_t *__restrict__ kept_total) {
-    __shared__ int32_t s_stage[kTile];
-    __shared__ uint32_t s_tot[kWaves];
-    __shared__ uint32_t s_tile;
-    __shared__ uint32_t s_base;
+    int32_t pb, void *scratch, uint32_t num_tiles, uint32_t capacity,
+    int32_t *__restrict__ count, int32_t *__restrict__ ranks,
+    const int32_t *__restrict__ kept_total) {
+    __shared__ int32_t s_stage[kSub];
+    __shared__ uint32_t s_tot[kRounds * kWaves];
+    __shared__ uint32_t s_tile, s_tag, s_base;
 
-    if (threadIdx.x == 0) s_tile = claim_tile(tile_counter);
+    const ScratchView sv = view(scratch);
+    if (threadIdx.x == 0) {
+        const uint64_t c = claim_tile(sv, num_tiles, capacity);
+        s_tile = static_cast<uint32_t>(c);
+        s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
+    }
     __syncthreads();
     const uint32_t tile = s_tile;
-    if (tile >= num_tiles) return;  // only if the counter was not cleared
+    const uint32_t tag = s_tag;
+    if (tile >= num_tiles) return;  // only if the scratch was never initialised
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
-    const int64_t chunk = tile_start + static_cast<int64_t>(w) * kChunk;
     const bool full = tile_start + kTile <= n;
 
-    int32_t v[kLoads][4];
-    load_chunk<VEC>(in, chunk, lane, n, full, v);
+    int32_t v[kRounds][kLoads][4];
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q)
+        load_chunk<VEC>(in, tile_start + q * kSub + w * kChunk, lane, n, full, v[q]);
 
-    bool f[kLoads][4];
-    uint32_t kb[kLoads][4];
-    const uint32_t wave_total = chunk_ranks<P>(v, chunk, lane, n, full, pa, pb, f, kb);
-    if (lane == 0) s_tot[w] = wave_total;
+    uint32_t lead[kRounds][kLoads];
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+        const uint32_t t = chunk_ranks<P>(v[q], tile_start + q * kSub + w * kChunk, lane, n, full,
+                                          pa, pb, lead[q]);
+        if (lane == 0) s_tot[q * kWaves + w] = t;
+    }
     __syncthreads();
-    uint32_t wave_below, agg;
-    wave_offsets(s_tot, w, wave_below, agg);
+    uint32_t chunk_before[kRounds];
+    uint32_t sub_before[kRounds + 1];
+    tile_prefixes(s_tot, w, chunk_before, sub_before);
+    const uint32_t agg = sub_before[kRounds];
 
     if (threadIdx.x == 0)
-        publish(desc + tile, tile == 0 ? kStatusInclusive : kStatusAggregate, agg);
+        publish(sv.desc + tile, tag, tile == 0 ? kStatusInclusive : kStatusAggregate, agg);
 
-    // Stage: survivors at their tile rank; for a partition the rejected
-    // elements follow at A + (local index - rank).
+    // Stage sub-tile q in LDS: survivors at their rank inside the sub-tile,
+    // and for a partition the rejected elements after them at
+    // A_q + (index in sub-tile - rank in sub-tile).
+    auto stage = [&](int q) {
+        const int64_t chunk = tile_start + q * kSub + w * kChunk;
+        const uint32_t a_q = sub_before[q + 1] - sub_before[q];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+        for (int j = 0; j < kLoads; ++j) {
+            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+            uint32_t r = chunk_before[q] - sub_before[q] + lead[q][j];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t local = static_cast<uint32_t>(w * kChunk + j * (kWave * 4) + lane * 4 + k);
-            const uint32_t r = wave_below + kb[j][k];
-            if (f[j][k]) {
-                s_stage[r] = v[j][k];
-            } else if constexpr (PARTITION) {
-                if (full || tile_start + local < n) s_stage[agg + local - r] = v[j][k];
+            for (int k = 0; k < 4; ++k) {
+                const bool f = flag_of<P>(v[q][j][k], at + k, n, full, pa, pb);
+                if (f) {
+                    s_stage[r] = v[q][j][k];
+                } else if constexpr (PARTITION) {
+                    const uint32_t local =
+                        static_cast<uint32_t>(w * kChunk + j * (kWave * 4) + lane * 4 + k);
+                    if (full || at + k < n) s_stage[a_q + local - r] = v[q][j][k];
+                }
+                r += f ? 1u : 0u;
             }
         }
-    }
+    };
 
+    stage(0);
     if (w == 0) {
         uint32_t base = 0;
         if (tile != 0) {
-            base = look_back<SumU32>(desc, tile, timed_out);
-            if (lane == 0) publish(desc + tile, kStatusInclusive, base + agg);
+            base = look_back<SumU32>(sv.desc, tile, tag, sv.timed_out);
+            if (lane == 0) publish(sv.desc + tile, tag, kStatusInclusive, base + agg);
         }
         if (lane == 0) {
             s_base = base;
@@ -243,102 +336,141 @@ __global__ __launch_bounds__(kBlock) void select_kernel(
     }
     __syncthreads();
     const uint32_t base = s_base;
+    const uint32_t kept = PARTITION ? static_cast<uint32_t>(*kept_total) : 0u;
+
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q) {
+        if (q > 0) {
+            stage(q);
+            __syncthreads();
+        }
+        const uint32_t a_q = sub_before[q + 1] - sub_before[q];
+        const uint32_t kept_base = base + sub_before[q];  // survivors before this sub-tile
+        if constexpr (!PARTITION) {
+            // Range-checked: a correct look-back never trips it; a broken one
+            // gives wrong results instead of stray writes.
+            for (uint32_t i = threadIdx.x; i < a_q; i += kBlock)
+                if (kept_base + i < n) out[kept_base + i] = s_stage[i];
+        } else {
+            const int64_t sub_start = tile_start + q * kSub;
+            const int64_t left = n - sub_start;
+            const uint32_t len =
+                left >= kSub ? static_cast<uint32_t>(kSub) : (left > 0 ? static_cast<uint32_t>(left) : 0u);
+            // rejected elements before this sub-tile = sub_start - kept_base
+            const uint32_t rej_base = kept + static_cast<uint32_t>(sub_start) - kept_base - a_q;
+            for (uint32_t i = threadIdx.x; i < len; i += kBlock) {
+                const uint32_t dst = (i < a_q ? kept_base : rej_base) + i;
+                if (dst < n) out[dst] = s_stage[i];
+            }
+        }
+        __syncthreads();
+    }
 
     if constexpr (!PARTITION) {
-        // Range-checked: a correct look-back never trips it; a broken one
-        // gives wrong results instead of stray writes.
-        for (uint32_t i = threadIdx.x; i < agg; i += kBlock)
-            if (base + i < n) out[base + i] = s_stage[i];
         if (ranks != nullptr) {
-            int32_t rk[kLoads][4];
 #pragma unroll
-            for (int j = 0; j < kLoads; ++j)
+            for (int q = 0; q < kRounds; ++q) {
+                const int64_t chunk = tile_start + q * kSub + w * kChunk;
+                int32_t rk[kLoads][4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    rk[j][k] = static_cast<int32_t>(base + wave_below + kb[j][k]);
-            store_chunk<VEC>(ranks, chunk, lane, n, full, rk);
-        }
-    } else {
-        const uint32_t kept = static_cast<uint32_t>(*kept_total);
-        const uint32_t len = full ? kTile : static_cast<uint32_t>(n - tile_start);
-        // rejected elements before this tile = tile_start - base
-        const uint32_t rej_base = kept + static_cast<uint32_t>(tile_start) - base - agg;
-        for (uint32_t i = threadIdx.x; i < len; i += kBlock) {
-            const uint32_t dst = (i < agg ? base : rej_base) + i;
-            if (dst < n) out[dst] = s_stage[i];
+                for (int j = 0; j < kLoads; ++j) {
+                    const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+                    uint32_t r = base + chunk_before[q] + lead[q][j];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        rk[j][k] = static_cast<int32_t>(r);
+                        r += flag_of<P>(v[q][j][k], at + k, n, full, pa, pb) ? 1u : 0u;
+                    }
+                }
+                store_chunk<VEC>(ranks, chunk, lane, n, full, rk);
+            }
         }
     }
 }
 
 // =========================================================== scan kernel ---
-// Exclusive scan of 32-bit values, same tile shape and look-back; the tile
-// aggregate is the sum of the values. Per load j a lane sums its 4 values,
-// a DPP wavefront scan gives the lane offsets, and the outputs are written
-// back with the same 128-bit layout they were read with. in == out allowed.
+// Exclusive scan of 32-bit values with the same tile shape and look-back;
+// the tile aggregate is the sum of the values. Per load j a lane sums its 4
+// values, a DPP wavefront scan gives the lane offsets, and results leave
+// with the same 128-bit layout they were read with. in == out is allowed.
 template <class Op, bool VEC>
-__global__ __launch_bounds__(kBlock) void scan_kernel(
-    const typename Op::T *in, typename Op::T *out, int64_t n, uint64_t *__restrict__ desc,
-    uint32_t *__restrict__ tile_counter, uint32_t *__restrict__ timed_out, uint32_t num_tiles,
-    typename Op::T *total) {
+__global__ __launch_bounds__(kBlock) void scan_kernel(const typename Op::T *in,
+                                                      typename Op::T *out, int64_t n,
+                                                      void *scratch, uint32_t num_tiles,
+                                                      uint32_t capacity, typename Op::T *total) {
     using T = typename Op::T;
-    __shared__ uint32_t s_tot[kWaves];
-    __shared__ uint32_t s_tile;
-    __shared__ uint32_t s_base;
+    __shared__ uint32_t s_tot[kRounds * kWaves];
+    __shared__ uint32_t s_tile, s_tag, s_base;
 
-    if (threadIdx.x == 0) s_tile = claim_tile(tile_counter);
+    const ScratchView sv = view(scratch);
+    if (threadIdx.x == 0) {
+        const uint64_t c = claim_tile(sv, num_tiles, capacity);
+        s_tile = static_cast<uint32_t>(c);
+        s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
+    }
     __syncthreads();
     const uint32_t tile = s_tile;
-    if (tile >= num_tiles) return;  // only if the counter was not cleared
+    const uint32_t tag = s_tag;
+    if (tile >= num_tiles) return;  // only if the scratch was never initialised
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
-    const int64_t chunk = tile_start + static_cast<int64_t>(w) * kChunk;
     const bool full = tile_start + kTile <= n;
 
-    T v[kLoads][4];
-    load_chunk<VEC>(in, chunk, lane, n, full, v);  // missing elements read as 0
+    T v[kRounds][kLoads][4];
+#pragma unroll
+    for (int q = 0; q < kRounds; ++q)
+        load_chunk<VEC>(in, tile_start + q * kSub + w * kChunk, lane, n, full, v[q]);
 
-    // Per load: in-lane exclusive prefixes, lane offset within the wavefront,
-    // and the wavefront-uniform running total of earlier loads.
-    T lane_off[kLoads];
-    T load_run[kLoads];
-    T running = Op::zero();
+    // Replace each value by its exclusive prefix inside the wavefront chunk.
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        T s = Op::zero();
+    for (int q = 0; q < kRounds; ++q) {
+        T running = Op::zero();
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const T x = v[j][k];
-            v[j][k] = s;  // in-lane exclusive prefix
-            s = Op::add(s, x);
+        for (int j = 0; j < kLoads; ++j) {
+            T s = Op::zero();
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const T x = v[q][j][k];
+                v[q][j][k] = s;
+                s = Op::add(s, x);
+            }
+            const T incl = wave_inclusive_scan<Op>(s);
+            const uint32_t up =
+                static_cast<uint32_t>(__shfl_up(static_cast<int>(Op::bits(incl)), 1));
+            const T lead = Op::add(running, lane == 0 ? Op::zero() : Op::from_bits(up));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[q][j][k] = Op::add(lead, v[q][j][k]);
+            running = Op::add(running, Op::from_bits(static_cast<uint32_t>(
+                                           __builtin_amdgcn_readlane(
+                                               static_cast<int>(Op::bits(incl)), kWave - 1))));
         }
-        const T incl = wave_inclusive_scan<Op>(s);
-        const uint32_t up = static_cast<uint32_t>(
-            __shfl_up(static_cast<int>(Op::bits(incl)), 1));
-        lane_off[j] = lane == 0 ? Op::zero() : Op::from_bits(up);
-        load_run[j] = running;
-        const T load_total = Op::from_bits(static_cast<uint32_t>(
-            __builtin_amdgcn_readlane(static_cast<int>(Op::bits(incl)), kWave - 1)));
-        running = Op::add(running, load_total);
+        if (lane == 0) s_tot[q * kWaves + w] = Op::bits(running);
     }
-    if (lane == 0) s_tot[w] = Op::bits(running);
     __syncthreads();
-    T wave_below = Op::zero();
+    T chunk_before[kRounds];
     T agg = Op::zero();
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        const T t = Op::from_bits(s_tot[i]);
-        if (i < w) wave_below = Op::add(wave_below, t);
-        agg = Op::add(agg, t);
+    for (int q = 0; q < kRounds; ++q) {
+        T mine = agg;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            const T t = Op::from_bits(s_tot[q * kWaves + i]);
+            if (i < w) mine = Op::add(mine, t);
+            agg = Op::add(agg, t);
+        }
+        chunk_before[q] = mine;
     }
     if (threadIdx.x == 0)
-        publish(desc + tile, tile == 0 ? kStatusInclusive : kStatusAggregate, Op::bits(agg));
+        publish(sv.desc + tile, tag, tile == 0 ? kStatusInclusive : kStatusAggregate,
+                Op::bits(agg));
 
     if (w == 0) {
         T base = Op::zero();
         if (tile != 0) {
-            base = look_back<Op>(desc, tile, timed_out);
-            if (lane == 0) publish(desc + tile, kStatusInclusive, Op::bits(Op::add(base, agg)));
+            base = look_back<Op>(sv.desc, tile, tag, sv.timed_out);
+            if (lane == 0)
+                publish(sv.desc + tile, tag, kStatusInclusive, Op::bits(Op::add(base, agg)));
         }
         if (lane == 0) {
             s_base = Op::bits(base);
@@ -346,64 +478,90 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(
         }
     }
     __syncthreads();
-    const T chunk_base = Op::add(Op::from_bits(s_base), wave_below);
+    const T base = Op::from_bits(s_base);
 
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        const T lead = Op::add(load_run[j], lane_off[j]);
+    for (int q = 0; q < kRounds; ++q) {
+        const T chunk_base = Op::add(base, chunk_before[q]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[j][k] = Op::add(chunk_base, Op::add(lead, v[j][k]));
+        for (int j = 0; j < kLoads; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[q][j][k] = Op::add(chunk_base, v[q][j][k]);
+        store_chunk<VEC>(out, tile_start + q * kSub + w * kChunk, lane, n, full, v[q]);
     }
-    store_chunk<VEC>(out, chunk, lane, n, full, v);
 }
 
 // ======================================================= counting kernels ---
-// Grid-stride over tiles; each wavefront adds popcount(ballot(flag)) and
-// makes one atomic add at the end. *count must be zero beforehand.
+// Grid-stride over sub-tiles. Each workgroup reduces its flag count in LDS,
+// adds it to one of kSpread accumulators (spreading the atomics over several
+// addresses), then counts itself done; the last workgroup to finish sums the
+// accumulators, writes the result and clears the accumulators and the done
+// counter for the next call. Thread 0 does all of a workgroup's global
+// atomics, so its acquire-release on the done counter orders them.
 template <int P, bool VEC>
 __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t *__restrict__ in, int64_t n,
-                                                       int32_t pa, int32_t pb, uint32_t num_tiles,
-                                                       int32_t *__restrict__ count) {
+                                                       int32_t pa, int32_t pb, uint32_t num_subs,
+                                                       void *scratch, int32_t *__restrict__ result) {
+    __shared__ uint32_t s_cnt[kWaves];
+    const ScratchView sv = view(scratch);
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     uint32_t acc = 0;
-    for (uint32_t tile = blockIdx.x; tile < num_tiles; tile += gridDim.x) {
-        const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
-        const int64_t chunk = tile_start + static_cast<int64_t>(w) * kChunk;
-        const bool full = tile_start + kTile <= n;
+    for (uint32_t sub = blockIdx.x; sub < num_subs; sub += gridDim.x) {
+        const int64_t sub_start = static_cast<int64_t>(sub) * kSub;
+        const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
+        const bool full = sub_start + kSub <= n;
         int32_t v[kLoads][4];
         load_chunk<VEC>(in, chunk, lane, n, full, v);
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             const int64_t at = chunk + j * (kWave * 4) + lane * 4;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bool f = (full || at + k < n) && pred_eval<P>(v[j][k], pa, pb);
-                acc += static_cast<uint32_t>(__builtin_popcountll(ballot(f)));
-            }
+            for (int k = 0; k < 4; ++k)
+                acc += static_cast<uint32_t>(__builtin_popcountll(
+                    ballot(flag_of<P>(v[j][k], at + k, n, full, pa, pb))));
         }
     }
-    if (lane == 0 && acc != 0)
-        __hip_atomic_fetch_add(count, static_cast<int32_t>(acc), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) s_cnt[w] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t total = 0;
+        for (int i = 0; i < kWaves; ++i) total += s_cnt[i];
+        if (total != 0)
+            __hip_atomic_fetch_add(sv.acc + (blockIdx.x % kSpread), total, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t done =
+            __hip_atomic_fetch_add(sv.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            uint32_t k = 0;
+            for (int i = 0; i < kSpread; ++i) {
+                k += __hip_atomic_load(sv.acc + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sv.acc + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            *result = static_cast<int32_t>(k);
+            __hip_atomic_store(sv.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
-// For every bit b, the number of keys whose bit b is clear, added into
-// clear_counts[0..31] (zero beforehand). Lane b carries bit b's total to one
-// atomic add per wavefront.
+// For every bit b, the number of keys whose bit b is clear, left in
+// kept32[0..31] of the scratch (same last-workgroup protocol as above; the
+// 32 per-bit accumulators are 32 different addresses).
 template <bool VEC>
 __global__ __launch_bounds__(kBlock) void bit_clear_count_kernel(const uint32_t *__restrict__ in,
-                                                                 int64_t n, uint32_t num_tiles,
-                                                                 uint32_t *__restrict__ clear_counts) {
+                                                                 int64_t n, uint32_t num_subs,
+                                                                 void *scratch) {
+    __shared__ uint32_t s_cnt[kWaves][32];
+    const ScratchView sv = view(scratch);
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     uint32_t acc[32];
 #pragma unroll
     for (int b = 0; b < 32; ++b) acc[b] = 0;
-    for (uint32_t tile = blockIdx.x; tile < num_tiles; tile += gridDim.x) {
-        const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
-        const int64_t chunk = tile_start + static_cast<int64_t>(w) * kChunk;
-        const bool full = tile_start + kTile <= n;
+    for (uint32_t sub = blockIdx.x; sub < num_subs; sub += gridDim.x) {
+        const int64_t sub_start = static_cast<int64_t>(sub) * kSub;
+        const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
+        const bool full = sub_start + kSub <= n;
         uint32_t v[kLoads][4];
         load_chunk<VEC>(in, chunk, lane, n, full, v);
 #pragma unroll
@@ -420,51 +578,87 @@ __global__ __launch_bounds__(kBlock) void bit_clear_count_kernel(const uint32_t 
             }
         }
     }
-    uint32_t mine = 0;
+    if (lane == 0) {
 #pragma unroll
-    for (int b = 0; b < 32; ++b) mine = (lane == b) ? acc[b] : mine;
-    if (lane < 32 && mine != 0)
-        __hip_atomic_fetch_add(clear_counts + lane, mine, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        for (int b = 0; b < 32; ++b) s_cnt[w][b] = acc[b];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int b = 0; b < 32; ++b) {
+            uint32_t t = 0;
+            for (int i = 0; i < kWaves; ++i) t += s_cnt[i][b];
+            if (t != 0)
+                __hip_atomic_fetch_add(sv.acc32 + b, t, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint32_t done =
+            __hip_atomic_fetch_add(sv.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+            for (int b = 0; b < 32; ++b) {
+                const uint32_t t =
+                    __hip_atomic_load(sv.acc32 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sv.kept32 + b, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sv.acc32 + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __hip_atomic_store(sv.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // ================================================ unordered (atomic) kernel ---
-// Comparison only: no scan, no order. VARIANT 0: each wavefront takes one
-// slot range of size popcount for its whole chunk with one atomic add;
-// VARIANT 1: one atomic add per survivor. *count must be zero beforehand.
+// Comparison only: no scan, no order. One sub-tile per workgroup.
+// VARIANT 0: the workgroup reserves one slot range for all its survivors with
+// a single atomic add; VARIANT 1: one atomic add per survivor. *count must
+// be zero beforehand.
 template <int P, bool VEC, int VARIANT>
 __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *__restrict__ in,
                                                                 int32_t *__restrict__ out,
                                                                 int64_t n, int32_t pa, int32_t pb,
                                                                 int32_t *__restrict__ count) {
+    __shared__ uint32_t s_tot[kWaves];
+    __shared__ uint32_t s_slot;
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
-    const int64_t tile_start = static_cast<int64_t>(blockIdx.x) * kTile;
-    const int64_t chunk = tile_start + static_cast<int64_t>(w) * kChunk;
-    const bool full = tile_start + kTile <= n;
+    const int64_t sub_start = static_cast<int64_t>(blockIdx.x) * kSub;
+    const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
+    const bool full = sub_start + kSub <= n;
     int32_t v[kLoads][4];
     load_chunk<VEC>(in, chunk, lane, n, full, v);
     if constexpr (VARIANT == 0) {
-        bool f[kLoads][4];
-        uint32_t kb[kLoads][4];
-        const uint32_t total = chunk_ranks<P>(v, chunk, lane, n, full, pa, pb, f, kb);
-        uint32_t slot = 0;
-        if (lane == 0 && total != 0)
-            slot = static_cast<uint32_t>(__hip_atomic_fetch_add(
-                count, static_cast<int32_t>(total), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        slot = uniform(slot);
+        uint32_t lead[kLoads];
+        const uint32_t t = chunk_ranks<P>(v, chunk, lane, n, full, pa, pb, lead);
+        if (lane == 0) s_tot[w] = t;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t total = 0;
+            for (int i = 0; i < kWaves; ++i) total += s_tot[i];
+            s_slot = total ? static_cast<uint32_t>(__hip_atomic_fetch_add(
+                                 count, static_cast<int32_t>(total), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT))
+                           : 0u;
+        }
+        __syncthreads();
+        uint32_t slot = s_slot;
+        for (int i = 0; i < w; ++i) slot += s_tot[i];
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j)
+        for (int j = 0; j < kLoads; ++j) {
+            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+            uint32_t r = slot + lead[j];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (f[j][k] && slot + kb[j][k] < n) out[slot + kb[j][k]] = v[j][k];
+            for (int k = 0; k < 4; ++k) {
+                if (flag_of<P>(v[j][k], at + k, n, full, pa, pb)) {
+                    if (r < n) out[r] = v[j][k];
+                    ++r;
+                }
+            }
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
             const int64_t at = chunk + j * (kWave * 4) + lane * 4;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                if ((full || at + k < n) && pred_eval<P>(v[j][k], pa, pb)) {
+                if (flag_of<P>(v[j][k], at + k, n, full, pa, pb)) {
                     const int32_t slot = __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED,
                                                                 __HIP_MEMORY_SCOPE_AGENT);
                     if (slot < n) out[slot] = v[j][k];
@@ -480,16 +674,15 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const int32_t *__restrict_
                                                       int32_t *__restrict__ out, int64_t n) {
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
-    const int64_t tile_start = static_cast<int64_t>(blockIdx.x) * kTile;
-    const int64_t chunk = tile_start + static_cast<int64_t>(w) * kChunk;
-    const bool full = tile_start + kTile <= n;
+    const int64_t sub_start = static_cast<int64_t>(blockIdx.x) * kSub;
+    const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
+    const bool full = sub_start + kSub <= n;
     int32_t v[kLoads][4];
     load_chunk<VEC>(in, chunk, lane, n, full, v);
     store_chunk<VEC>(out, chunk, lane, n, full, v);
 }
 
-// Clears `words` 32-bit words (scratch: counters and descriptors; a kernel
-// rather than a memset node).
+// Clears `words` 32-bit words (a kernel rather than a memset node).
 __global__ __launch_bounds__(kBlock) void clear_kernel(uint32_t *__restrict__ p, int64_t words) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < words;
          i += static_cast<int64_t>(gridDim.x) * kBlock)
@@ -499,7 +692,7 @@ __global__ __launch_bounds__(kBlock) void clear_kernel(uint32_t *__restrict__ p,
 }  // namespace ssc
 
 // ======================================================================
-// Host side: argument checks, scratch clearing, dispatch.
+// Host side: argument checks and dispatch.
 // ======================================================================
 namespace {
 
@@ -558,9 +751,20 @@ int check_n(int64_t n) {
     return SSC_OK;
 }
 
+size_t scratch_need(int64_t n) {
+    const int64_t t = n > 0 ? tiles_for(n) : 0;
+    return kHeaderBytes + static_cast<size_t>(t) * sizeof(uint64_t);
+}
+
 int check_scratch(const void *scratch, size_t bytes, size_t need) {
     if (scratch == nullptr || !aligned(scratch, 8) || bytes < need) return SSC_ERR_SCRATCH;
     return SSC_OK;
+}
+
+// Descriptor slots the scratch holds (the stale-slot sweep stays inside them).
+uint32_t capacity_of(size_t scratch_bytes) {
+    const size_t slots = (scratch_bytes - kHeaderBytes) / sizeof(uint64_t);
+    return slots > kMaxTiles ? kMaxTiles : static_cast<uint32_t>(slots);
 }
 
 int launched() {
@@ -577,25 +781,11 @@ int clear_words(void *p, int64_t words, hipStream_t s) {
     return launched();
 }
 
-// Scratch header: word 0 the tile counter, word 1 the look-back time-out
-// flag; the descriptors follow the header.
-struct Scratch {
-    uint32_t *counter;
-    uint32_t *timed_out;
-    uint64_t *desc;
-};
+uint32_t subs_for(int64_t n) { return static_cast<uint32_t>((n + kSub - 1) / kSub); }
 
-Scratch carve(void *scratch) {
-    Scratch s;
-    s.counter = static_cast<uint32_t *>(scratch);
-    s.timed_out = s.counter + 1;
-    s.desc = reinterpret_cast<uint64_t *>(static_cast<char *>(scratch) + kHeaderBytes);
-    return s;
-}
-
-size_t scratch_need(int64_t n) {
-    const int64_t t = n > 0 ? tiles_for(n) : 0;
-    return kHeaderBytes + static_cast<size_t>(t) * sizeof(uint64_t);
+uint32_t reduce_grid(int64_t n) {
+    const uint32_t subs = subs_for(n);
+    return subs < static_cast<uint32_t>(kReduceGrid) ? subs : static_cast<uint32_t>(kReduceGrid);
 }
 
 // ---- template dispatch on the predicate and the load width ----
@@ -614,27 +804,25 @@ int dispatch_pred(int pred, bool vec, A... a) {
 template <int P, bool VEC>
 struct LaunchSelect {
     static int run(bool partition, const int32_t *in, int32_t *out, int64_t n, int32_t pa,
-                   int32_t pb, Scratch sc, uint32_t tiles, int32_t *count, int32_t *ranks,
+                   int32_t pb, void *scratch, uint32_t capacity, int32_t *count, int32_t *ranks,
                    const int32_t *kept, hipStream_t s) {
+        const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
         if (partition)
             hipLaunchKernelGGL((select_kernel<P, VEC, true>), dim3(tiles), dim3(kBlock), 0, s, in,
-                               out, n, pa, pb, sc.desc, sc.counter, sc.timed_out, tiles, count,
-                               ranks, kept);
+                               out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
         else
             hipLaunchKernelGGL((select_kernel<P, VEC, false>), dim3(tiles), dim3(kBlock), 0, s, in,
-                               out, n, pa, pb, sc.desc, sc.counter, sc.timed_out, tiles, count,
-                               ranks, kept);
+                               out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
         return launched();
     }
 };
 
 template <int P, bool VEC>
 struct LaunchCount {
-    static int run(const int32_t *in, int64_t n, int32_t pa, int32_t pb, uint32_t tiles,
-                   int32_t *count, hipStream_t s) {
-        const uint32_t grid = tiles < static_cast<uint32_t>(kReduceGrid) ? tiles : kReduceGrid;
-        hipLaunchKernelGGL((count_kernel<P, VEC>), dim3(grid), dim3(kBlock), 0, s, in, n, pa, pb,
-                           tiles, count);
+    static int run(const int32_t *in, int64_t n, int32_t pa, int32_t pb, void *scratch,
+                   int32_t *result, hipStream_t s) {
+        hipLaunchKernelGGL((count_kernel<P, VEC>), dim3(reduce_grid(n)), dim3(kBlock), 0, s, in, n,
+                           pa, pb, subs_for(n), scratch, result);
         return launched();
     }
 };
@@ -642,20 +830,21 @@ struct LaunchCount {
 template <int P, bool VEC>
 struct LaunchAtomic {
     static int run(int variant, const int32_t *in, int32_t *out, int64_t n, int32_t pa,
-                   int32_t pb, uint32_t tiles, int32_t *count, hipStream_t s) {
+                   int32_t pb, int32_t *count, hipStream_t s) {
+        const uint32_t subs = subs_for(n);
         if (variant == 0)
-            hipLaunchKernelGGL((compact_atomic_kernel<P, VEC, 0>), dim3(tiles), dim3(kBlock), 0, s,
+            hipLaunchKernelGGL((compact_atomic_kernel<P, VEC, 0>), dim3(subs), dim3(kBlock), 0, s,
                                in, out, n, pa, pb, count);
         else
-            hipLaunchKernelGGL((compact_atomic_kernel<P, VEC, 1>), dim3(tiles), dim3(kBlock), 0, s,
+            hipLaunchKernelGGL((compact_atomic_kernel<P, VEC, 1>), dim3(subs), dim3(kBlock), 0, s,
                                in, out, n, pa, pb, count);
         return launched();
     }
 };
 
-#define SSC_TRY(expr)                 \
-    do {                              \
-        const int rc_ = (expr);       \
+#define SSC_TRY(expr)                  \
+    do {                               \
+        const int rc_ = (expr);        \
         if (rc_ != SSC_OK) return rc_; \
     } while (0)
 
@@ -671,20 +860,19 @@ int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename
     if (total && (overlap(total, sizeof(T), in, bytes) || overlap(total, sizeof(T), out, bytes)))
         return SSC_ERR_ALIAS;
     SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
-    if (overlap(scratch, scratch_need(n), in, bytes) || overlap(scratch, scratch_need(n), out, bytes) ||
-        (total && overlap(scratch, scratch_need(n), total, sizeof(T))))
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        (total && overlap(scratch, scratch_bytes, total, sizeof(T))))
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return total ? clear_words(total, 1, s) : SSC_OK;
     const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
-    SSC_TRY(clear_words(scratch, static_cast<int64_t>(scratch_need(n) / 4), s));
-    const Scratch sc = carve(scratch);
+    const uint32_t cap = capacity_of(scratch_bytes);
     if (aligned(in, 16) && aligned(out, 16))
         hipLaunchKernelGGL((scan_kernel<Op, true>), dim3(tiles), dim3(kBlock), 0, s, in, out, n,
-                           sc.desc, sc.counter, sc.timed_out, tiles, total);
+                           scratch, tiles, cap, total);
     else
         hipLaunchKernelGGL((scan_kernel<Op, false>), dim3(tiles), dim3(kBlock), 0, s, in, out, n,
-                           sc.desc, sc.counter, sc.timed_out, tiles, total);
+                           scratch, tiles, cap, total);
     return launched();
 }
 
@@ -699,9 +887,14 @@ int64_t ssc_tile_elems(void) { return kTile; }
 
 size_t ssc_scratch_bytes(int64_t n) { return scratch_need(n < 0 ? 0 : n); }
 
-size_t ssc_radix_sort_scratch_bytes(int64_t n) {
-    const int64_t t = n > 0 ? tiles_for(n) : 0;
-    return kRadixHeaderBytes + 32 * static_cast<size_t>(t) * sizeof(uint64_t);
+size_t ssc_radix_sort_scratch_bytes(int64_t n) { return scratch_need(n < 0 ? 0 : n); }
+
+int ssc_scratch_init(void *scratch, size_t scratch_bytes, void *stream) {
+    if (scratch == nullptr || !aligned(scratch, 8) || scratch_bytes < kHeaderBytes)
+        return SSC_ERR_SCRATCH;
+    SSC_TRY(check_device());
+    return clear_words(scratch, static_cast<int64_t>(scratch_bytes / 4),
+                       static_cast<hipStream_t>(stream));
 }
 
 int ssc_exclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
@@ -727,23 +920,22 @@ int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_
     if (!aligned(in, 4) || !aligned(out, 4) || !aligned(count, 4) || (ranks && !aligned(ranks, 4)))
         return SSC_ERR_ARG;
     const size_t bytes = static_cast<size_t>(n) * 4;
-    const size_t need = scratch_need(n);
     if (overlap(in, bytes, out, bytes) || overlap(count, 4, in, bytes) ||
         overlap(count, 4, out, bytes) ||
         (ranks && (overlap(ranks, bytes, in, bytes) || overlap(ranks, bytes, out, bytes) ||
                    overlap(ranks, bytes, count, 4))))
         return SSC_ERR_ALIAS;
-    SSC_TRY(check_scratch(scratch, scratch_bytes, need));
-    if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, bytes) ||
-        overlap(scratch, need, count, 4) || (ranks && overlap(scratch, need, ranks, bytes)))
+    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        overlap(scratch, scratch_bytes, count, 4) ||
+        (ranks && overlap(scratch, scratch_bytes, ranks, bytes)))
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
-    const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
-    SSC_TRY(clear_words(scratch, static_cast<int64_t>(need / 4), s));
     const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect>(pred, vec, false, in, out, n, pa, pb, carve(scratch), tiles,
-                                       count, ranks, static_cast<const int32_t *>(nullptr), s);
+    return dispatch_pred<LaunchSelect>(pred, vec, false, in, out, n, pa, pb, scratch,
+                                       capacity_of(scratch_bytes), count, ranks,
+                                       static_cast<const int32_t *>(nullptr), s);
 }
 
 int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
@@ -754,40 +946,38 @@ int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int3
     SSC_TRY(check_pred(pred, pa, pb));
     if (!aligned(in, 4) || !aligned(out, 4) || !aligned(count, 4)) return SSC_ERR_ARG;
     const size_t bytes = static_cast<size_t>(n) * 4;
-    const size_t need = scratch_need(n);
     if (overlap(in, bytes, out, bytes) || overlap(count, 4, in, bytes) ||
         overlap(count, 4, out, bytes))
         return SSC_ERR_ALIAS;
-    SSC_TRY(check_scratch(scratch, scratch_bytes, need));
-    if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, bytes) ||
-        overlap(scratch, need, count, 4))
+    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        overlap(scratch, scratch_bytes, count, 4))
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
-    SSC_TRY(clear_words(count, 1, s));
-    if (n == 0) return SSC_OK;
-    const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
-    SSC_TRY(clear_words(scratch, static_cast<int64_t>(need / 4), s));
+    if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16);
-    SSC_TRY(dispatch_pred<LaunchCount>(pred, vec, in, n, pa, pb, tiles, count, s));
-    return dispatch_pred<LaunchSelect>(pred, vec, true, in, out, n, pa, pb, carve(scratch), tiles,
-                                       static_cast<int32_t *>(nullptr),
+    SSC_TRY(dispatch_pred<LaunchCount>(pred, vec, in, n, pa, pb, scratch, count, s));
+    return dispatch_pred<LaunchSelect>(pred, vec, true, in, out, n, pa, pb, scratch,
+                                       capacity_of(scratch_bytes), static_cast<int32_t *>(nullptr),
                                        static_cast<int32_t *>(nullptr),
                                        static_cast<const int32_t *>(count), s);
 }
 
 int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t pb,
-                     int32_t *count, void *stream) {
+                     int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     SSC_TRY(check_n(n));
     if (count == nullptr || (n > 0 && in == nullptr)) return SSC_ERR_ARG;
     SSC_TRY(check_pred(pred, pa, pb));
     if (!aligned(in, 4) || !aligned(count, 4)) return SSC_ERR_ARG;
-    if (overlap(count, 4, in, static_cast<size_t>(n) * 4)) return SSC_ERR_ALIAS;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (overlap(count, 4, in, bytes)) return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch(scratch, scratch_bytes, kHeaderBytes));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, count, 4))
+        return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
-    SSC_TRY(clear_words(count, 1, s));
-    if (n == 0) return SSC_OK;
-    const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
-    return dispatch_pred<LaunchCount>(pred, aligned(in, 16), in, n, pa, pb, tiles, count, s);
+    if (n == 0) return clear_words(count, 1, s);
+    return dispatch_pred<LaunchCount>(pred, aligned(in, 16), in, n, pa, pb, scratch, count, s);
 }
 
 int ssc_compact_atomic_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
@@ -805,9 +995,8 @@ int ssc_compact_atomic_i32(const int32_t *in, int32_t *out, int64_t n, int pred,
     SSC_TRY(check_device());
     SSC_TRY(clear_words(count, 1, s));
     if (n == 0) return SSC_OK;
-    const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
-    return dispatch_pred<LaunchAtomic>(pred, aligned(in, 16), variant, in, out, n, pa, pb, tiles,
-                                       count, s);
+    return dispatch_pred<LaunchAtomic>(pred, aligned(in, 16), variant, in, out, n, pa, pb, count,
+                                       s);
 }
 
 int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t n, void *scratch,
@@ -820,50 +1009,34 @@ int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t
     if ((in != out && overlap(in, bytes, out, bytes)) || overlap(tmp, bytes, in, bytes) ||
         overlap(tmp, bytes, out, bytes))
         return SSC_ERR_ALIAS;
-    const size_t need = ssc_radix_sort_scratch_bytes(n);
-    SSC_TRY(check_scratch(scratch, scratch_bytes, need));
-    if (overlap(scratch, need, in, bytes) || overlap(scratch, need, out, bytes) ||
-        overlap(scratch, need, tmp, bytes))
+    SSC_TRY(check_scratch(scratch, scratch_bytes, ssc_radix_sort_scratch_bytes(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        overlap(scratch, scratch_bytes, tmp, bytes))
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return SSC_OK;
-    const int64_t tiles64 = tiles_for(n);
-    const uint32_t tiles = static_cast<uint32_t>(tiles64);
-    SSC_TRY(clear_words(scratch, static_cast<int64_t>(need / 4), s));
-    // Header: 32 tile counters (one per pass), 32 bit-clear counts, then the
-    // look-back time-out flag; 32 descriptor arrays follow.
-    uint32_t *counters = static_cast<uint32_t *>(scratch);
-    uint32_t *clear_counts = counters + 32;
-    uint32_t *timed_out = counters + 64;
-    uint64_t *desc0 =
-        reinterpret_cast<uint64_t *>(static_cast<char *>(scratch) + kRadixHeaderBytes);
+    const ScratchView sv = view(scratch);
     const bool vec = aligned(in, 16) && aligned(out, 16) && aligned(tmp, 16);
-    {
-        const uint32_t grid = tiles < static_cast<uint32_t>(kReduceGrid) ? tiles : kReduceGrid;
-        if (vec)
-            hipLaunchKernelGGL((bit_clear_count_kernel<true>), dim3(grid), dim3(kBlock), 0, s, in,
-                               n, tiles, clear_counts);
-        else
-            hipLaunchKernelGGL((bit_clear_count_kernel<false>), dim3(grid), dim3(kBlock), 0, s, in,
-                               n, tiles, clear_counts);
-        SSC_TRY(launched());
-    }
+    if (vec)
+        hipLaunchKernelGGL((bit_clear_count_kernel<true>), dim3(reduce_grid(n)), dim3(kBlock), 0,
+                           s, in, n, subs_for(n), scratch);
+    else
+        hipLaunchKernelGGL((bit_clear_count_kernel<false>), dim3(reduce_grid(n)), dim3(kBlock), 0,
+                           s, in, n, subs_for(n), scratch);
+    SSC_TRY(launched());
+    const uint32_t cap = capacity_of(scratch_bytes);
     const uint32_t *src = in;
     for (int b = 0; b < 32; ++b) {
         uint32_t *dst = (b % 2 == 0) ? tmp : out;  // pass 31 lands in out
-        Scratch sc;
-        sc.counter = counters + b;
-        sc.timed_out = timed_out;
-        sc.desc = desc0 + static_cast<size_t>(b) * tiles64;
-        const int32_t *kept = reinterpret_cast<const int32_t *>(clear_counts + b);
+        const int32_t *kept = reinterpret_cast<const int32_t *>(sv.kept32 + b);
         if (vec)
             SSC_TRY((LaunchSelect<4, true>::run(true, reinterpret_cast<const int32_t *>(src),
-                                                reinterpret_cast<int32_t *>(dst), n, b, 0, sc,
-                                                tiles, nullptr, nullptr, kept, s)));
+                                                reinterpret_cast<int32_t *>(dst), n, b, 0, scratch,
+                                                cap, nullptr, nullptr, kept, s)));
         else
             SSC_TRY((LaunchSelect<4, false>::run(true, reinterpret_cast<const int32_t *>(src),
-                                                 reinterpret_cast<int32_t *>(dst), n, b, 0, sc,
-                                                 tiles, nullptr, nullptr, kept, s)));
+                                                 reinterpret_cast<int32_t *>(dst), n, b, 0,
+                                                 scratch, cap, nullptr, nullptr, kept, s)));
         src = dst;
     }
     return SSC_OK;
@@ -878,11 +1051,11 @@ int ssc_copy_i32(const int32_t *in, int32_t *out, int64_t n, void *stream) {
     if (overlap(in, bytes, out, bytes)) return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return SSC_OK;
-    const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
     if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL((copy_kernel<true>), dim3(tiles), dim3(kBlock), 0, s, in, out, n);
+        hipLaunchKernelGGL((copy_kernel<true>), dim3(subs_for(n)), dim3(kBlock), 0, s, in, out, n);
     else
-        hipLaunchKernelGGL((copy_kernel<false>), dim3(tiles), dim3(kBlock), 0, s, in, out, n);
+        hipLaunchKernelGGL((copy_kernel<false>), dim3(subs_for(n)), dim3(kBlock), 0, s, in, out,
+                           n);
     return launched();
 }
 

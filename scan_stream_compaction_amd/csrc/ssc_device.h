@@ -106,36 +106,40 @@ __device__ __forceinline__ bool pred_eval(int32_t x, int32_t pa, int32_t pb) {
 }
 
 // ------------------------------------------------------ tile descriptors ---
-// One 64-bit word per tile: status in the high half, a 32-bit value (count,
-// int sum or fp32 bits) in the low half, written and read as a single
-// agent-scope atomic so status and value always travel together. All-zero
-// is "no information yet", which is what clearing the scratch produces.
+// One 64-bit word per tile: the low half holds a 32-bit value (a count, an
+// int sum or fp32 bits); the high half holds (tag << 2) | status, where tag
+// is the call's epoch modulo 2^30. Status and value are written and read as
+// a single agent-scope atomic, so they always travel together. A word whose
+// tag is not the current call's, or whose status is 0 (all-zero memory
+// included), means "nothing published yet": descriptors never need clearing
+// between calls.
 
-constexpr uint32_t kStatusNone = 0;       // nothing published
 constexpr uint32_t kStatusAggregate = 1;  // value = this tile's own total
 constexpr uint32_t kStatusInclusive = 2;  // value = total of tiles 0..t
+constexpr uint32_t kTagMask = 0x3FFFFFFFu;
 
-__device__ __forceinline__ void publish(uint64_t *desc, uint32_t status, uint32_t value) {
-    const uint64_t word = (static_cast<uint64_t>(status) << 32) | value;
-    __hip_atomic_store(desc, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t descriptor(uint32_t tag, uint32_t status, uint32_t value) {
+    return (static_cast<uint64_t>((tag << 2) | status) << 32) | value;
+}
+
+__device__ __forceinline__ void publish(uint64_t *desc, uint32_t tag, uint32_t status,
+                                        uint32_t value) {
+    __hip_atomic_store(desc, descriptor(tag, status, value), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
     return __hip_atomic_load(desc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint32_t claim_tile(uint32_t *counter) {
-    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Decoupled look-back, run by one whole wavefront of the tile's workgroup.
 // Reads the descriptors of the 64 tiles just below `tile` at once; while any
-// of them has published nothing it sleeps and reads again. Once all 64 have
-// published, the nearest inclusive one ends the walk: the result is its value
-// plus the aggregates above it. With no inclusive value in the window all 64
-// aggregates are added and the window moves 64 tiles down. Tiles below 0
-// count as inclusive with value 0. Returns the exclusive prefix of `tile`
-// (the total of tiles 0..tile-1) in every lane.
+// of them has published nothing in this call it sleeps and reads again. Once
+// all 64 have published, the nearest inclusive one ends the walk: the result
+// is its value plus the aggregates above it. With no inclusive value in the
+// window all 64 aggregates are added and the window moves 64 tiles down.
+// Tiles below 0 count as inclusive with value 0. Returns the exclusive prefix
+// of `tile` (the total of tiles 0..tile-1) in every lane.
 //
 // Forward progress: a tile only waits on lower-numbered tiles, whose numbers
 // were claimed earlier by workgroups that are already running, and tile 0
@@ -148,7 +152,8 @@ __device__ __forceinline__ uint32_t claim_tile(uint32_t *counter) {
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 template <class Op>
-__device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t *timed_out) {
+__device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
+                                    uint32_t *timed_out) {
     using T = typename Op::T;
     const int lane = lane_id();
     T prefix = Op::zero();
@@ -157,11 +162,12 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t *tim
     while (true) {
         const int64_t idx = end - kWave + lane;
         uint64_t word;
+        uint32_t status;
         while (true) {
-            word = idx >= 0 ? peek(desc + idx)
-                            : (static_cast<uint64_t>(kStatusInclusive) << 32);
-            const bool ready = (word >> 32) != kStatusNone;
-            if (ballot(!ready) == 0) break;
+            word = idx >= 0 ? peek(desc + idx) : descriptor(tag, kStatusInclusive, 0u);
+            const uint32_t hi = static_cast<uint32_t>(word >> 32);
+            status = ((hi >> 2) == tag) ? (hi & 3u) : 0u;
+            if (ballot(status == 0u) == 0) break;
             if (++spins > kSpinLimit) {
                 if (lane == 0)
                     __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -169,7 +175,7 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t *tim
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        const uint64_t inclusive = ballot((word >> 32) == kStatusInclusive);
+        const uint64_t inclusive = ballot(status == kStatusInclusive);
         const T value = Op::from_bits(static_cast<uint32_t>(word));
         if (inclusive != 0) {
             const int top = 63 - __builtin_clzll(inclusive);

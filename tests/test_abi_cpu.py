@@ -67,12 +67,13 @@ def test_enum_numbering_agrees_with_oracle_and_binding():
 def test_tile_and_scratch_sizes():
     L = ssc.lib()
     T = L.ssc_tile_elems()
-    assert T == 4096
+    assert T == 32768
     for n in (0, 1, T - 1, T, T + 1, 2**28, INT32_MAX):
         tiles = (n + T - 1) // T
-        assert L.ssc_scratch_bytes(n) == 256 + 8 * tiles
-        assert L.ssc_radix_sort_scratch_bytes(n) == 512 + 32 * 8 * tiles
-    assert L.ssc_scratch_bytes(-5) == 256
+        assert L.ssc_scratch_bytes(n) == 512 + 8 * tiles
+        assert L.ssc_radix_sort_scratch_bytes(n) == 512 + 8 * tiles
+    assert L.ssc_scratch_bytes(INT32_MAX) == 512 + 8 * 65536
+    assert L.ssc_scratch_bytes(-5) == 512
 
 
 def test_status_strings():
@@ -110,8 +111,8 @@ def test_compact_argument_errors():
     assert _compact(ranks=B + 8) == ALIAS
     assert _compact(scratch=None) == SCRATCH
     assert _compact(scratch=S + 4) == SCRATCH  # not 8-byte aligned
-    assert _compact(sbytes=255) == SCRATCH
-    assert _compact(n=5000, sbytes=256 + 8) == SCRATCH  # needs two descriptors
+    assert _compact(sbytes=511) == SCRATCH
+    assert _compact(n=40000, sbytes=512 + 8) == SCRATCH  # needs two descriptors
     assert _compact(scratch=A) == ALIAS
 
 
@@ -132,14 +133,20 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     assert L.ssc_partition_i32(A, B, 100, 2, 0, 0, None, S, big, None) == ARG
     assert L.ssc_partition_i32(A, B, 100, 2, 0, 0, C, S, 8, None) == SCRATCH
     # count_if
-    assert L.ssc_count_if_i32(A, 100, 0, 0, 0, A + 8, None) == ALIAS
-    assert L.ssc_count_if_i32(A, 100, 5, 0, 0, C, None) == ARG
+    assert L.ssc_count_if_i32(A, 100, 0, 0, 0, A + 8, S, big, None) == ALIAS
+    assert L.ssc_count_if_i32(A, 100, 5, 0, 0, C, S, big, None) == ARG
+    assert L.ssc_count_if_i32(A, 100, 0, 0, 0, C, S, 100, None) == SCRATCH
+    assert L.ssc_count_if_i32(A, 100, 0, 0, 0, C, A, big, None) == ALIAS
+    # scratch_init rejects what it cannot clear, before touching HIP
+    assert L.ssc_scratch_init(None, big, None) == SCRATCH
+    assert L.ssc_scratch_init(S + 4, big, None) == SCRATCH
+    assert L.ssc_scratch_init(S, 100, None) == SCRATCH
     # atomic
     assert L.ssc_compact_atomic_i32(A, B, 100, 1, 0, 0, C, 2, None) == ARG
     assert L.ssc_compact_atomic_i32(A, A + 8, 100, 1, 0, 0, C, 0, None) == ALIAS
     # radix sort: tmp must not overlap; scratch must hold 32 descriptor arrays
     assert L.ssc_radix_sort_u32(A, B, B + 64, 100, S, big, None) == ALIAS
-    assert L.ssc_radix_sort_u32(A, B, C, 100, S, 512 + 8, None) == SCRATCH
+    assert L.ssc_radix_sort_u32(A, B, C, 100, S, 512 + 7, None) == SCRATCH
     assert L.ssc_radix_sort_u32(A, B, None, 100, S, big, None) == ARG
     # copy
     assert L.ssc_copy_i32(A, A + 4, 100, None) == ALIAS

@@ -5,7 +5,7 @@ relative of the fp64 oracle (bit-exact where every prefix is an exact
 integer below 2^24). The unordered atomic compaction is checked as a
 multiset. Inputs come from the seeded generators in
 scan_stream_compaction_amd.workloads, at the five workloads' full sizes and
-at edge sizes around the 4096-element tile.
+at edge sizes around the 32768-element tile and its 8192-element sub-tiles.
 """
 from __future__ import annotations
 
@@ -22,7 +22,8 @@ from tests import checks
 
 pytestmark = pytest.mark.gpu
 
-T = 4096
+T = 32768   # elements per tile
+S = 8192    # elements per sub-tile
 SENTINEL = -123456789
 DEV = "cuda"
 
@@ -197,8 +198,9 @@ def test_radix_sort_full_size():
 
 # -------------------------------------------------------------- edge cases ---
 
-EDGE_N = [0, 1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, T - 1, T, T + 1,
-          2 * T - 1, 2 * T, 2 * T + 1, 5 * T + 611, 64 * T + 13, 65 * T + T - 1]
+EDGE_N = [0, 1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, S - 1, S, S + 1,
+          3 * S + 5, T - 1, T, T + 1, 2 * T - 1, 2 * T, 2 * T + 1, 5 * T + 611,
+          64 * T + 13, 65 * T + T - 1]
 
 
 @pytest.mark.parametrize("n", EDGE_N)
@@ -242,8 +244,8 @@ def test_keep_all_is_copy_and_keep_none_writes_nothing():
     check_partition(x, "mod_lt", 100, 0)                        # nothing kept: out == in
 
 
-@pytest.mark.parametrize("n", [T - 3, 3 * T + 611, 100_003])
-def test_unaligned_arrays_take_the_32bit_path(n):
+@pytest.mark.parametrize("n", [S - 3, 3 * T + 611, 100_003])
+def test_unaligned_arrays_take_the_32bit_path(n):  # noqa: C901
     """Arrays 4-byte but not 16-byte aligned (offset by one element)."""
     x = wl.uniform_below(9, n + 1, 10)
     base = dev(x)
@@ -298,8 +300,45 @@ def test_repeated_runs_are_identical():
     for it in range(10):
         ssc.exclusive_scan(xd, out=sout, scratch=scratch)
         assert torch.equal(sout, swd), it
-    # word 1 of the scratch: set only if a look-back wait gave up
-    assert int(host(scratch[4:8].view(torch.int32))[0]) == 0
+    # word 2 of the scratch: set only if a look-back wait gave up
+    assert int(host(scratch[8:12].view(torch.int32))[0]) == 0
+
+
+def test_one_scratch_across_sizes_and_ops():
+    """One scratch buffer serves many calls of different sizes and kinds in a
+    row: the epoch tags keep descriptors of earlier calls from being read."""
+    big = wl.uniform_below(123, 40 * T + 7, 5)
+    small = wl.uniform_below(321, 3 * T + 1, 5)
+    scratch = ssc.new_scratch(big.size, torch.device(DEV))
+    plan = [big, small, big, small[:100], big, small, big[: T + 1], big]
+    for it, x in enumerate(plan):
+        xd = dev(x)
+        want, m = oracle.compact_i32(x, oracle.PRED_NONZERO)
+        out, cnt = ssc.compact(xd, "nonzero", scratch=scratch)
+        assert int(host(cnt)[0]) == m, it
+        assert checks.first_mismatch(host(out)[:m], want) == -1, it
+        sw, stot = oracle.exclusive_scan_i32(x)
+        sout, tot = ssc.exclusive_scan(xd, scratch=scratch)
+        assert checks.first_mismatch(host(sout), sw) == -1, it
+        pw, k = oracle.partition_i32(x, oracle.PRED_ODD)
+        pout, kc = ssc.partition(xd, "odd", scratch=scratch)
+        assert int(host(kc)[0]) == k and checks.first_mismatch(host(pout), pw) == -1, it
+        c = ssc.count_if(xd, "even", scratch=scratch)
+        assert int(host(c)[0]) == oracle.count(x, oracle.PRED_EVEN), it
+    assert int(host(scratch[8:12].view(torch.int32))[0]) == 0
+
+
+def test_scratch_init_zero_fills():
+    scratch = torch.full((ssc.scratch_bytes(5 * T),), 0x5A, dtype=torch.uint8, device=DEV)
+    rc = ssc.lib().ssc_scratch_init(scratch.data_ptr(), scratch.numel(),
+                                    torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    assert int(host(scratch).astype(np.int64).sum()) == 0
+    x = wl.uniform_below(77, 5 * T, 3)
+    want, m = oracle.compact_i32(x, oracle.PRED_NONZERO)
+    out, cnt = ssc.compact(dev(x), "nonzero", scratch=scratch)
+    assert int(host(cnt)[0]) == m
+    assert checks.first_mismatch(host(out)[:m], want) == -1
 
 
 def test_runs_on_a_side_stream():
