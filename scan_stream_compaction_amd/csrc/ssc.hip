@@ -10,16 +10,18 @@
 // survivors before it by a decoupled look-back over per-tile descriptors.
 //
 // MI355X-first tile shape. A same-address device-scope atomic is serialised
-// across the 8 XCDs at roughly 11-12 ns, so the tile number is claimed once
-// per 32768 elements (128 KiB), not per few thousand: a 512-thread workgroup
-// (8 wavefronts of 64 lanes) holds its whole tile in registers, 64 elements
-// per lane from sixteen 128-bit loads. The tile is 4 sub-tiles of 8192; in
-// each sub-tile every wavefront owns 1024 consecutive elements read by four
-// 128-bit loads per lane, each load instruction covering 1 KiB of contiguous
-// bytes. Element order inside a wavefront chunk is (load j, lane, component
-// k). Ranks inside a wavefront come from ballot + mbcnt, wavefront totals
-// meet in LDS, and survivors are staged in LDS one sub-tile at a time (32
-// KiB) and leave as one contiguous run of coalesced stores per sub-tile.
+// across the 8 XCDs at roughly 11-12 ns, so a tile number is claimed once per
+// 30720 elements (120 KiB). A 1024-thread workgroup = 15 data wavefronts +
+// 1 control wavefront: the control wavefront walks the look-back while the
+// data wavefronts load (the look-back's waits cannot share a wavefront with
+// outstanding data loads, whose completions count in the same in-order
+// counter). Each data lane holds 32 elements from eight 128-bit nontemporal
+// loads, every load instruction covering 1 KiB of contiguous bytes; element
+// order in a wavefront chunk is (load j, lane, component k). Ranks come from
+// ballot + mbcnt, the last data wavefront to finish scans the 30 chunk totals
+// and publishes the tile aggregate at once, and survivors are staged in LDS
+// (60 KiB per round) and leave as one contiguous run of coalesced stores per
+// round. At most 64 VGPRs: two workgroups (32 wavefronts) per CU.
 //
 // Scratch needs no clearing between calls: tile numbers and an epoch come
 // from one 64-bit atomic word {epoch:32 | next tile:32}; the workgroup that
@@ -36,17 +38,31 @@
 namespace ssc {
 
 // ------------------------------------------------------------ tile shape ---
-constexpr int kBlock = 512;                    // threads per workgroup
-constexpr int kWaves = kBlock / kWave;         // 8 wavefronts
-constexpr int kLoads = 4;                      // 128-bit loads per lane per sub-tile
-constexpr int kChunk = kWave * kLoads * 4;     // 1024 elements per wavefront per sub-tile
-constexpr int kSub = kBlock * kLoads * 4;      // 8192 elements per sub-tile
-constexpr int kRounds = 4;                     // sub-tiles per tile
-constexpr int kTile = kSub * kRounds;          // 32768 elements per tile
-constexpr uint32_t kMaxTiles = 1u << 16;       // tiles of the largest n (INT32_MAX)
+// Streaming kernels (copy, counting, unordered comparison): a 512-thread
+// workgroup (8 wavefronts) handles a sub-tile of 8192 elements, each
+// wavefront 1024 consecutive ones with four 128-bit loads per lane.
+constexpr int kBlock = 512;
+constexpr int kWaves = kBlock / kWave;         // 8
+constexpr int kLoads = 4;                      // 128-bit loads per lane per chunk
+constexpr int kChunk = kWave * kLoads * 4;     // 1024 elements per wavefront chunk
+constexpr int kSub = kBlock * kLoads * 4;      // 8192 elements per streaming sub-tile
+
+// Look-back kernels (compaction, partition, scan): a 1024-thread workgroup =
+// 15 data wavefronts + 1 control wavefront. The control wavefront claims the
+// tile and walks the look-back while the data wavefronts load and rank; a
+// tile is 2 rounds of 15 chunks (30720 elements, 120 KiB), 32 elements per
+// data lane from eight 128-bit loads.
+constexpr int kLbBlock = 1024;
+constexpr int kDataWaves = 15;
+constexpr int kCtrlWave = 15;                  // index of the control wavefront
+constexpr int kLbRounds = 2;                   // chunks per data wavefront per tile
+constexpr int kLbSub = kDataWaves * kChunk;    // 15360 elements per round
+constexpr int kTile = kLbSub * kLbRounds;      // 30720 elements per tile
+constexpr uint32_t kMaxTiles = 1u << 17;       // power of two >= tiles of the largest n
 constexpr int kReduceGrid = 512;               // workgroups of the grid-stride counting kernels
 constexpr int kSpread = 16;                    // accumulators a counting pass spreads over
 
+static_assert(kLbBlock == (kDataWaves + 1) * kWave, "one control wavefront");
 static_assert(static_cast<int64_t>(kMaxTiles) * kTile >= 2147483647LL, "kMaxTiles");
 
 // Scratch header (bytes). Descriptors follow it, one 64-bit word per tile.
@@ -98,93 +114,126 @@ __host__ __device__ inline ScratchView view(void *scratch) {
 }
 
 // --------------------------------------------------------------- loading ---
-// Loads one wavefront chunk: v[j][k] = in[chunk + j*256 + lane*4 + k].
-// `full` (uniform) says the whole tile is in range; otherwise every element is
-// checked against n and missing ones read as 0. VEC selects 128-bit accesses
-// (the array is 16-byte aligned) or 32-bit ones.
+// A chunk is the 1024 elements one wavefront owns: element (j, lane, k) is at
+// chunk + j*256 + lane*4 + k. `rem` (uniform) is the number of valid
+// elements from the chunk's start (>= kChunk: the chunk is full), so validity
+// is a 32-bit compare. Addresses are a uniform base (SGPRs) plus one 32-bit
+// per-lane byte offset. VEC selects 128-bit accesses (the array is 16-byte
+// aligned) or 32-bit ones. Full-chunk 128-bit accesses are nontemporal:
+// every byte is touched once, so streaming it past the caches leaves them to
+// the descriptors (measured faster on MI355X for GiB-sized arrays).
+
+__device__ __forceinline__ uint32_t chunk_rem(int64_t n, int64_t chunk) {
+    const int64_t r = n - chunk;
+    return r <= 0 ? 0u : (r >= kChunk ? static_cast<uint32_t>(kChunk) : static_cast<uint32_t>(r));
+}
+
+__device__ __forceinline__ bool in_chunk(uint32_t rem, int j, int lane, int k) {
+    return static_cast<uint32_t>(j * (kWave * 4) + lane * 4 + k) < rem;
+}
+
 template <bool VEC, class T>
 __device__ __forceinline__ void load_chunk(const T *__restrict__ in, int64_t chunk, int lane,
-                                           int64_t n, bool full, T (&v)[kLoads][4]) {
+                                           uint32_t rem, T (&v)[kLoads][4]) {
     static_assert(sizeof(T) == 4, "32-bit elements");
-    if (full) {
+    const char *base = reinterpret_cast<const char *>(in + chunk);
+    const uint32_t lane_off = static_cast<uint32_t>(lane) * 16u;
+    if (rem >= static_cast<uint32_t>(kChunk)) {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+            const char *bj = base + j * (kWave * 16);
             if constexpr (VEC) {
-                const u32x4 q = *reinterpret_cast<const u32x4 *>(in + at);
+                const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(bj + lane_off));
                 v[j][0] = from_u32<T>(q[0]);
                 v[j][1] = from_u32<T>(q[1]);
                 v[j][2] = from_u32<T>(q[2]);
                 v[j][3] = from_u32<T>(q[3]);
             } else {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) v[j][k] = in[at + k];
+                for (int k = 0; k < 4; ++k)
+                    v[j][k] = *reinterpret_cast<const T *>(bj + lane_off + 4u * k);
             }
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+            const char *bj = base + j * (kWave * 16);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[j][k] = (at + k < n) ? in[at + k] : T(0);
+            for (int k = 0; k < 4; ++k)
+                v[j][k] = in_chunk(rem, j, lane, k) ? *reinterpret_cast<const T *>(bj + lane_off + 4u * k)
+                                                    : T(0);
         }
     }
 }
 
 template <bool VEC, class T>
-__device__ __forceinline__ void store_chunk(T *out, int64_t chunk, int lane, int64_t n, bool full,
+__device__ __forceinline__ void store_chunk(T *out, int64_t chunk, int lane, uint32_t rem,
                                             const T (&v)[kLoads][4]) {
-    if (full) {
+    char *base = reinterpret_cast<char *>(out + chunk);
+    const uint32_t lane_off = static_cast<uint32_t>(lane) * 16u;
+    if (rem >= static_cast<uint32_t>(kChunk)) {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+            char *bj = base + j * (kWave * 16);
             if constexpr (VEC) {
                 u32x4 q;
                 q[0] = to_u32(v[j][0]);
                 q[1] = to_u32(v[j][1]);
                 q[2] = to_u32(v[j][2]);
                 q[3] = to_u32(v[j][3]);
-                *reinterpret_cast<u32x4 *>(out + at) = q;
+                __builtin_nontemporal_store(q, reinterpret_cast<u32x4 *>(bj + lane_off));
             } else {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) out[at + k] = v[j][k];
+                for (int k = 0; k < 4; ++k) *reinterpret_cast<T *>(bj + lane_off + 4u * k) = v[j][k];
             }
         }
     } else {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+            char *bj = base + j * (kWave * 16);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                if (at + k < n) out[at + k] = v[j][k];
+                if (in_chunk(rem, j, lane, k)) *reinterpret_cast<T *>(bj + lane_off + 4u * k) = v[j][k];
         }
     }
 }
 
-// Flag of one element: in range and predicate true.
-template <int P>
-__device__ __forceinline__ bool flag_of(int32_t x, int64_t at, int64_t n, bool full, int32_t pa,
-                                        int32_t pb) {
-    return (full || at < n) && pred_eval<P>(x, pa, pb);
+// Streams staged[0 .. len) to dst_base[0 .. len) with all threads of a
+// workgroup of `block` threads; element i goes to dst_base + i unless
+// dst_base + i >= limit (range check). Uniform base, 32-bit per-lane offset.
+template <int BLOCK>
+__device__ __forceinline__ void stream_out(const int32_t *staged, int32_t *out, uint32_t dst_base,
+                                           uint32_t len, int64_t limit) {
+    int32_t *b = out + dst_base;
+    const uint32_t room = static_cast<int64_t>(dst_base) + len <= limit
+                              ? len
+                              : (limit > dst_base ? static_cast<uint32_t>(limit - dst_base) : 0u);
+    for (uint32_t i = threadIdx.x; i < room; i += BLOCK)
+        __builtin_nontemporal_store(staged[i], reinterpret_cast<int32_t *>(
+                                                   reinterpret_cast<char *>(b) + 4u * i));
 }
 
-// Wavefront-local ranks of one chunk. lead[j] = flagged elements in earlier
-// loads of the chunk plus those of load j in lower lanes; the element's rank
-// inside the chunk is lead[j] + (flagged components before k in its lane).
-// Returns the chunk's flag total (uniform).
+// Wavefront-local ranks of one chunk. Evaluates the predicate once per valid
+// element and records the flags in `mask` at bit (bit0 + j*4 + k).
+// lead[j] = flagged elements in earlier loads of the chunk plus those of
+// load j in lower lanes; the element's rank inside the chunk is lead[j] +
+// (flagged components before k in its lane). Returns the chunk's flag total
+// (uniform).
 template <int P>
-__device__ __forceinline__ uint32_t chunk_ranks(const int32_t (&v)[kLoads][4], int64_t chunk,
-                                                int lane, int64_t n, bool full, int32_t pa,
-                                                int32_t pb, uint32_t (&lead)[kLoads]) {
+__device__ __forceinline__ uint32_t chunk_ranks(const int32_t (&v)[kLoads][4], int lane,
+                                                uint32_t rem, int32_t pa, int32_t pb,
+                                                uint32_t (&lead)[kLoads], uint64_t &mask,
+                                                int bit0) {
     uint32_t running = 0;
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-        const int64_t at = chunk + j * (kWave * 4) + lane * 4;
         uint32_t below = 0;
         uint32_t total = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint64_t m = ballot(flag_of<P>(v[j][k], at + k, n, full, pa, pb));
+            const bool f = in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pa, pb);
+            mask |= static_cast<uint64_t>(f) << (bit0 + j * 4 + k);
+            const uint64_t m = ballot(f);
             below += mbcnt64(m);
             total += static_cast<uint32_t>(__builtin_popcountll(m));
         }
@@ -194,31 +243,65 @@ __device__ __forceinline__ uint32_t chunk_ranks(const int32_t (&v)[kLoads][4], i
     return running;
 }
 
-// Exclusive prefixes over the (sub-tile, wavefront) chunk totals in LDS,
-// read after the barrier that published them: for every sub-tile q,
-// chunk_before[q] = total of chunks before (q, w) in tile order, and
-// sub_before[q] = total of sub-tiles before q; sub_before[kRounds] is the
-// tile aggregate.
-__device__ __forceinline__ void tile_prefixes(const uint32_t *s_tot, int w,
-                                              uint32_t (&chunk_before)[kRounds],
-                                              uint32_t (&sub_before)[kRounds + 1]) {
-    uint32_t acc = 0;
+__device__ __forceinline__ bool bit(uint64_t mask, int b) { return (mask >> b) & 1u; }
+
+// lead[j] of chunk_ranks, recomputed from the recorded flags (ballots are
+// cheap; keeping lead[] live across the look-back costs registers).
+__device__ __forceinline__ void leads_from_mask(uint64_t mask, int bit0, uint32_t (&lead)[kLoads]) {
+    uint32_t running = 0;
 #pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
-        sub_before[q] = acc;
-        uint32_t mine = 0;
+    for (int j = 0; j < kLoads; ++j) {
+        uint32_t below = 0;
+        uint32_t total = 0;
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            const uint32_t t = s_tot[q * kWaves + i];
-            mine += (i < w) ? t : 0u;
-            acc += t;
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t m = ballot(bit(mask, bit0 + j * 4 + k));
+            below += mbcnt64(m);
+            total += static_cast<uint32_t>(__builtin_popcountll(m));
         }
-        chunk_before[q] = sub_before[q] + mine;
+        lead[j] = running + below;
+        running += total;
     }
-    sub_before[kRounds] = acc;
 }
 
-// Claims the next tile for this workgroup (thread 0 only). Returns
+// Chunk totals of a tile live in LDS in (round q, data wavefront d) order,
+// s_tot[q * kDataWaves + d]. The last data wavefront to finish scans them
+// once (lanes 0..29, one DPP wavefront scan, a fixed order, so the fp32 sums
+// are the same for every reader) into s_pre: s_pre[i] = total of chunks
+// before chunk i, s_pre[kLbRounds * kDataWaves] = tile aggregate.
+constexpr int kChunksPerTile = kLbRounds * kDataWaves;  // 30
+
+template <class Op>
+__device__ __forceinline__ typename Op::T scan_chunk_totals(const uint32_t *s_tot, uint32_t *s_pre,
+                                                            int lane) {
+    using T = typename Op::T;
+    const T mine = lane < kChunksPerTile ? Op::from_bits(s_tot[lane]) : Op::zero();
+    const T incl = wave_inclusive_scan<Op>(mine);
+    const uint32_t up = static_cast<uint32_t>(__shfl_up(static_cast<int>(Op::bits(incl)), 1));
+    if (lane < kChunksPerTile) s_pre[lane] = lane == 0 ? Op::bits(Op::zero()) : up;
+    const T agg = Op::from_bits(static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(Op::bits(incl)), kChunksPerTile - 1)));
+    if (lane == 0) s_pre[kChunksPerTile] = Op::bits(agg);
+    return agg;
+}
+
+// Offsets for data wavefront w after the barrier that follows the scan:
+// chunk_before[q] = total of chunks before (q, w); round_before[q] = total
+// of rounds before q; round_before[kLbRounds] = tile aggregate. Uniform.
+template <class Op>
+__device__ __forceinline__ void tile_prefixes(const uint32_t *s_pre, int w,
+                                              typename Op::T (&chunk_before)[kLbRounds],
+                                              typename Op::T (&round_before)[kLbRounds + 1]) {
+    const int d = w < kDataWaves ? w : 0;
+#pragma unroll
+    for (int q = 0; q < kLbRounds; ++q) {
+        chunk_before[q] = Op::from_bits(uniform(s_pre[q * kDataWaves + d]));
+        round_before[q] = Op::from_bits(uniform(s_pre[q * kDataWaves]));
+    }
+    round_before[kLbRounds] = Op::from_bits(uniform(s_pre[kChunksPerTile]));
+}
+
+// Claims the next tile for this workgroup (one thread). Returns
 // {epoch:32 | tile:32}. The claimer of the last tile resets the counter,
 // advances the epoch, and clears one stale descriptor slot: slot
 // (epoch mod kMaxTiles) when this call does not use it. Over any kMaxTiles
@@ -240,191 +323,243 @@ __device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t n
     return c;
 }
 
+// Arrival of a data wavefront (whole wavefront) after writing its chunk
+// totals to LDS. The last of the kDataWaves to arrive scans the totals into
+// s_pre and publishes the tile's descriptor at once -- {aggregate, A}, or
+// {inclusive, A} for tile 0 -- without waiting for the control wavefront, so a
+// slow look-back never delays the successors. (If this store ever lands after
+// the control wavefront's later {inclusive} store, successors just walk one
+// tile further: both are valid states.)
+template <class Op>
+__device__ __forceinline__ void arrive_and_publish(uint32_t *s_arrive, const uint32_t *s_tot,
+                                                   uint32_t *s_pre, uint64_t *desc, uint32_t tile,
+                                                   uint32_t tag, int lane) {
+    uint32_t before = 0;
+    if (lane == 0)
+        before = __hip_atomic_fetch_add(s_arrive, 1u, __ATOMIC_ACQ_REL,
+                                        __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (uniform(before) == kDataWaves - 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const uint32_t agg = Op::bits(scan_chunk_totals<Op>(s_tot, s_pre, lane));
+        if (lane == 0)
+            publish(desc + tile, tag, tile == 0 ? kStatusInclusive : kStatusAggregate, agg);
+    }
+}
+
 // ===================================================== compaction kernel ---
 // One tile per workgroup, tile number from the atomic counter.
-//   1. claim a tile; issue all sixteen 128-bit loads; flag and rank each
-//      wavefront chunk (ballot + mbcnt); chunk totals to LDS;
-//   2. tile aggregate A and chunk offsets from LDS; publish {aggregate, A}
-//      (tile 0 publishes {inclusive, A});
-//   3. stage sub-tile 0 in LDS while wavefront 0 looks back; publish
-//      {inclusive, base + A};
-//   4. per sub-tile: stage (survivors at their rank; for a partition the
-//      rejected ones after them), barrier, stream the run(s) out, barrier.
+//   control wavefront: claim; walk the look-back for the tile's exclusive
+//     prefix (the survivors of all earlier tiles) while the data load;
+//   data wavefronts: eight 128-bit loads per lane; flag and rank each chunk
+//     (ballot + mbcnt); chunk totals to LDS; the last to arrive publishes
+//     {aggregate, A};
+//   barrier; the control wavefront publishes {inclusive, base + A};
+//   per round: data wavefronts stage the round's survivors in LDS at their
+//     rank (for a partition the rejected ones after them), barrier, all 16
+//     wavefronts stream the run(s) out, barrier.
 // PARTITION reads K from *kept_total (written by the counting pass).
 template <int P, bool VEC, bool PARTITION>
-__global__ __launch_bounds__(kBlock) void select_kernel(
+__global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void select_kernel(
     const int32_t *__restrict__ in, int32_t *__restrict__ out, int64_t n, int32_t pa,
     int32_t pb, void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
     const int32_t *__restrict__ kept_total) {
-    __shared__ int32_t s_stage[kSub];
-    __shared__ uint32_t s_tot[kRounds * kWaves];
-    __shared__ uint32_t s_tile, s_tag, s_base;
+    __shared__ int32_t s_stage[kLbSub];
+    __shared__ uint32_t s_tot[kChunksPerTile];
+    __shared__ uint32_t s_pre[kChunksPerTile + 1];
+    __shared__ uint32_t s_tile, s_tag, s_base, s_arrive;
 
     const ScratchView sv = view(scratch);
     if (threadIdx.x == 0) {
         const uint64_t c = claim_tile(sv, num_tiles, capacity);
         s_tile = static_cast<uint32_t>(c);
         s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
+        s_arrive = 0;
     }
     __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint32_t tag = s_tag;
+    const uint32_t tile = uniform(s_tile);
+    const uint32_t tag = uniform(s_tag);
     if (tile >= num_tiles) return;  // only if the scratch was never initialised
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
-    const bool full = tile_start + kTile <= n;
 
-    int32_t v[kRounds][kLoads][4];
-#pragma unroll
-    for (int q = 0; q < kRounds; ++q)
-        load_chunk<VEC>(in, tile_start + q * kSub + w * kChunk, lane, n, full, v[q]);
+    // Both branches below pass the same barriers (B1, then 2 per round but
+    // the last): the control wavefront never holds the data registers.
+    const auto write_round = [&](int q, uint32_t base, const uint32_t (&round_before)[kLbRounds + 1],
+                                 uint32_t kept) {
+        const int64_t round_start = tile_start + q * kLbSub;
+        const uint32_t a_q = round_before[q + 1] - round_before[q];
+        const uint32_t kept_base = base + round_before[q];  // survivors before this round
+        // Range-checked against n: a correct look-back never trips it; a
+        // broken one gives wrong results instead of stray writes.
+        stream_out<kLbBlock>(s_stage, out, kept_base, a_q, n);
+        if constexpr (PARTITION) {
+            const int64_t left = n - round_start;
+            const uint32_t len = left >= kLbSub ? static_cast<uint32_t>(kLbSub)
+                                                : (left > 0 ? static_cast<uint32_t>(left) : 0u);
+            // rejected elements before this round = round_start - kept_base
+            const uint32_t rej_before = static_cast<uint32_t>(round_start) - kept_base;
+            stream_out<kLbBlock>(s_stage + a_q, out, kept + rej_before, len - a_q, n);
+        }
+    };
 
-    uint32_t lead[kRounds][kLoads];
+    if (w == kCtrlWave) {
+        uint32_t prefix = 0;
+        if (tile != 0) prefix = look_back<SumU32>(sv.desc, tile, tag, sv.timed_out);
+        if (lane == 0) s_base = prefix;
+        __syncthreads();  // B1
+        uint32_t chunk_before[kLbRounds];
+        uint32_t round_before[kLbRounds + 1];
+        tile_prefixes<SumU32>(s_pre, 0, chunk_before, round_before);
+        const uint32_t agg = round_before[kLbRounds];
+        if (lane == 0) {
+            if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, prefix + agg);
+            if (!PARTITION && tile == num_tiles - 1) *count = static_cast<int32_t>(prefix + agg);
+        }
+        const uint32_t kept = PARTITION ? static_cast<uint32_t>(*kept_total) : 0u;
 #pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
-        const uint32_t t = chunk_ranks<P>(v[q], tile_start + q * kSub + w * kChunk, lane, n, full,
-                                          pa, pb, lead[q]);
-        if (lane == 0) s_tot[q * kWaves + w] = t;
+        for (int q = 0; q < kLbRounds; ++q) {
+            __syncthreads();  // round q staged
+            write_round(q, prefix, round_before, kept);
+            if (q + 1 < kLbRounds) __syncthreads();  // LDS free for the next round
+        }
+        return;
     }
-    __syncthreads();
-    uint32_t chunk_before[kRounds];
-    uint32_t sub_before[kRounds + 1];
-    tile_prefixes(s_tot, w, chunk_before, sub_before);
-    const uint32_t agg = sub_before[kRounds];
 
-    if (threadIdx.x == 0)
-        publish(sv.desc + tile, tag, tile == 0 ? kStatusInclusive : kStatusAggregate, agg);
+    int32_t v[kLbRounds][kLoads][4];
+    uint64_t fmask = 0;  // flag of (q, j, k) at bit q*16 + j*4 + k
+    static_assert(kLbRounds * kLoads * 4 <= 64, "flags of one lane fit a 64-bit mask");
+#pragma unroll
+    for (int q = 0; q < kLbRounds; ++q) {
+        const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
+        load_chunk<VEC>(in, chunk, lane, chunk_rem(n, chunk), v[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < kLbRounds; ++q) {
+        const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
+        uint32_t lead[kLoads];
+        const uint32_t t = chunk_ranks<P>(v[q], lane, chunk_rem(n, chunk), pa, pb, lead, fmask,
+                                          q * kLoads * 4);
+        if (lane == 0) s_tot[q * kDataWaves + w] = t;
+    }
+    arrive_and_publish<SumU32>(&s_arrive, s_tot, s_pre, sv.desc, tile, tag, lane);
+    __syncthreads();  // B1
+    const uint32_t base = uniform(s_base);
+    uint32_t chunk_before[kLbRounds];
+    uint32_t round_before[kLbRounds + 1];
+    tile_prefixes<SumU32>(s_pre, w, chunk_before, round_before);
+    const uint32_t kept = PARTITION ? static_cast<uint32_t>(*kept_total) : 0u;
 
-    // Stage sub-tile q in LDS: survivors at their rank inside the sub-tile,
-    // and for a partition the rejected elements after them at
-    // A_q + (index in sub-tile - rank in sub-tile).
-    auto stage = [&](int q) {
-        const int64_t chunk = tile_start + q * kSub + w * kChunk;
-        const uint32_t a_q = sub_before[q + 1] - sub_before[q];
+#pragma unroll
+    for (int q = 0; q < kLbRounds; ++q) {
+        // Stage: survivors at their rank inside the round; for a partition
+        // the rejected after them at a_q + (index - rank).
+        const uint32_t a_q = round_before[q + 1] - round_before[q];
+        const uint32_t rem = chunk_rem(n, tile_start + q * kLbSub + w * kChunk);
+        uint32_t lead[kLoads];
+        leads_from_mask(fmask, q * kLoads * 4, lead);
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
-            uint32_t r = chunk_before[q] - sub_before[q] + lead[q][j];
+            uint32_t r = chunk_before[q] - round_before[q] + lead[j];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const bool f = flag_of<P>(v[q][j][k], at + k, n, full, pa, pb);
+                const bool f = bit(fmask, q * kLoads * 4 + j * 4 + k);
                 if (f) {
                     s_stage[r] = v[q][j][k];
                 } else if constexpr (PARTITION) {
                     const uint32_t local =
                         static_cast<uint32_t>(w * kChunk + j * (kWave * 4) + lane * 4 + k);
-                    if (full || at + k < n) s_stage[a_q + local - r] = v[q][j][k];
+                    if (in_chunk(rem, j, lane, k)) s_stage[a_q + local - r] = v[q][j][k];
                 }
                 r += f ? 1u : 0u;
             }
         }
-    };
-
-    stage(0);
-    if (w == 0) {
-        uint32_t base = 0;
-        if (tile != 0) {
-            base = look_back<SumU32>(sv.desc, tile, tag, sv.timed_out);
-            if (lane == 0) publish(sv.desc + tile, tag, kStatusInclusive, base + agg);
-        }
-        if (lane == 0) {
-            s_base = base;
-            if (!PARTITION && tile == num_tiles - 1) *count = static_cast<int32_t>(base + agg);
-        }
-    }
-    __syncthreads();
-    const uint32_t base = s_base;
-    const uint32_t kept = PARTITION ? static_cast<uint32_t>(*kept_total) : 0u;
-
-#pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
-        if (q > 0) {
-            stage(q);
-            __syncthreads();
-        }
-        const uint32_t a_q = sub_before[q + 1] - sub_before[q];
-        const uint32_t kept_base = base + sub_before[q];  // survivors before this sub-tile
-        if constexpr (!PARTITION) {
-            // Range-checked: a correct look-back never trips it; a broken one
-            // gives wrong results instead of stray writes.
-            for (uint32_t i = threadIdx.x; i < a_q; i += kBlock)
-                if (kept_base + i < n) out[kept_base + i] = s_stage[i];
-        } else {
-            const int64_t sub_start = tile_start + q * kSub;
-            const int64_t left = n - sub_start;
-            const uint32_t len =
-                left >= kSub ? static_cast<uint32_t>(kSub) : (left > 0 ? static_cast<uint32_t>(left) : 0u);
-            // rejected elements before this sub-tile = sub_start - kept_base
-            const uint32_t rej_base = kept + static_cast<uint32_t>(sub_start) - kept_base - a_q;
-            for (uint32_t i = threadIdx.x; i < len; i += kBlock) {
-                const uint32_t dst = (i < a_q ? kept_base : rej_base) + i;
-                if (dst < n) out[dst] = s_stage[i];
-            }
-        }
-        __syncthreads();
+        __syncthreads();  // round q staged
+        write_round(q, base, round_before, kept);
+        if (q + 1 < kLbRounds) __syncthreads();  // LDS free for the next round
     }
 
     if constexpr (!PARTITION) {
         if (ranks != nullptr) {
 #pragma unroll
-            for (int q = 0; q < kRounds; ++q) {
-                const int64_t chunk = tile_start + q * kSub + w * kChunk;
+            for (int q = 0; q < kLbRounds; ++q) {
+                const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
                 int32_t rk[kLoads][4];
+                uint32_t lead[kLoads];
+                leads_from_mask(fmask, q * kLoads * 4, lead);
 #pragma unroll
                 for (int j = 0; j < kLoads; ++j) {
-                    const int64_t at = chunk + j * (kWave * 4) + lane * 4;
-                    uint32_t r = base + chunk_before[q] + lead[q][j];
+                    uint32_t r = base + chunk_before[q] + lead[j];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         rk[j][k] = static_cast<int32_t>(r);
-                        r += flag_of<P>(v[q][j][k], at + k, n, full, pa, pb) ? 1u : 0u;
+                        r += bit(fmask, q * kLoads * 4 + j * 4 + k) ? 1u : 0u;
                     }
                 }
-                store_chunk<VEC>(ranks, chunk, lane, n, full, rk);
+                store_chunk<VEC>(ranks, chunk, lane, chunk_rem(n, chunk), rk);
             }
         }
     }
 }
 
 // =========================================================== scan kernel ---
-// Exclusive scan of 32-bit values with the same tile shape and look-back;
-// the tile aggregate is the sum of the values. Per load j a lane sums its 4
-// values, a DPP wavefront scan gives the lane offsets, and results leave
-// with the same 128-bit layout they were read with. in == out is allowed.
+// Exclusive scan of 32-bit values with the same tile shape, control
+// wavefront and look-back; the tile aggregate is the sum of the values. Per
+// load j a lane sums its 4 values, a DPP wavefront scan gives the lane
+// offsets, and results leave with the same 128-bit layout they were read
+// with. in == out is allowed.
 template <class Op, bool VEC>
-__global__ __launch_bounds__(kBlock) void scan_kernel(const typename Op::T *in,
-                                                      typename Op::T *out, int64_t n,
-                                                      void *scratch, uint32_t num_tiles,
-                                                      uint32_t capacity, typename Op::T *total) {
+__global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void scan_kernel(const typename Op::T *in,
+                                                        typename Op::T *out, int64_t n,
+                                                        void *scratch, uint32_t num_tiles,
+                                                        uint32_t capacity, typename Op::T *total) {
     using T = typename Op::T;
-    __shared__ uint32_t s_tot[kRounds * kWaves];
-    __shared__ uint32_t s_tile, s_tag, s_base;
+    __shared__ uint32_t s_tot[kChunksPerTile];
+    __shared__ uint32_t s_pre[kChunksPerTile + 1];
+    __shared__ uint32_t s_tile, s_tag, s_base, s_arrive;
 
     const ScratchView sv = view(scratch);
     if (threadIdx.x == 0) {
         const uint64_t c = claim_tile(sv, num_tiles, capacity);
         s_tile = static_cast<uint32_t>(c);
         s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
+        s_arrive = 0;
     }
     __syncthreads();
-    const uint32_t tile = s_tile;
-    const uint32_t tag = s_tag;
+    const uint32_t tile = uniform(s_tile);
+    const uint32_t tag = uniform(s_tag);
     if (tile >= num_tiles) return;  // only if the scratch was never initialised
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
-    const bool full = tile_start + kTile <= n;
 
-    T v[kRounds][kLoads][4];
-#pragma unroll
-    for (int q = 0; q < kRounds; ++q)
-        load_chunk<VEC>(in, tile_start + q * kSub + w * kChunk, lane, n, full, v[q]);
+    if (w == kCtrlWave) {
+        T prefix = Op::zero();
+        if (tile != 0) prefix = look_back<Op>(sv.desc, tile, tag, sv.timed_out);
+        if (lane == 0) s_base = Op::bits(prefix);
+        __syncthreads();  // B1
+        T chunk_before[kLbRounds];
+        T round_before[kLbRounds + 1];
+        tile_prefixes<Op>(s_pre, 0, chunk_before, round_before);
+        const T agg = round_before[kLbRounds];
+        if (lane == 0) {
+            if (tile != 0)
+                publish(sv.desc + tile, tag, kStatusInclusive, Op::bits(Op::add(prefix, agg)));
+            if (total != nullptr && tile == num_tiles - 1) *total = Op::add(prefix, agg);
+        }
+        return;
+    }
 
-    // Replace each value by its exclusive prefix inside the wavefront chunk.
+    T v[kLbRounds][kLoads][4];
 #pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
+    for (int q = 0; q < kLbRounds; ++q) {
+        const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
+        load_chunk<VEC>(in, chunk, lane, chunk_rem(n, chunk), v[q]);  // missing read as 0
+    }
+    // Replace each value by its exclusive prefix inside the chunk.
+#pragma unroll
+    for (int q = 0; q < kLbRounds; ++q) {
         T running = Op::zero();
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
@@ -445,49 +580,23 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(const typename Op::T *in,
                                            __builtin_amdgcn_readlane(
                                                static_cast<int>(Op::bits(incl)), kWave - 1))));
         }
-        if (lane == 0) s_tot[q * kWaves + w] = Op::bits(running);
+        if (lane == 0) s_tot[q * kDataWaves + w] = Op::bits(running);
     }
-    __syncthreads();
-    T chunk_before[kRounds];
-    T agg = Op::zero();
+    arrive_and_publish<Op>(&s_arrive, s_tot, s_pre, sv.desc, tile, tag, lane);
+    __syncthreads();  // B1
+    const T base = Op::from_bits(uniform(s_base));
+    T chunk_before[kLbRounds];
+    T round_before[kLbRounds + 1];
+    tile_prefixes<Op>(s_pre, w, chunk_before, round_before);
 #pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
-        T mine = agg;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i) {
-            const T t = Op::from_bits(s_tot[q * kWaves + i]);
-            if (i < w) mine = Op::add(mine, t);
-            agg = Op::add(agg, t);
-        }
-        chunk_before[q] = mine;
-    }
-    if (threadIdx.x == 0)
-        publish(sv.desc + tile, tag, tile == 0 ? kStatusInclusive : kStatusAggregate,
-                Op::bits(agg));
-
-    if (w == 0) {
-        T base = Op::zero();
-        if (tile != 0) {
-            base = look_back<Op>(sv.desc, tile, tag, sv.timed_out);
-            if (lane == 0)
-                publish(sv.desc + tile, tag, kStatusInclusive, Op::bits(Op::add(base, agg)));
-        }
-        if (lane == 0) {
-            s_base = Op::bits(base);
-            if (total != nullptr && tile == num_tiles - 1) *total = Op::add(base, agg);
-        }
-    }
-    __syncthreads();
-    const T base = Op::from_bits(s_base);
-
-#pragma unroll
-    for (int q = 0; q < kRounds; ++q) {
+    for (int q = 0; q < kLbRounds; ++q) {
         const T chunk_base = Op::add(base, chunk_before[q]);
 #pragma unroll
         for (int j = 0; j < kLoads; ++j)
 #pragma unroll
             for (int k = 0; k < 4; ++k) v[q][j][k] = Op::add(chunk_base, v[q][j][k]);
-        store_chunk<VEC>(out, tile_start + q * kSub + w * kChunk, lane, n, full, v[q]);
+        const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
+        store_chunk<VEC>(out, chunk, lane, chunk_rem(n, chunk), v[q]);
     }
 }
 
@@ -508,19 +617,16 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t *__restrict
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     uint32_t acc = 0;
     for (uint32_t sub = blockIdx.x; sub < num_subs; sub += gridDim.x) {
-        const int64_t sub_start = static_cast<int64_t>(sub) * kSub;
-        const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
-        const bool full = sub_start + kSub <= n;
+        const int64_t chunk = static_cast<int64_t>(sub) * kSub + static_cast<int64_t>(w) * kChunk;
+        const uint32_t rem = chunk_rem(n, chunk);
         int32_t v[kLoads][4];
-        load_chunk<VEC>(in, chunk, lane, n, full, v);
+        load_chunk<VEC>(in, chunk, lane, rem, v);
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
+        for (int j = 0; j < kLoads; ++j)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 acc += static_cast<uint32_t>(__builtin_popcountll(
-                    ballot(flag_of<P>(v[j][k], at + k, n, full, pa, pb))));
-        }
+                    ballot(in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pa, pb))));
     }
     if (lane == 0) s_cnt[w] = acc;
     __syncthreads();
@@ -559,17 +665,15 @@ __global__ __launch_bounds__(kBlock) void bit_clear_count_kernel(const uint32_t 
 #pragma unroll
     for (int b = 0; b < 32; ++b) acc[b] = 0;
     for (uint32_t sub = blockIdx.x; sub < num_subs; sub += gridDim.x) {
-        const int64_t sub_start = static_cast<int64_t>(sub) * kSub;
-        const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
-        const bool full = sub_start + kSub <= n;
+        const int64_t chunk = static_cast<int64_t>(sub) * kSub + static_cast<int64_t>(w) * kChunk;
+        const uint32_t rem = chunk_rem(n, chunk);
         uint32_t v[kLoads][4];
-        load_chunk<VEC>(in, chunk, lane, n, full, v);
+        load_chunk<VEC>(in, chunk, lane, rem, v);
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const bool valid = full || at + k < n;
+                const bool valid = in_chunk(rem, j, lane, k);
                 const uint32_t x = v[j][k];
 #pragma unroll
                 for (int b = 0; b < 32; ++b)
@@ -619,14 +723,15 @@ __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *_
     __shared__ uint32_t s_slot;
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
-    const int64_t sub_start = static_cast<int64_t>(blockIdx.x) * kSub;
-    const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
-    const bool full = sub_start + kSub <= n;
+    const int64_t chunk =
+        static_cast<int64_t>(blockIdx.x) * kSub + static_cast<int64_t>(w) * kChunk;
+    const uint32_t rem = chunk_rem(n, chunk);
     int32_t v[kLoads][4];
-    load_chunk<VEC>(in, chunk, lane, n, full, v);
+    load_chunk<VEC>(in, chunk, lane, rem, v);
     if constexpr (VARIANT == 0) {
         uint32_t lead[kLoads];
-        const uint32_t t = chunk_ranks<P>(v, chunk, lane, n, full, pa, pb, lead);
+        uint64_t fmask = 0;
+        const uint32_t t = chunk_ranks<P>(v, lane, rem, pa, pb, lead, fmask, 0);
         if (lane == 0) s_tot[w] = t;
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -642,11 +747,10 @@ __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *_
         for (int i = 0; i < w; ++i) slot += s_tot[i];
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
             uint32_t r = slot + lead[j];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                if (flag_of<P>(v[j][k], at + k, n, full, pa, pb)) {
+                if (bit(fmask, j * 4 + k)) {
                     if (r < n) out[r] = v[j][k];
                     ++r;
                 }
@@ -655,10 +759,9 @@ __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *_
     } else {
 #pragma unroll
         for (int j = 0; j < kLoads; ++j) {
-            const int64_t at = chunk + j * (kWave * 4) + lane * 4;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                if (flag_of<P>(v[j][k], at + k, n, full, pa, pb)) {
+                if (in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pa, pb)) {
                     const int32_t slot = __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED,
                                                                 __HIP_MEMORY_SCOPE_AGENT);
                     if (slot < n) out[slot] = v[j][k];
@@ -674,12 +777,12 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const int32_t *__restrict_
                                                       int32_t *__restrict__ out, int64_t n) {
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
-    const int64_t sub_start = static_cast<int64_t>(blockIdx.x) * kSub;
-    const int64_t chunk = sub_start + static_cast<int64_t>(w) * kChunk;
-    const bool full = sub_start + kSub <= n;
+    const int64_t chunk =
+        static_cast<int64_t>(blockIdx.x) * kSub + static_cast<int64_t>(w) * kChunk;
+    const uint32_t rem = chunk_rem(n, chunk);
     int32_t v[kLoads][4];
-    load_chunk<VEC>(in, chunk, lane, n, full, v);
-    store_chunk<VEC>(out, chunk, lane, n, full, v);
+    load_chunk<VEC>(in, chunk, lane, rem, v);
+    store_chunk<VEC>(out, chunk, lane, rem, v);
 }
 
 // Clears `words` 32-bit words (a kernel rather than a memset node).
@@ -808,10 +911,10 @@ struct LaunchSelect {
                    const int32_t *kept, hipStream_t s) {
         const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
         if (partition)
-            hipLaunchKernelGGL((select_kernel<P, VEC, true>), dim3(tiles), dim3(kBlock), 0, s, in,
+            hipLaunchKernelGGL((select_kernel<P, VEC, true>), dim3(tiles), dim3(kLbBlock), 0, s, in,
                                out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
         else
-            hipLaunchKernelGGL((select_kernel<P, VEC, false>), dim3(tiles), dim3(kBlock), 0, s, in,
+            hipLaunchKernelGGL((select_kernel<P, VEC, false>), dim3(tiles), dim3(kLbBlock), 0, s, in,
                                out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
         return launched();
     }
@@ -868,10 +971,10 @@ int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename
     const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
     const uint32_t cap = capacity_of(scratch_bytes);
     if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL((scan_kernel<Op, true>), dim3(tiles), dim3(kBlock), 0, s, in, out, n,
+        hipLaunchKernelGGL((scan_kernel<Op, true>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
                            scratch, tiles, cap, total);
     else
-        hipLaunchKernelGGL((scan_kernel<Op, false>), dim3(tiles), dim3(kBlock), 0, s, in, out, n,
+        hipLaunchKernelGGL((scan_kernel<Op, false>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
                            scratch, tiles, cap, total);
     return launched();
 }

@@ -133,23 +133,48 @@ __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
 }
 
 // Decoupled look-back, run by one whole wavefront of the tile's workgroup.
-// Reads the descriptors of the 64 tiles just below `tile` at once; while any
-// of them has published nothing in this call it sleeps and reads again. Once
-// all 64 have published, the nearest inclusive one ends the walk: the result
-// is its value plus the aggregates above it. With no inclusive value in the
-// window all 64 aggregates are added and the window moves 64 tiles down.
-// Tiles below 0 count as inclusive with value 0. Returns the exclusive prefix
+//
+// Waiting: first the wavefront polls only the immediate predecessor's
+// descriptor (one lane, one 8-byte agent-scope load), sleeping about 3.4 us
+// (s_sleep 127) between polls, until it has published. Measured on MI355X,
+// frequent coherent polling by hundreds of waiting tiles costs more
+// throughput than it saves latency: shorter sleeps and wider polls were
+// slower.
+//
+// Walking: then each step reads the descriptors of the 64 tiles just below
+// the window end at once (one load, 512 contiguous bytes). While any tile in the window has
+// published nothing in this call it polls again. Once all have published,
+// the nearest inclusive one ends the walk: the result is its value plus the
+// aggregates above it. With no inclusive value in the window all aggregates
+// are added and the window moves down. Tiles below 0 count as inclusive with
+// value 0. Waiting for the whole window costs nothing extra: an {inclusive}
+// tile implies every lower tile has published. Returns the exclusive prefix
 // of `tile` (the total of tiles 0..tile-1) in every lane.
 //
 // Forward progress: a tile only waits on lower-numbered tiles, whose numbers
-// were claimed earlier by workgroups that are already running, and tile 0
-// never waits.
+// were claimed earlier by workgroups that are already running and whose
+// aggregates are published without waiting on anything; tile 0 never waits.
 //
-// The wait is bounded: after kSpinLimit re-reads without progress (seconds,
-// far beyond any legitimate wait) the walk stops, *timed_out is set to 1 and
-// the partial prefix is returned, so a fault elsewhere can corrupt results
-// but can never leave the kernel spinning.
-constexpr uint32_t kSpinLimit = 1u << 22;
+// The wait is bounded: after kSpinLimit polls without progress (far beyond
+// any legitimate wait) the walk stops, *timed_out is set to 1 and the
+// partial prefix is returned, so a fault elsewhere can corrupt results but
+// can never leave the kernel spinning.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(127); }
+
+// Descriptor of tile idx (>= 0) read as base + 32-bit byte offset, so the
+// address needs one VGPR; tiles below 0 read as inclusive with value 0.
+__device__ __forceinline__ uint64_t peek_tile(uint64_t *desc, int32_t idx, uint32_t tag) {
+    const uint32_t off = static_cast<uint32_t>(idx < 0 ? 0 : idx) * 8u;
+    const uint64_t w = peek(reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(desc) + off));
+    return idx < 0 ? descriptor(tag, kStatusInclusive, 0u) : w;
+}
+
+__device__ __forceinline__ uint32_t status_of(uint64_t word, uint32_t tag) {
+    const uint32_t hi = static_cast<uint32_t>(word >> 32);
+    return (hi >> 2) == tag ? (hi & 3u) : 0u;
+}
 
 template <class Op>
 __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
@@ -157,32 +182,45 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
     using T = typename Op::T;
     const int lane = lane_id();
     T prefix = Op::zero();
-    int64_t end = static_cast<int64_t>(tile);
     uint32_t spins = 0;
+    // wait on the immediate predecessor alone
     while (true) {
-        const int64_t idx = end - kWave + lane;
+        uint64_t w1 = 0;
+        if (lane == 0) w1 = peek_tile(desc, static_cast<int32_t>(tile) - 1, tag);
+        if (status_of(w1, tag) != 0u && lane == 0) spins |= 0x80000000u;
+        if (uniform(spins) & 0x80000000u) break;
+        if (++spins > kSpinLimit) {
+            if (lane == 0)
+                __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return prefix;
+        }
+        poll_pause();
+    }
+    spins &= 0x7FFFFFFFu;
+    int32_t end = static_cast<int32_t>(tile);
+    while (true) {
         uint64_t word;
-        uint32_t status;
+        uint32_t st;
         while (true) {
-            word = idx >= 0 ? peek(desc + idx) : descriptor(tag, kStatusInclusive, 0u);
-            const uint32_t hi = static_cast<uint32_t>(word >> 32);
-            status = ((hi >> 2) == tag) ? (hi & 3u) : 0u;
-            if (ballot(status == 0u) == 0) break;
+            word = peek_tile(desc, end - kWave + lane, tag);
+            st = status_of(word, tag);
+            if (ballot(st == 0u) == 0) break;
             if (++spins > kSpinLimit) {
                 if (lane == 0)
                     __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return prefix;
             }
-            __builtin_amdgcn_s_sleep(1);
+            poll_pause();
         }
-        const uint64_t inclusive = ballot(status == kStatusInclusive);
-        const T value = Op::from_bits(static_cast<uint32_t>(word));
-        if (inclusive != 0) {
-            const int top = 63 - __builtin_clzll(inclusive);
-            prefix = Op::add(prefix, wave_sum<Op>(lane >= top ? value : Op::zero()));
-            return prefix;
-        }
-        prefix = Op::add(prefix, wave_sum<Op>(value));
+        // nearest inclusive tile = highest lane with status inclusive; add
+        // the values from it up (all 64 when there is none)
+        const uint64_t inclusive = ballot(st == kStatusInclusive);
+        const int top = inclusive ? 63 - __builtin_clzll(inclusive) : -1;
+        const T mine = lane >= top ? Op::from_bits(static_cast<uint32_t>(word)) : Op::zero();
+        const T all = wave_inclusive_scan<Op>(mine);
+        prefix = Op::add(prefix, Op::from_bits(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                                     static_cast<int>(Op::bits(all)), kWave - 1))));
+        if (inclusive) return prefix;
         end -= kWave;
     }
 }

@@ -67,12 +67,12 @@ def test_enum_numbering_agrees_with_oracle_and_binding():
 def test_tile_and_scratch_sizes():
     L = ssc.lib()
     T = L.ssc_tile_elems()
-    assert T == 32768
+    assert T == 30720          # 2 rounds x 15 data wavefronts x 1024 elements
     for n in (0, 1, T - 1, T, T + 1, 2**28, INT32_MAX):
         tiles = (n + T - 1) // T
         assert L.ssc_scratch_bytes(n) == 512 + 8 * tiles
         assert L.ssc_radix_sort_scratch_bytes(n) == 512 + 8 * tiles
-    assert L.ssc_scratch_bytes(INT32_MAX) == 512 + 8 * 65536
+    assert L.ssc_scratch_bytes(INT32_MAX) == 512 + 8 * 69906
     assert L.ssc_scratch_bytes(-5) == 512
 
 

@@ -5,7 +5,8 @@ relative of the fp64 oracle (bit-exact where every prefix is an exact
 integer below 2^24). The unordered atomic compaction is checked as a
 multiset. Inputs come from the seeded generators in
 scan_stream_compaction_amd.workloads, at the five workloads' full sizes and
-at edge sizes around the 32768-element tile and its 8192-element sub-tiles.
+at edge sizes around the 30720-element tile, its 15360-element rounds and
+1024-element wavefront chunks.
 """
 from __future__ import annotations
 
@@ -22,8 +23,9 @@ from tests import checks
 
 pytestmark = pytest.mark.gpu
 
-T = 32768   # elements per tile
-S = 8192    # elements per sub-tile
+T = 30720   # elements per tile (one claim)
+S = 15360   # elements per round (15 data wavefronts x 1024)
+C = 1024    # elements per wavefront chunk
 SENTINEL = -123456789
 DEV = "cuda"
 
@@ -198,9 +200,9 @@ def test_radix_sort_full_size():
 
 # -------------------------------------------------------------- edge cases ---
 
-EDGE_N = [0, 1, 2, 3, 5, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025, S - 1, S, S + 1,
-          3 * S + 5, T - 1, T, T + 1, 2 * T - 1, 2 * T, 2 * T + 1, 5 * T + 611,
-          64 * T + 13, 65 * T + T - 1]
+EDGE_N = [0, 1, 2, 3, 5, 63, 64, 65, 255, 256, 257, C - 1, C, C + 1, 7 * C + 3, S - 1, S,
+          S + 1, T - 1, T, T + 1, 2 * T - 1, 2 * T, 2 * T + 1, 5 * T + 611, 64 * T + 13,
+          65 * T + T - 1]
 
 
 @pytest.mark.parametrize("n", EDGE_N)
