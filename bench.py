@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "ordered compaction GB/s and % HBM peak, 2^28 int32, 50% selectivity"
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_compact_odd_2p28.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "compact_odd_2p28_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "scan_stream_compaction_amd", "csrc", f)
                   for f in ("ssc.hip", "ssc_device.h")]
 
@@ -43,17 +43,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_bytes_alg: float):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
-    when it is missing or was taken from a different kernel source."""
+def measured_traffic():
+    """HBM bytes per launch of the compaction kernel from the committed
+    rocprofv3 PMC summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    counter reads for the copy kernel of known size), or None when the summary
+    is missing or was taken from a different kernel source."""
     try:
         with open(PMC_SUMMARY) as f:
-            s = json.load(f)
-    except (OSError, ValueError):
+            fields = dict(line.split(":", 1) for line in f if line.startswith("- ") and ":" in line)
+    except OSError:
         return None
-    if s.get("kernel_source_sha256_16") != kernel_source_hash():
+    fields = {k[2:].strip(): v.strip() for k, v in fields.items()}
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return s.get("hbm_bytes_per_launch")
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def timed_calls(fn, steps: int, stream):
@@ -121,8 +127,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true",
-                    help="skip the copy / selectivity-sweep / atomic comparison rows")
+    ap.add_argument("--extra", choices=("all", "copy", "none"), default="all",
+                    help="extra rows: copy ceiling, selectivity sweep and atomic comparison")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the path is a single-GPU kernel; "
@@ -175,10 +181,10 @@ def main():
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     log(f"compact odd: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s "
         f"({value / HBM_PEAK_GBPS * 100:.1f}% of {HBM_PEAK_GBPS:.0f}), "
-        f"per-launch {kernel_ms * 1e3:.1f} us, wall {wall * 1e3 / args.steps:.1f} us/step")
+        f"per-launch {kernel_ms * 1e3:.1f} us, wall {wall * 1e6 / args.steps:.1f} us/step")
 
     extra = {}
-    if not args.no_extra:
+    if args.extra in ("all", "copy"):
         cp = torch.empty_like(x)
         _, cp_per, _ = timed_calls(lambda: ssc.copy(x, cp), args.steps, stream)
         assert torch.equal(cp, x)
@@ -188,6 +194,7 @@ def main():
                              "bytes": 8 * n}
         extra["compact_odd_pct_of_copy"] = round(achieved / cp_gbps * 100, 1)
         del cp
+    if args.extra == "all":
         for s in wl.SWEEP_KEEP:
             cnt = torch.zeros(1, dtype=torch.int32, device=dev)
             fn = lambda: ssc.compact(x, "mod_lt", wl.SWEEP_MOD, s, out=out, count=cnt,
@@ -212,9 +219,10 @@ def main():
             k_ms = sum(per) / len(per)
             extra[f"atomic_mod100_lt{s}"] = {
                 "us": round(k_ms * 1e3, 2), "GB/s": round(b / (k_ms * 1e-3) / 1e9, 1)}
+    if extra:
         log("extra: " + json.dumps(extra))
 
-    traffic = measured_traffic(alg_bytes)
+    traffic = measured_traffic()
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -243,7 +251,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "select_kernel<odd, 128-bit, compact>",
+            "kernel": "ssc::select_kernel<1, true, false> (odd, 128-bit, compaction)",
             "kernel_us": round(kernel_ms * 1e3, 2),
         },
         "extra": extra,

@@ -19,7 +19,7 @@
  *     scan of 0/1 predicate flags whose values are output indices; the odd
  *     predicate is x & 1 (Listing 13-17).
  *   - "Day 32 scan_2.cu", scanExclusiveCpu: exclusive scan with a double
- *     accumulator (the "house rule" of accumulating in double).
+ *     accumulator (partial sums are kept in double precision).
  *   - "CIS 565 Project 2: Stream Compaction": the printed exclusive-scan and
  *     compaction transcripts fix the exclusive convention and the order.
  *

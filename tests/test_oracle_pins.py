@@ -179,7 +179,7 @@ def test_empty_inputs():
     (oracle.PRED_EVEN, 0, 0, 10), (oracle.PRED_BIT_SET, 7, 0, 1 << 31),
     (oracle.PRED_BIT_CLEAR, 30, 0, 1 << 31), (oracle.PRED_MOD_LT, 100, 50, 1 << 31)])
 def test_count_is_top_of_scan(pred, pa, pb, k):
-    """"Day 33 compaction.cu": the survivor count falls out of the top of the scan."""
+    """"Day 33 compaction.cu": the survivor count is the last prefix plus the last flag."""
     from scan_stream_compaction_amd import workloads
     x = (workloads.hi32(99 + pred, 50_001).astype(np.int64) % k).astype(np.int32) \
         if k < (1 << 31) else workloads.full_int32(99 + pred, 50_001)
