@@ -302,18 +302,20 @@ __device__ __forceinline__ void tile_prefixes(const uint32_t *s_pre, int w,
 }
 
 // Claims the next tile for this workgroup (one thread). Returns
-// {epoch:32 | tile:32}. The claimer of the last tile resets the counter,
-// advances the epoch, and clears one stale descriptor slot: slot
-// (epoch mod kMaxTiles) when this call does not use it. Over any kMaxTiles
-// consecutive calls every slot is thus rewritten or cleared, far within the
-// 2^30-call period of the tag, so no stale descriptor can match a later tag.
+// {epoch:32 | tile:32}. A call makes exactly `claims` claims in all; the one
+// that receives the last number resets the counter and advances the epoch
+// (every claim of a call therefore carries the same epoch), and clears one
+// stale descriptor slot: slot (epoch mod kMaxTiles) when this call does not
+// use it. Over any kMaxTiles consecutive calls every slot is thus rewritten
+// or cleared, far within the 2^30-call period of the tag, so no stale
+// descriptor can match a later tag.
 __device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t num_tiles,
-                                               uint32_t capacity) {
+                                               uint32_t claims, uint32_t capacity) {
     const uint64_t c =
         __hip_atomic_fetch_add(sv.claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t tile = static_cast<uint32_t>(c);
     const uint32_t epoch = static_cast<uint32_t>(c >> 32);
-    if (tile == num_tiles - 1) {
+    if (tile == claims - 1) {
         __hip_atomic_store(sv.claim, static_cast<uint64_t>(epoch + 1u) << 32, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t slot = epoch & (kMaxTiles - 1u);
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 
     const ScratchView sv = view(scratch);
     if (threadIdx.x == 0) {
-        const uint64_t c = claim_tile(sv, num_tiles, capacity);
+        const uint64_t c = claim_tile(sv, num_tiles, num_tiles, capacity);
         s_tile = static_cast<uint32_t>(c);
         s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
         s_arrive = 0;
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 
     const ScratchView sv = view(scratch);
     if (threadIdx.x == 0) {
-        const uint64_t c = claim_tile(sv, num_tiles, capacity);
+        const uint64_t c = claim_tile(sv, num_tiles, num_tiles, capacity);
         s_tile = static_cast<uint32_t>(c);
         s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
         s_arrive = 0;

@@ -161,7 +161,10 @@ __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
 // can never leave the kernel spinning.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(127); }
+#ifndef SSC_POLL_SLEEP
+#define SSC_POLL_SLEEP 127  // s_sleep units of 64 clocks
+#endif
+__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(SSC_POLL_SLEEP); }
 
 // Descriptor of tile idx (>= 0) read as base + 32-bit byte offset, so the
 // address needs one VGPR; tiles below 0 read as inclusive with value 0.
