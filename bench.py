@@ -121,6 +121,88 @@ def cpu_baseline(x_np, target_s: float = 12.0):
     }
 
 
+def other_workloads(dev, steps: int, stream) -> dict:
+    """The other workloads of the method, each checked against torch before it
+    is timed: per-launch time from HIP events and effective GB/s over the
+    algorithmic bytes. Their working sets (at most 128 MiB) fit the 256 MB
+    Infinity Cache, so these rates are not HBM roofline figures."""
+    import numpy as np
+    import torch
+
+    import scan_stream_compaction_amd as ssc
+    from scan_stream_compaction_amd import workloads as wl
+
+    rows = {}
+
+    def timed(name, fn, alg_bytes, **info):
+        fn()
+        _, per, _ = timed_calls(fn, steps, stream)
+        us = sum(per) / len(per) * 1e3
+        rows[name] = {"us": round(us, 2), "effective_GB/s": round(alg_bytes / (us * 1e-6) / 1e9, 1),
+                      "algorithmic_bytes": alg_bytes, **info}
+
+    def excl(t):
+        c = torch.cumsum(t.to(torch.int64), 0)
+        return (c - t.to(torch.int64)).to(torch.int32)
+
+    # 65,533 values in [0, 4); nonzero kept; out, count and ranks
+    x = torch.from_numpy(wl.small_compact_input()).to(dev)
+    n = x.numel()
+    sc = ssc.new_scratch(n, dev)
+    out, cnt, rk = ssc.compact(x, "nonzero", ranks=True, scratch=sc)
+    mask = x != 0
+    k = int(mask.sum())
+    assert int(cnt.item()) == k and torch.equal(out[:k], x[mask]) and torch.equal(rk, excl(mask.int()))
+    timed("compact_nonzero_ranks_65533", lambda: ssc.compact(x, "nonzero", out=out, count=cnt, ranks=rk,
+                                                             scratch=sc), 4 * n + 4 * k + 4 * n, kept=k)
+
+    # 8,387,997 values in [0, 10): zero removal and even/odd partition
+    x = torch.from_numpy(wl.zero_removal_input()).to(dev)
+    n = x.numel()
+    sc = ssc.new_scratch(n, dev)
+    out, cnt = ssc.compact(x, "nonzero", scratch=sc)
+    mask = x != 0
+    k = int(mask.sum())
+    assert int(cnt.item()) == k and torch.equal(out[:k], x[mask])
+    timed("compact_nonzero_8387997", lambda: ssc.compact(x, "nonzero", out=out, count=cnt, scratch=sc),
+          4 * n + 4 * k, kept=k)
+    out, cnt = ssc.partition(x, "even", scratch=sc)
+    ev = (x & 1) == 0
+    k = int(ev.sum())
+    assert int(cnt.item()) == k and torch.equal(out, torch.cat([x[ev], x[~ev]]))
+    timed("partition_even_8387997", lambda: ssc.partition(x, "even", out=out, count=cnt, scratch=sc),
+          8 * n, kept=k, note="algorithmic 8N; the counting pre-pass adds a 4N read")
+
+    # 10^7 scans: int32 (i % 8) + 1 and fp32 uniform [0, 1)
+    x = torch.from_numpy(wl.mod8_plus1(wl.N_SCAN)).to(dev)
+    n = x.numel()
+    sc = ssc.new_scratch(n, dev)
+    out, tot = ssc.exclusive_scan(x, scratch=sc)
+    assert torch.equal(out, excl(x)) and int(tot.item()) == 45_000_000
+    timed("scan_i32_1e7", lambda: ssc.exclusive_scan(x, out=out, total=tot, scratch=sc), 8 * n)
+    x = torch.from_numpy(wl.scan_f32_input()).to(dev)
+    outf, totf = ssc.exclusive_scan(x, scratch=sc)
+    ref = torch.cumsum(x.to(torch.float64), 0) - x.to(torch.float64)
+    rel = ((outf.to(torch.float64) - ref).abs() / ref.abs().clamp_min(1e-300))[1:]
+    assert float(rel.max()) <= 1e-5 and float(outf[0]) == 0.0
+    timed("scan_f32_1e7", lambda: ssc.exclusive_scan(x, out=outf, total=totf, scratch=sc), 8 * n,
+          max_rel_err=float(rel.max()))
+
+    # 2^24 uint32 keys: 32 chained stable partitions by bit
+    x = torch.from_numpy(wl.radix_input().view(np.int32)).to(dev)
+    n = x.numel()
+    sc = ssc.new_scratch(n, dev, radix=True)
+    out = torch.empty_like(x)
+    tmp = torch.empty_like(x)
+    ssc.radix_sort(x, out=out, tmp=tmp, scratch=sc)
+    want = torch.sort(x.to(torch.int64) & 0xFFFFFFFF).values
+    assert torch.equal(out.to(torch.int64) & 0xFFFFFFFF, want)
+    timed("radix_sort_u32_2p24", lambda: ssc.radix_sort(x, out=out, tmp=tmp, scratch=sc), 32 * 8 * n,
+          note="32 one-bit passes, 8N algorithmic each; each pass adds a 4N counting read")
+    rows["radix_sort_u32_2p24"]["keys_per_s"] = round(n / (rows["radix_sort_u32_2p24"]["us"] * 1e-6), 1)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +301,8 @@ def main():
             k_ms = sum(per) / len(per)
             extra[f"atomic_mod100_lt{s}"] = {
                 "us": round(k_ms * 1e3, 2), "GB/s": round(b / (k_ms * 1e-3) / 1e9, 1)}
+    if args.extra == "all":
+        extra["other_workloads"] = other_workloads(dev, max(5, args.steps // 5), stream)
     if extra:
         log("extra: " + json.dumps(extra))
 
