@@ -200,6 +200,13 @@ def other_workloads(dev, steps: int, stream) -> dict:
     timed("radix_sort_u32_2p24", lambda: ssc.radix_sort(x, out=out, tmp=tmp, scratch=sc), 32 * 8 * n,
           note="32 one-bit passes, 8N algorithmic each; each pass adds a 4N counting read")
     rows["radix_sort_u32_2p24"]["keys_per_s"] = round(n / (rows["radix_sort_u32_2p24"]["us"] * 1e-6), 1)
+    sc4 = torch.zeros(ssc.radix_sort4_scratch_bytes(n), dtype=torch.uint8, device=dev)
+    ssc.radix_sort4(x, out=out, tmp=tmp, scratch=sc4)
+    assert torch.equal(out.to(torch.int64) & 0xFFFFFFFF, want)
+    timed("radix_sort4_u32_2p24", lambda: ssc.radix_sort4(x, out=out, tmp=tmp, scratch=sc4), 8 * 8 * n,
+          note="8 passes of 4-bit digits, 8N algorithmic each; each pass adds a 4N counting read "
+               "and a scan of the 16 x tiles count table")
+    rows["radix_sort4_u32_2p24"]["keys_per_s"] = round(n / (rows["radix_sort4_u32_2p24"]["us"] * 1e-6), 1)
     return rows
 
 

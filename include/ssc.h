@@ -91,6 +91,10 @@ size_t ssc_scratch_bytes(int64_t n);
 /* Scratch bytes needed by ssc_radix_sort_u32 for n keys. */
 size_t ssc_radix_sort_scratch_bytes(int64_t n);
 
+/* Scratch bytes needed by ssc_radix_sort4_u32 for n keys: a scan scratch for
+ * a 16 x ceil(n / 8192) table of per-tile digit counts, then the table. */
+size_t ssc_radix_sort4_scratch_bytes(int64_t n);
+
 /* Zero-fills a scratch buffer on `stream` (needed once, before first use). */
 int ssc_scratch_init(void *scratch, size_t scratch_bytes, void *stream);
 
@@ -157,6 +161,21 @@ int ssc_compact_atomic_i32(const int32_t *in, int32_t *out, int64_t n, int pred,
  * compaction primitives, checked against std::sort). */
 int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t n,
                        void *scratch, size_t scratch_bytes, void *stream);
+
+/* LSD radix sort of uint32 keys with 4-bit digits: `passes` (1..8) stable
+ * 16-way splits, pass p by digit (x >> 4p) & 15, so out[] ends stably sorted
+ * by the low 4*passes bits of the keys (passes = 8: ascending). One 4-bit
+ * split gives the same order as the four 1-bit splits of those bits in
+ * ssc_radix_sort_u32, each a stable partition by a bit-test predicate. Each
+ * pass: per-tile digit counts (tiles of 8192 keys), one exclusive scan of
+ * the digit-major count table (the single-pass scan), then a stable scatter
+ * in 16 contiguous runs per tile. tmp is n words of caller workspace; in is
+ * not modified. out == in is allowed when passes is even; tmp must not
+ * overlap in or out. passes outside 1..8 is SSC_ERR_ARG.
+ * Source: "CIS 565 Project 2: Stream Compaction" (radix sort built on
+ * split, LSD bit order); the digit width is this library's. */
+int ssc_radix_sort4_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t n, int passes,
+                        void *scratch, size_t scratch_bytes, void *stream);
 
 /* out[i] = in[i]: the copy kernel with the same tile and load/store width as
  * the single pass, the practical bandwidth ceiling ("Day 33 compaction.cu",

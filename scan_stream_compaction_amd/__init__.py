@@ -41,6 +41,8 @@ SIGNATURES = {
     "ssc_count_if_i32": (_INT, [_P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
     "ssc_compact_atomic_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _INT, _P]),
     "ssc_radix_sort_u32": (_INT, [_P, _P, _P, _I64, _P, _SZ, _P]),
+    "ssc_radix_sort4_scratch_bytes": (_SZ, [_I64]),
+    "ssc_radix_sort4_u32": (_INT, [_P, _P, _P, _I64, _INT, _P, _SZ, _P]),
     "ssc_copy_i32": (_INT, [_P, _P, _I64, _P]),
     "ssc_status_str": (ctypes.c_char_p, [_INT]),
     "ssc_last_hip_error": (_INT, []),
@@ -232,6 +234,28 @@ def radix_sort(x: torch.Tensor, *, out: torch.Tensor | None = None,
     _check("ssc_radix_sort_u32", lib().ssc_radix_sort_u32(
         x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, scratch.data_ptr(), scratch.numel(),
         _stream(x)))
+    return out
+
+
+def radix_sort4_scratch_bytes(n: int) -> int:
+    return int(lib().ssc_radix_sort4_scratch_bytes(n))
+
+
+def radix_sort4(x: torch.Tensor, passes: int = 8, *, out: torch.Tensor | None = None,
+                tmp: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """Stable LSD sort of 32-bit keys taken as unsigned (int32 storage) by
+    their low 4*passes bits, 4-bit digits; passes=8 sorts ascending."""
+    _dev(x)
+    n = x.numel()
+    if out is None:
+        out = torch.empty_like(x)
+    if tmp is None:
+        tmp = torch.empty_like(x)
+    if scratch is None:
+        scratch = torch.zeros(radix_sort4_scratch_bytes(n), dtype=torch.uint8, device=x.device)
+    _check("ssc_radix_sort4_u32", lib().ssc_radix_sort4_u32(
+        x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, passes, scratch.data_ptr(),
+        scratch.numel(), _stream(x)))
     return out
 
 

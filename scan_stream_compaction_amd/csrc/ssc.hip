@@ -711,6 +711,151 @@ __global__ __launch_bounds__(kBlock) void bit_clear_count_kernel(const uint32_t 
     }
 }
 
+// ======================================== radix sort with 4-bit digits ---
+// Each pass is a stable 16-way split of the keys by digit (x >> shift) & 15,
+// done as three steps over tiles of 8192 keys (one 512-thread workgroup, 16
+// keys per lane):
+//   digit_count_kernel: cnt[d * tiles + t] = keys of tile t with digit d;
+//   one exclusive scan of that digit-major table (scan_kernel) turns it
+//     into off[d * tiles + t] = number of keys that precede, in the output,
+//     the first digit-d key of tile t (all keys of smaller digits, plus the
+//     digit-d keys of earlier tiles);
+//   digit_scatter_kernel: stable ranks inside the tile, the tile staged in
+//     LDS in digit order, then 16 contiguous runs written out.
+// Composing four 1-bit splits of bits shift..shift+3 gives the same order, so
+// after pass p the keys are stably sorted by their low 4(p+1) bits.
+constexpr int kRadixDigits = 16;
+constexpr int kRadixPassesMax = 8;
+
+__host__ __device__ constexpr int64_t radix_tiles_for(int64_t n) { return (n + kSub - 1) / kSub; }
+
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void digit_count_kernel(const uint32_t *__restrict__ in,
+                                                             int64_t n, int shift,
+                                                             uint32_t *__restrict__ cnt,
+                                                             uint32_t tiles) {
+    __shared__ uint32_t s_c[kWaves][kRadixDigits];
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
+    if (lane < kRadixDigits) s_c[w][lane] = 0;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.x) * kSub + static_cast<int64_t>(w) * kChunk;
+    const uint32_t rem = chunk_rem(n, chunk);
+    uint32_t v[kLoads][4];
+    load_chunk<VEC>(in, chunk, lane, rem, v);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (in_chunk(rem, j, lane, k))
+                __hip_atomic_fetch_add(&s_c[w][(v[j][k] >> shift) & 15u], 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (threadIdx.x < kRadixDigits) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) t += s_c[i][threadIdx.x];
+        cnt[threadIdx.x * tiles + blockIdx.x] = t;
+    }
+}
+
+// Stable 16-way split of one tile. Ranks: each wavefront first transposes
+// its 1024 keys through LDS so that slot (j, k) of lane l holds key
+// j*256 + k*64 + l of its chunk; slots then run in key order. Per slot, four
+// ballots of the digit bits give every lane the mask of lanes holding its
+// digit; its rank is the running count of that digit in the wavefront (16
+// LDS counters, bumped by the last lane of each digit) plus the matching
+// lanes below it. Wavefront offsets per digit and the tile's digit starts
+// follow from the 8 x 16 counts.
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void digit_scatter_kernel(const uint32_t *__restrict__ in,
+                                                               uint32_t *__restrict__ out,
+                                                               int64_t n, int shift,
+                                                               const uint32_t *__restrict__ off,
+                                                               uint32_t tiles) {
+    __shared__ __attribute__((aligned(16))) uint32_t s_keys[kSub];  // transposes, then the staged tile
+    __shared__ uint32_t s_run[kWaves][kRadixDigits];
+    __shared__ uint32_t s_before[kWaves][kRadixDigits];
+    __shared__ uint32_t s_start[kRadixDigits];
+    __shared__ uint32_t s_obase[kRadixDigits];
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
+    const int64_t tile_start = static_cast<int64_t>(blockIdx.x) * kSub;
+    const int64_t chunk = tile_start + static_cast<int64_t>(w) * kChunk;
+    const uint32_t rem = chunk_rem(n, chunk);
+    if (lane < kRadixDigits) s_run[w][lane] = 0;
+
+    uint32_t v[kLoads][4];
+    load_chunk<VEC>(in, chunk, lane, rem, v);
+    uint32_t *mine = s_keys + w * kChunk;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        u32x4 q;
+        q[0] = v[j][0];
+        q[1] = v[j][1];
+        q[2] = v[j][2];
+        q[3] = v[j][3];
+        *reinterpret_cast<u32x4 *>(mine + j * (kWave * 4) + lane * 4) = q;
+    }
+    uint32_t x[kLoads * 4];
+    uint32_t rk[kLoads * 4];
+#pragma unroll
+    for (int t = 0; t < kLoads * 4; ++t) x[t] = mine[(t >> 2) * (kWave * 4) + (t & 3) * kWave + lane];
+
+#pragma unroll
+    for (int t = 0; t < kLoads * 4; ++t) {
+        const uint32_t e = static_cast<uint32_t>((t >> 2) * (kWave * 4) + (t & 3) * kWave + lane);
+        const bool valid = e < rem;
+        const uint32_t d = (x[t] >> shift) & 15u;
+        uint64_t m = ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint64_t bb = ballot(valid && ((d >> b) & 1u));
+            m &= ((d >> b) & 1u) ? bb : ~bb;
+        }
+        const uint32_t below = mbcnt64(m);
+        const uint32_t same = static_cast<uint32_t>(__builtin_popcountll(m));
+        const uint32_t run = s_run[w][d];
+        rk[t] = run + below;
+        if (valid && below + 1u == same) s_run[w][d] = run + same;
+    }
+    __syncthreads();
+    if (w == 0) {
+        uint32_t acc = 0;
+        if (lane < kRadixDigits) {
+#pragma unroll
+            for (int i = 0; i < kWaves; ++i) {
+                s_before[i][lane] = acc;
+                acc += s_run[i][lane];
+            }
+        }
+        const uint32_t start = wave_inclusive_scan<SumU32>(acc) - acc;
+        if (lane < kRadixDigits) {
+            s_start[lane] = start;
+            s_obase[lane] = off[lane * tiles + blockIdx.x] - start;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kLoads * 4; ++t) {
+        const uint32_t e = static_cast<uint32_t>((t >> 2) * (kWave * 4) + (t & 3) * kWave + lane);
+        if (e < rem) {
+            const uint32_t d = (x[t] >> shift) & 15u;
+            s_keys[s_start[d] + s_before[w][d] + rk[t]] = x[t];
+        }
+    }
+    __syncthreads();
+    const int64_t left = n - tile_start;
+    const uint32_t len = left >= kSub ? static_cast<uint32_t>(kSub) : static_cast<uint32_t>(left);
+    for (uint32_t i = threadIdx.x; i < len; i += kBlock) {
+        const uint32_t y = s_keys[i];
+        const uint32_t o = s_obase[(y >> shift) & 15u] + i;
+        // a correct count table never trips this; a broken one gives wrong
+        // results instead of stray writes
+        if (static_cast<int64_t>(o) < n) __builtin_nontemporal_store(y, out + o);
+    }
+}
+
 // ================================================ unordered (atomic) kernel ---
 // Comparison only: no scan, no order. One sub-tile per workgroup.
 // VARIANT 0: the workgroup reserves one slot range for all its survivors with
@@ -981,6 +1126,18 @@ int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename
     return launched();
 }
 
+// 4-bit radix sort scratch: a scan scratch for the 16 x tiles count table,
+// then the table itself.
+size_t radix4_scan_part(int64_t n) {
+    const int64_t entries = kRadixDigits * radix_tiles_for(n);
+    return (scratch_need(entries) + 255) & ~static_cast<size_t>(255);
+}
+
+size_t radix4_scratch_need(int64_t n) {
+    if (n <= 0) return kHeaderBytes;
+    return radix4_scan_part(n) + static_cast<size_t>(kRadixDigits * radix_tiles_for(n)) * 4;
+}
+
 }  // namespace
 
 // ======================================================================
@@ -1142,6 +1299,54 @@ int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t
             SSC_TRY((LaunchSelect<4, false>::run(true, reinterpret_cast<const int32_t *>(src),
                                                  reinterpret_cast<int32_t *>(dst), n, b, 0,
                                                  scratch, cap, nullptr, nullptr, kept, s)));
+        src = dst;
+    }
+    return SSC_OK;
+}
+
+size_t ssc_radix_sort4_scratch_bytes(int64_t n) { return radix4_scratch_need(n); }
+
+int ssc_radix_sort4_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t n, int passes,
+                        void *scratch, size_t scratch_bytes, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (passes < 1 || passes > kRadixPassesMax) return SSC_ERR_ARG;
+    if (n > 0 && (in == nullptr || out == nullptr || tmp == nullptr)) return SSC_ERR_ARG;
+    if (!aligned(in, 4) || !aligned(out, 4) || !aligned(tmp, 4)) return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    // pass 0 writes tmp when passes is even, so only then may out be in
+    if ((n > 0 && in == out && passes % 2 == 1) || (in != out && overlap(in, bytes, out, bytes)) ||
+        overlap(tmp, bytes, in, bytes) || overlap(tmp, bytes, out, bytes))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch(scratch, scratch_bytes, radix4_scratch_need(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        overlap(scratch, scratch_bytes, tmp, bytes))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return SSC_OK;
+    const uint32_t tiles = static_cast<uint32_t>(radix_tiles_for(n));
+    const int64_t entries = static_cast<int64_t>(kRadixDigits) * tiles;
+    const size_t scan_bytes = radix4_scan_part(n);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(static_cast<char *>(scratch) + scan_bytes);
+    const bool vec = aligned(in, 16) && aligned(out, 16) && aligned(tmp, 16);
+    const uint32_t *src = in;
+    for (int p = 0; p < passes; ++p) {
+        uint32_t *dst = (passes - 1 - p) % 2 == 0 ? out : tmp;  // the last pass lands in out
+        if (vec)
+            hipLaunchKernelGGL((digit_count_kernel<true>), dim3(tiles), dim3(kBlock), 0, s, src, n,
+                               4 * p, cnt, tiles);
+        else
+            hipLaunchKernelGGL((digit_count_kernel<false>), dim3(tiles), dim3(kBlock), 0, s, src, n,
+                               4 * p, cnt, tiles);
+        SSC_TRY(launched());
+        SSC_TRY(scan_impl<SumU32>(cnt, cnt, entries, nullptr, scratch, scan_bytes, s));
+        if (vec)
+            hipLaunchKernelGGL((digit_scatter_kernel<true>), dim3(tiles), dim3(kBlock), 0, s, src,
+                               dst, n, 4 * p, cnt, tiles);
+        else
+            hipLaunchKernelGGL((digit_scatter_kernel<false>), dim3(tiles), dim3(kBlock), 0, s, src,
+                               dst, n, 4 * p, cnt, tiles);
+        SSC_TRY(launched());
         src = dst;
     }
     return SSC_OK;

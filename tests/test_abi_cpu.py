@@ -74,6 +74,14 @@ def test_tile_and_scratch_sizes():
         assert L.ssc_radix_sort_scratch_bytes(n) == 512 + 8 * tiles
     assert L.ssc_scratch_bytes(INT32_MAX) == 512 + 8 * 69906
     assert L.ssc_scratch_bytes(-5) == 512
+    # 4-bit radix sort: a scan scratch (256-byte rounded) for the 16 x tiles
+    # count table, then the table
+    for n in (1, 8191, 8192, 8193, 2**24, INT32_MAX):
+        rt = (n + 8191) // 8192
+        scan = 512 + 8 * ((16 * rt + T - 1) // T)
+        assert L.ssc_radix_sort4_scratch_bytes(n) == (scan + 255) // 256 * 256 + 64 * rt
+    assert L.ssc_radix_sort4_scratch_bytes(0) == 512
+    assert L.ssc_radix_sort4_scratch_bytes(INT32_MAX) == 1792 + 64 * 262144
 
 
 def test_status_strings():
@@ -148,6 +156,14 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     assert L.ssc_radix_sort_u32(A, B, B + 64, 100, S, big, None) == ALIAS
     assert L.ssc_radix_sort_u32(A, B, C, 100, S, 512 + 7, None) == SCRATCH
     assert L.ssc_radix_sort_u32(A, B, None, 100, S, big, None) == ARG
+    # 4-bit radix sort: passes 1..8; out == in only with an even pass count
+    assert L.ssc_radix_sort4_u32(A, B, C, 100, 0, S, big, None) == ARG
+    assert L.ssc_radix_sort4_u32(A, B, C, 100, 9, S, big, None) == ARG
+    assert L.ssc_radix_sort4_u32(A, A, C, 100, 3, S, big, None) == ALIAS
+    assert L.ssc_radix_sort4_u32(A, B, B + 64, 100, 8, S, big, None) == ALIAS
+    assert L.ssc_radix_sort4_u32(A, B, None, 100, 8, S, big, None) == ARG
+    assert L.ssc_radix_sort4_u32(A, B, C, 100, 8, S, 512 + 7, None) == SCRATCH
+    assert L.ssc_radix_sort4_u32(A, B, C, 100, 8, A, big, None) == ALIAS
     # copy
     assert L.ssc_copy_i32(A, A + 4, 100, None) == ALIAS
     assert L.ssc_copy_i32(A, B, -1, None) == ARG

@@ -198,6 +198,63 @@ def test_radix_sort_full_size():
     assert checks.first_mismatch(got, oracle.radix_sort_u32(x)) == -1
 
 
+R4 = 8192  # keys per tile of the 4-bit radix sort
+
+
+def test_radix4_full_size():
+    """2^24 uint32 keys, 8 passes of 4-bit digits vs numpy's sort and the oracle."""
+    x = wl.radix_input()
+    got = host(ssc.radix_sort4(dev(x.view(np.int32)))).view(np.uint32)
+    assert checks.first_mismatch(got, np.sort(x)) == -1
+    assert checks.first_mismatch(got, oracle.radix_sort_u32(x)) == -1
+
+
+@pytest.mark.parametrize("n", [3 * R4 + 1234, 100_003])
+def test_radix4_partial_passes_match_the_bit_split_oracle(n):
+    """After p 4-bit passes the keys must equal the oracle's state after 4p
+    one-bit splits: stably sorted by the low 4p bits, equal low bits kept in
+    input order (stability is visible because the high bits differ)."""
+    x = wl.full_uint32(0x5EED0105 + n, n)
+    xd = dev(x.view(np.int32))
+    for p in range(1, 9):
+        got = host(ssc.radix_sort4(xd, passes=p)).view(np.uint32)
+        want = oracle.radix_sort_u32(x, passes=4 * p)
+        assert checks.first_mismatch(got, want) == -1, (n, p)
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 63, 64, 65, 1023, 1024, 1025, R4 - 1, R4, R4 + 1,
+                               2 * R4 - 1, 2 * R4 + 1, 7 * R4 + 611])
+def test_radix4_edge_sizes(n):
+    x = wl.full_uint32(0x5EED0205 + n, n)
+    got = host(ssc.radix_sort4(dev(x.view(np.int32)))).view(np.uint32)
+    assert checks.first_mismatch(got, np.sort(x)) == -1
+    # few distinct digits: every lane of a wavefront shares a digit with many others
+    y = wl.uniform_below(0x5EED0305 + n, n, 16).view(np.uint32) * np.uint32(0x11111111)
+    got = host(ssc.radix_sort4(dev(y.view(np.int32)), passes=3)).view(np.uint32)
+    assert checks.first_mismatch(got, oracle.radix_sort_u32(y, passes=12)) == -1
+
+
+def test_radix4_unaligned_in_place_and_odd_passes():
+    n = 5 * R4 + 77
+    x = wl.full_uint32(0x5EED0405, n)
+    # 4-byte but not 16-byte aligned arrays take the 32-bit path
+    base = torch.empty(n + 1, dtype=torch.int32, device=DEV)
+    base[1:] = dev(x.view(np.int32))
+    out = torch.empty(n + 1, dtype=torch.int32, device=DEV)[1:]
+    tmp = torch.empty(n + 1, dtype=torch.int32, device=DEV)[1:]
+    got = host(ssc.radix_sort4(base[1:], passes=5, out=out, tmp=tmp)).view(np.uint32)
+    assert checks.first_mismatch(got, oracle.radix_sort_u32(x, passes=20)) == -1
+    assert checks.first_mismatch(host(base[1:]).view(np.uint32), x) == -1, "input modified"
+    # out == in with an even number of passes
+    xd = dev(x.view(np.int32))
+    ssc.radix_sort4(xd, passes=8, out=xd)
+    assert checks.first_mismatch(host(xd).view(np.uint32), np.sort(x)) == -1
+    with pytest.raises(ssc.SSCError):
+        ssc.radix_sort4(xd, passes=7, out=xd)
+    with pytest.raises(ssc.SSCError):
+        ssc.radix_sort4(xd, passes=0)
+
+
 # -------------------------------------------------------------- edge cases ---
 
 EDGE_N = [0, 1, 2, 3, 5, 63, 64, 65, 255, 256, 257, C - 1, C, C + 1, 7 * C + 3, S - 1, S,
