@@ -11,21 +11,21 @@
 //
 // MI355X-first tile shape. A same-address device-scope atomic is serialised
 // across the 8 XCDs at roughly 11-12 ns, so a tile number is claimed once per
-// 30720 elements (120 KiB). A 1024-thread workgroup = 15 data wavefronts +
-// 1 control wavefront: the control wavefront walks the look-back while the
-// data wavefronts load (the look-back's waits cannot share a wavefront with
-// outstanding data loads, whose completions count in the same in-order
-// counter). Each data lane holds 32 elements from eight 128-bit nontemporal
-// loads, every load instruction covering 1 KiB of contiguous bytes; element
-// order in a wavefront chunk is (load j, lane, component k). Ranks come from
-// ballot + mbcnt, the last data wavefront to finish scans the 30 chunk totals
-// and publishes the tile aggregate at once, and survivors are staged in LDS
-// (60 KiB per round) and leave as one contiguous run of coalesced stores per
-// round. At most 64 VGPRs: two workgroups (32 wavefronts) per CU.
+// 30720 elements (120 KiB). Workgroups are 1024 threads: 15 data wavefronts
+// + 1 control wavefront that walks the look-back (its waits cannot share a
+// wavefront with outstanding data loads, whose completions count in the same
+// in-order counter). The compaction and partition kernel is persistent, one
+// workgroup per compute unit, with each data wavefront holding its chunk of
+// the current tile and, in flight, its chunk of the next: every tile's
+// aggregate is published as soon as its data has landed, the loads of later
+// tiles overlap the look-back waits, and survivors leave as contiguous runs
+// staged in LDS. Ranks inside a wavefront come from ballot + mbcnt. The scan
+// kernel keeps one tile per workgroup: two rounds of 15 chunks, the last data
+// wavefront to finish scanning the 30 chunk totals.
 //
 // Scratch needs no clearing between calls: tile numbers and an epoch come
 // from one 64-bit atomic word {epoch:32 | next tile:32}; the workgroup that
-// claims the last tile resets the counter and advances the epoch, and
+// makes a call's last claim resets the counter and advances the epoch, and
 // descriptors carry the epoch as a tag. The counting passes reset their own
 // accumulators (the last workgroup to finish does it).
 #include <hip/hip_runtime.h>
@@ -198,21 +198,6 @@ __device__ __forceinline__ void store_chunk(T *out, int64_t chunk, int lane, uin
     }
 }
 
-// Streams staged[0 .. len) to dst_base[0 .. len) with all threads of a
-// workgroup of `block` threads; element i goes to dst_base + i unless
-// dst_base + i >= limit (range check). Uniform base, 32-bit per-lane offset.
-template <int BLOCK>
-__device__ __forceinline__ void stream_out(const int32_t *staged, int32_t *out, uint32_t dst_base,
-                                           uint32_t len, int64_t limit) {
-    int32_t *b = out + dst_base;
-    const uint32_t room = static_cast<int64_t>(dst_base) + len <= limit
-                              ? len
-                              : (limit > dst_base ? static_cast<uint32_t>(limit - dst_base) : 0u);
-    for (uint32_t i = threadIdx.x; i < room; i += BLOCK)
-        __builtin_nontemporal_store(staged[i], reinterpret_cast<int32_t *>(
-                                                   reinterpret_cast<char *>(b) + 4u * i));
-}
-
 // Wavefront-local ranks of one chunk. Evaluates the predicate once per valid
 // element and records the flags in `mask` at bit (bit0 + j*4 + k).
 // lead[j] = flagged elements in earlier loads of the chunk plus those of
@@ -244,25 +229,6 @@ __device__ __forceinline__ uint32_t chunk_ranks(const int32_t (&v)[kLoads][4], i
 }
 
 __device__ __forceinline__ bool bit(uint64_t mask, int b) { return (mask >> b) & 1u; }
-
-// lead[j] of chunk_ranks, recomputed from the recorded flags (ballots are
-// cheap; keeping lead[] live across the look-back costs registers).
-__device__ __forceinline__ void leads_from_mask(uint64_t mask, int bit0, uint32_t (&lead)[kLoads]) {
-    uint32_t running = 0;
-#pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-        uint32_t below = 0;
-        uint32_t total = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint64_t m = ballot(bit(mask, bit0 + j * 4 + k));
-            below += mbcnt64(m);
-            total += static_cast<uint32_t>(__builtin_popcountll(m));
-        }
-        lead[j] = running + below;
-        running += total;
-    }
-}
 
 // Chunk totals of a tile live in LDS in (round q, data wavefront d) order,
 // s_tot[q * kDataWaves + d]. The last data wavefront to finish scans them
@@ -348,161 +314,371 @@ __device__ __forceinline__ void arrive_and_publish(uint32_t *s_arrive, const uin
     }
 }
 
+// ------------------------------------------- buffer-resource chunk access ---
+// The persistent compaction kernel reads and writes through buffer
+// resources: a resource over `bytes` bytes drops 32-bit lanes past its end
+// dword by dword (loads return 0, stores are discarded; a 128-bit load that
+// straddles the end keeps its in-range dwords). Partial chunks and
+// variable-length runs then need no branches, and every wavefront issues the
+// same memory instructions on every tile.
+constexpr int kSelLoads = 8;                       // 128-bit loads per data lane per tile
+constexpr int kSelChunk = kWave * kSelLoads * 4;   // 2048 elements per data wavefront
+static_assert(kDataWaves * kSelChunk == kTile, "a tile is one chunk per data wavefront");
+static_assert(kSelLoads * 4 <= 32, "a chunk's flags fit a 32-bit lane mask");
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, no swizzle
+constexpr int kNT = 2;                  // nontemporal cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0),
+                                             static_cast<int>(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ uint32_t sel_chunk_rem(int64_t n, int64_t chunk) {
+    const int64_t r = n - chunk;
+    return r <= 0 ? 0u : (r >= kSelChunk ? static_cast<uint32_t>(kSelChunk) : static_cast<uint32_t>(r));
+}
+
+// Loads a chunk (rem valid elements) in the (j, lane, k) layout: element
+// j*256 + lane*4 + k; missing elements read as 0. VEC: eight 128-bit loads
+// per lane, else 32 loads of 32 bits. Nontemporal: every byte is read once.
+template <bool VEC>
+__device__ __forceinline__ void load_chunk_rsrc(const int32_t *in, int64_t chunk, uint32_t rem,
+                                                int lane, int32_t (&v)[kSelLoads][4]) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(in + chunk, rem * 4u);
+    const int lane_off = lane * 16;
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j) {
+        if constexpr (VEC) {
+            const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, j * (kWave * 16) + lane_off, 0, kNT);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[j][k] = static_cast<int32_t>(q[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[j][k] = static_cast<int32_t>(__builtin_amdgcn_raw_buffer_load_b32(
+                    r, j * (kWave * 16) + lane_off + 4 * k, 0, kNT));
+        }
+    }
+}
+
+// Writes run[0 .. len) (LDS) to out[at .. at + len) with kSelChunk / 64
+// stores per lane whatever len is: slots past len fall outside the resource
+// and are dropped, so up to kSelChunk - 1 slots past the run are read (the
+// staging array is padded for that). The run is also cut at n: a correct
+// look-back never needs it, a broken one then gives wrong results instead of
+// stray writes. Default cache policy (measured faster than nontemporal for
+// these 4-byte runs).
+__device__ __forceinline__ void stream_run(const int32_t *run, int32_t *out, uint32_t at,
+                                           uint32_t len, int64_t n, int lane) {
+    len = uniform(len);
+    const int64_t room = n - static_cast<int64_t>(at);
+    if (static_cast<int64_t>(len) > room) len = room > 0 ? static_cast<uint32_t>(room) : 0u;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(out + at, len * 4u);
+    const int32_t *src = run + lane;
+    const int voff = lane * 4;
+#pragma unroll
+    for (int i = 0; i < kSelChunk / kWave; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], r, voff + i * (kWave * 4), 0, 0);
+}
+
+// Flags of one chunk: bit (j*4 + k) of `mask` is the predicate of element
+// (j, lane, k), evaluated once. Returns the chunk's flag total (uniform).
+template <int P>
+__device__ __forceinline__ uint32_t chunk_flags(const int32_t (&v)[kSelLoads][4], int lane,
+                                                uint32_t rem, int32_t pa, int32_t pb,
+                                                uint32_t &mask) {
+    uint32_t total = 0;
+    mask = 0;
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            // element (j, lane, k) is valid iff lane*4 < rem - (j*256 + k): a
+            // uniform bound per (j, k) against one per-lane value
+            const bool valid = lane * 4 < static_cast<int>(rem) - (j * (kWave * 4) + k);
+            const bool f = valid && pred_eval<P>(v[j][k], pa, pb);
+            mask |= static_cast<uint32_t>(f) << (j * 4 + k);
+            total += static_cast<uint32_t>(__builtin_popcountll(ballot(f)));
+        }
+    return total;
+}
+
+// lead[j] = flagged elements of the chunk before element (j, lane, 0): the
+// flags of earlier loads plus those of load j in lower lanes (ballot +
+// mbcnt, recomputed from the mask rather than kept live across the tile).
+__device__ __forceinline__ void chunk_leads(uint32_t mask, uint32_t (&lead)[kSelLoads]) {
+    uint32_t running = 0;
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j) {
+        uint32_t below = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t m = ballot((mask >> (j * 4 + k)) & 1u);
+            below += mbcnt64(m);
+            total += static_cast<uint32_t>(__builtin_popcountll(m));
+        }
+        lead[j] = running + below;
+        running += total;
+    }
+}
+
+// ranks[i] = seg + (flags before element i in its chunk) for the chunk's rem
+// valid elements, written in the load layout. The lead of load j is built
+// up load by load (as in chunk_leads) so that no array of leads stays live.
+template <bool VEC>
+__device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint32_t rem,
+                                            uint32_t seg, uint32_t mask, int lane) {
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(ranks + chunk, rem * 4u);
+    uint32_t running = seg;
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j) {
+        uint32_t below = 0, total = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t m = ballot((mask >> (j * 4 + k)) & 1u);
+            below += mbcnt64(m);
+            total += static_cast<uint32_t>(__builtin_popcountll(m));
+        }
+        uint32_t x = running + below;
+        running += total;
+        uint32_t q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            q[k] = x;
+            x += (mask >> (j * 4 + k)) & 1u;
+        }
+        if constexpr (VEC) {
+            u32x4 v;
+            v[0] = q[0];
+            v[1] = q[1];
+            v[2] = q[2];
+            v[3] = q[3];
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, j * (kWave * 16) + lane * 16, 0, kNT);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                __builtin_amdgcn_raw_buffer_store_b32(q[k], r, j * (kWave * 16) + lane * 16 + 4 * k,
+                                                      0, kNT);
+        }
+    }
+}
+
 // ===================================================== compaction kernel ---
-// One tile per workgroup, tile number from the atomic counter.
-//   control wavefront: claim; walk the look-back for the tile's exclusive
-//     prefix (the survivors of all earlier tiles) while the data load;
-//   data wavefronts: eight 128-bit loads per lane; flag and rank each chunk
-//     (ballot + mbcnt); chunk totals to LDS; the last to arrive publishes
-//     {aggregate, A};
-//   barrier; the control wavefront publishes {inclusive, base + A};
-//   per round: data wavefronts stage the round's survivors in LDS at their
-//     rank (for a partition the rejected ones after them), barrier, all 16
-//     wavefronts stream the run(s) out, barrier.
-// PARTITION reads K from *kept_total (written by the counting pass).
-template <int P, bool VEC, bool PARTITION>
-__global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void select_kernel(
+// Persistent form: one 1024-thread workgroup per compute unit (its LDS and
+// 128 VGPRs per lane fill the unit) loops over tiles of 30720 elements whose
+// numbers come from the atomic counter, claimed three ahead. A tile is one
+// chunk of 2048 elements (eight 128-bit loads per lane) for each of the 15
+// data wavefronts; the 16th is the control wavefront.
+//
+// Per tile, a data wavefront holds two chunks in registers: the current
+// tile's, already flagged and ranked, and the next tile's, in flight. It
+//   1. stages the current chunk's survivors at their rank in its own LDS
+//      region (for a partition the rejected ones after them);
+//   2. issues the loads of the tile after next into the registers that just
+//      freed up;
+//   3. flags the next tile's chunk (waiting only for those loads), writes
+//      its total to LDS and arrives; the last of the 15 to arrive scans the
+//      totals and publishes the next tile's {aggregate} at once;
+//   4. waits at the tile's one workgroup barrier for the base (the survivors
+//      of all earlier tiles) that the control wavefront found;
+//   5. writes its region out to out[base + chunk prefix].
+// The control wavefront claims a tile, walks the look-back for the current
+// tile's base, passes the barrier and publishes {inclusive}. So every tile's
+// aggregate goes out before its workgroup waits on anything, and the next
+// two tiles' loads are in flight during both the look-back wait and the
+// write-out.
+//
+// Memory instructions per wavefront and tile are fixed (loads and stores go
+// through buffer resources that drop what lies past a chunk's or a run's
+// end), so the compiler's waits name exact counts: step 3 waits for the
+// next chunk's loads and never for the loads issued in step 2. The lane
+// number is made opaque once per tile so that address arithmetic stays in
+// the loop, folded into instruction offsets, instead of being hoisted into
+// registers held across it.
+//
+// Forward progress: a workgroup processes its claims in increasing order and
+// stops claiming after its first claim past the end, so a call makes exactly
+// tiles + gridDim.x claims. The lowest unfinished tile is the current tile
+// of the workgroup that claimed it (any earlier claim of that workgroup is
+// lower and finished), and its look-back needs only lower, finished tiles.
+enum { kCompact = 0, kCompactRanks = 1, kPartition = 2 };
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+
+template <int P, bool VEC, int KIND>
+__global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(
     const int32_t *__restrict__ in, int32_t *__restrict__ out, int64_t n, int32_t pa,
     int32_t pb, void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
     const int32_t *__restrict__ kept_total) {
-    __shared__ int32_t s_stage[kLbSub];
-    __shared__ uint32_t s_tot[kChunksPerTile];
-    __shared__ uint32_t s_pre[kChunksPerTile + 1];
-    __shared__ uint32_t s_tile, s_tag, s_base, s_arrive;
+    // one staging region per data wavefront, plus one of padding for run reads
+    __shared__ int32_t s_stage[kDataWaves + 1][kSelChunk];
+    __shared__ uint32_t s_tot[kDataWaves];
+    __shared__ uint32_t s_pre[3][kDataWaves + 1];  // chunk prefixes + aggregate, by tile mod 3
+    __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
+    __shared__ uint32_t s_first[3], s_tag, s_arrive;
 
     const ScratchView sv = view(scratch);
+    const uint32_t claims = num_tiles + gridDim.x;  // one claim past the end per workgroup
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     if (threadIdx.x == 0) {
-        const uint64_t c = claim_tile(sv, num_tiles, num_tiles, capacity);
-        s_tile = static_cast<uint32_t>(c);
+        // up to three claims, stopping at the first one past the end
+        const uint64_t c = claim_tile(sv, num_tiles, claims, capacity);
+        uint32_t t = static_cast<uint32_t>(c);
+        s_first[0] = t;
+        s_first[1] = s_first[2] = kNoTile;
+        if (t < num_tiles) {
+            t = static_cast<uint32_t>(claim_tile(sv, num_tiles, claims, capacity));
+            s_first[1] = t;
+            if (t < num_tiles)
+                s_first[2] = static_cast<uint32_t>(claim_tile(sv, num_tiles, claims, capacity));
+        }
         s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
         s_arrive = 0;
     }
-    __syncthreads();
-    const uint32_t tile = uniform(s_tile);
+    __syncthreads();  // B0
+    uint32_t tile = uniform(s_first[0]);
+    uint32_t nxt = uniform(s_first[1]);
+    uint32_t nxt2 = uniform(s_first[2]);
     const uint32_t tag = uniform(s_tag);
-    if (tile >= num_tiles) return;  // only if the scratch was never initialised
-    const int lane = lane_id();
-    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
-    const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
-
-    // Both branches below pass the same barriers (B1, then 2 per round but
-    // the last): the control wavefront never holds the data registers.
-    const auto write_round = [&](int q, uint32_t base, const uint32_t (&round_before)[kLbRounds + 1],
-                                 uint32_t kept) {
-        const int64_t round_start = tile_start + q * kLbSub;
-        const uint32_t a_q = round_before[q + 1] - round_before[q];
-        const uint32_t kept_base = base + round_before[q];  // survivors before this round
-        // Range-checked against n: a correct look-back never trips it; a
-        // broken one gives wrong results instead of stray writes.
-        stream_out<kLbBlock>(s_stage, out, kept_base, a_q, n);
-        if constexpr (PARTITION) {
-            const int64_t left = n - round_start;
-            const uint32_t len = left >= kLbSub ? static_cast<uint32_t>(kLbSub)
-                                                : (left > 0 ? static_cast<uint32_t>(left) : 0u);
-            // rejected elements before this round = round_start - kept_base
-            const uint32_t rej_before = static_cast<uint32_t>(round_start) - kept_base;
-            stream_out<kLbBlock>(s_stage + a_q, out, kept + rej_before, len - a_q, n);
-        }
-    };
+    if (tile >= num_tiles) return;  // this workgroup's one claim past the end
+    uint32_t par = 0;  // tile parity within the workgroup: s_base, s_next
+    uint32_t tri = 0;  // tile number within the workgroup mod 3: s_pre
 
     if (w == kCtrlWave) {
-        uint32_t prefix = 0;
-        if (tile != 0) prefix = look_back<SumU32>(sv.desc, tile, tag, sv.timed_out);
-        if (lane == 0) s_base = prefix;
-        __syncthreads();  // B1
-        uint32_t chunk_before[kLbRounds];
-        uint32_t round_before[kLbRounds + 1];
-        tile_prefixes<SumU32>(s_pre, 0, chunk_before, round_before);
-        const uint32_t agg = round_before[kLbRounds];
-        if (lane == 0) {
-            if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, prefix + agg);
-            if (!PARTITION && tile == num_tiles - 1) *count = static_cast<int32_t>(prefix + agg);
-        }
-        const uint32_t kept = PARTITION ? static_cast<uint32_t>(*kept_total) : 0u;
-#pragma unroll
-        for (int q = 0; q < kLbRounds; ++q) {
-            __syncthreads();  // round q staged
-            write_round(q, prefix, round_before, kept);
-            if (q + 1 < kLbRounds) __syncthreads();  // LDS free for the next round
-        }
-        return;
-    }
-
-    int32_t v[kLbRounds][kLoads][4];
-    uint64_t fmask = 0;  // flag of (q, j, k) at bit q*16 + j*4 + k
-    static_assert(kLbRounds * kLoads * 4 <= 64, "flags of one lane fit a 64-bit mask");
-#pragma unroll
-    for (int q = 0; q < kLbRounds; ++q) {
-        const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
-        load_chunk<VEC>(in, chunk, lane, chunk_rem(n, chunk), v[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < kLbRounds; ++q) {
-        const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
-        uint32_t lead[kLoads];
-        const uint32_t t = chunk_ranks<P>(v[q], lane, chunk_rem(n, chunk), pa, pb, lead, fmask,
-                                          q * kLoads * 4);
-        if (lane == 0) s_tot[q * kDataWaves + w] = t;
-    }
-    arrive_and_publish<SumU32>(&s_arrive, s_tot, s_pre, sv.desc, tile, tag, lane);
-    __syncthreads();  // B1
-    const uint32_t base = uniform(s_base);
-    uint32_t chunk_before[kLbRounds];
-    uint32_t round_before[kLbRounds + 1];
-    tile_prefixes<SumU32>(s_pre, w, chunk_before, round_before);
-    const uint32_t kept = PARTITION ? static_cast<uint32_t>(*kept_total) : 0u;
-
-#pragma unroll
-    for (int q = 0; q < kLbRounds; ++q) {
-        // Stage: survivors at their rank inside the round; for a partition
-        // the rejected after them at a_q + (index - rank).
-        const uint32_t a_q = round_before[q + 1] - round_before[q];
-        const uint32_t rem = chunk_rem(n, tile_start + q * kLbSub + w * kChunk);
-        uint32_t lead[kLoads];
-        leads_from_mask(fmask, q * kLoads * 4, lead);
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
-            uint32_t r = chunk_before[q] - round_before[q] + lead[j];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bool f = bit(fmask, q * kLoads * 4 + j * 4 + k);
-                if (f) {
-                    s_stage[r] = v[q][j][k];
-                } else if constexpr (PARTITION) {
-                    const uint32_t local =
-                        static_cast<uint32_t>(w * kChunk + j * (kWave * 4) + lane * 4 + k);
-                    if (in_chunk(rem, j, lane, k)) s_stage[a_q + local - r] = v[q][j][k];
-                }
-                r += f ? 1u : 0u;
+        __syncthreads();  // B0': the first tile's arrivals are in
+        while (true) {
+            uint32_t nxt3 = kNoTile;
+            if (lane == 0 && nxt2 < num_tiles)
+                nxt3 = static_cast<uint32_t>(claim_tile(sv, num_tiles, claims, capacity));
+            uint32_t prefix = 0;
+            if (tile != 0) prefix = look_back<SumU32>(sv.desc, tile, tag, sv.timed_out);
+            if (lane == 0) {
+                s_base[par] = prefix;
+                s_next[par] = nxt3;
             }
+            __syncthreads();  // B1
+            const uint32_t agg = uniform(s_pre[tri][kDataWaves]);
+            if (lane == 0) {
+                if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, prefix + agg);
+                if (KIND != kPartition && tile == num_tiles - 1)
+                    *count = static_cast<int32_t>(prefix + agg);
+            }
+            if (nxt >= num_tiles) return;
+            tile = nxt;
+            nxt = nxt2;
+            nxt2 = uniform(nxt3);
+            par ^= 1u;
+            tri = tri == 2u ? 0u : tri + 1u;
         }
-        __syncthreads();  // round q staged
-        write_round(q, base, round_before, kept);
-        if (q + 1 < kLbRounds) __syncthreads();  // LDS free for the next round
     }
 
-    if constexpr (!PARTITION) {
-        if (ranks != nullptr) {
-#pragma unroll
-            for (int q = 0; q < kLbRounds; ++q) {
-                const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
-                int32_t rk[kLoads][4];
-                uint32_t lead[kLoads];
-                leads_from_mask(fmask, q * kLoads * 4, lead);
-#pragma unroll
-                for (int j = 0; j < kLoads; ++j) {
-                    uint32_t r = base + chunk_before[q] + lead[j];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        rk[j][k] = static_cast<int32_t>(r);
-                        r += bit(fmask, q * kLoads * 4 + j * 4 + k) ? 1u : 0u;
-                    }
-                }
-                store_chunk<VEC>(ranks, chunk, lane, chunk_rem(n, chunk), rk);
-            }
-        }
+    const uint32_t kept = KIND == kPartition ? static_cast<uint32_t>(*kept_total) : 0u;
+    int32_t va[kSelLoads][4], vb[kSelLoads][4];
+    uint32_t fm_cur = 0, fm_nxt = 0;  // flags of the current / next chunk
+    uint32_t a_cur = 0, a_nxt = 0;    // their totals
+    uint32_t rem_cur = 0, rem_nxt = 0;
+    const auto chunk_of = [&](uint32_t t) {
+        return static_cast<int64_t>(t) * kTile + static_cast<int64_t>(w) * kSelChunk;
+    };
+    // a tile past the end has no valid elements: its loads touch nothing
+    const auto rem_of = [&](uint32_t t) { return t < num_tiles ? sel_chunk_rem(n, chunk_of(t)) : 0u; };
+
+    // Flags of chunk V (tile T, R valid) into FM and A, then the arrival: the
+    // last data wavefront to arrive scans the 15 totals into s_pre[TRI] and
+    // publishes T's {aggregate} ({inclusive} for tile 0).
+#define SSC_FLAG_AND_ARRIVE(V, T, R, FM, A, TRI, LN)                                          \
+    {                                                                                         \
+        A = uniform(chunk_flags<P>(V, LN, R, pa, pb, FM));                                    \
+        if (LN == 0) s_tot[w] = A;                                                            \
+        uint32_t before_ = 0;                                                                 \
+        if (LN == 0)                                                                          \
+            before_ = __hip_atomic_fetch_add(&s_arrive, 1u, __ATOMIC_ACQ_REL,                 \
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);                   \
+        if (uniform(before_) == kDataWaves - 1) {                                             \
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");                            \
+            const uint32_t mine_ = LN < kDataWaves ? s_tot[LN] : 0u;                          \
+            const uint32_t incl_ = wave_inclusive_scan<SumU32>(mine_);                        \
+            if (LN < kDataWaves) s_pre[TRI][LN] = incl_ - mine_;                              \
+            const uint32_t agg_ = static_cast<uint32_t>(                                      \
+                __builtin_amdgcn_readlane(static_cast<int>(incl_), kDataWaves - 1));          \
+            if (LN == 0) {                                                                    \
+                s_arrive = 0;                                                                 \
+                s_pre[TRI][kDataWaves] = agg_;                                                \
+                if ((T) < num_tiles)                                                          \
+                    publish(sv.desc + (T), tag, (T) == 0 ? kStatusInclusive : kStatusAggregate, \
+                            agg_);                                                            \
+            }                                                                                 \
+        }                                                                                     \
     }
+
+    // One tile (steps 1-5 above) with CUR holding the current chunk and NX
+    // the next one in flight; the loop below alternates the two register sets.
+#define SSC_TILE(CUR, NX)                                                                     \
+    {                                                                                         \
+        int ln = lane;                                                                        \
+        asm volatile("" : "+v"(ln));                                                          \
+        {                                                                                     \
+            uint32_t lead[kSelLoads];                                                         \
+            chunk_leads(fm_cur, lead);                                                        \
+            _Pragma("unroll") for (int j = 0; j < kSelLoads; ++j) {                           \
+                uint32_t r = lead[j];                                                         \
+                _Pragma("unroll") for (int k = 0; k < 4; ++k) {                               \
+                    const bool f = (fm_cur >> (j * 4 + k)) & 1u;                              \
+                    if (f) {                                                                  \
+                        s_stage[w][r] = CUR[j][k];                                            \
+                    } else if constexpr (KIND == kPartition) {                                \
+                        const uint32_t local =                                                \
+                            static_cast<uint32_t>(j * (kWave * 4) + ln * 4 + k);              \
+                        if (local < rem_cur) s_stage[w][a_cur + local - r] = CUR[j][k];       \
+                    }                                                                         \
+                    r += f ? 1u : 0u;                                                         \
+                }                                                                             \
+            }                                                                                 \
+        }                                                                                     \
+        load_chunk_rsrc<VEC>(in, chunk_of(nxt2), rem_of(nxt2), ln, CUR);                      \
+        const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                     \
+        rem_nxt = rem_of(nxt);                                                                \
+        SSC_FLAG_AND_ARRIVE(NX, nxt, rem_nxt, fm_nxt, a_nxt, tri_n, ln)                       \
+        __syncthreads(); /* B1: this tile's base is known */                                  \
+        const uint32_t base = uniform(s_base[par]);                                           \
+        const uint32_t nxt3 = uniform(s_next[par]);                                           \
+        const int64_t chunk_now = chunk_of(tile);                                             \
+        const uint32_t seg = base + uniform(s_pre[tri][w]); /* kept before this chunk */      \
+        stream_run(s_stage[w], out, seg, a_cur, n, ln);                                       \
+        if constexpr (KIND == kPartition) {                                                   \
+            /* rejected before this chunk = elements before it - kept before it */            \
+            const uint32_t rej = static_cast<uint32_t>(chunk_now) - seg;                      \
+            stream_run(s_stage[w] + a_cur, out, kept + rej, rem_cur - a_cur, n, ln);          \
+        }                                                                                     \
+        if constexpr (KIND == kCompactRanks)                                                  \
+            write_ranks<VEC>(ranks, chunk_now, rem_cur, seg, fm_cur, ln);                     \
+        /* advance on every path; the caller leaves once tile is past the end */              \
+        tile = nxt;                                                                           \
+        nxt = nxt2;                                                                           \
+        nxt2 = nxt3;                                                                          \
+        par ^= 1u;                                                                            \
+        tri = tri_n;                                                                          \
+        fm_cur = fm_nxt;                                                                      \
+        a_cur = a_nxt;                                                                        \
+        rem_cur = rem_nxt;                                                                    \
+    }
+
+    rem_cur = rem_of(tile);
+    load_chunk_rsrc<VEC>(in, chunk_of(tile), rem_cur, lane, va);
+    load_chunk_rsrc<VEC>(in, chunk_of(nxt), rem_of(nxt), lane, vb);
+    SSC_FLAG_AND_ARRIVE(va, tile, rem_cur, fm_cur, a_cur, tri, lane)
+    // B0': without it a fast wavefront could arrive for the next tile
+    // before a slow one has arrived for this one
+    __syncthreads();
+    while (true) {
+        SSC_TILE(va, vb)
+        if (tile >= num_tiles) break;
+        SSC_TILE(vb, va)
+        if (tile >= num_tiles) break;
+    }
+#undef SSC_TILE
+#undef SSC_FLAG_AND_ARRIVE
 }
 
 // =========================================================== scan kernel ---
@@ -955,6 +1131,32 @@ int hip_fail(hipError_t e) {
     return SSC_ERR_HIP;
 }
 
+#define SSC_TRY(expr)                  \
+    do {                               \
+        const int rc_ = (expr);        \
+        if (rc_ != SSC_OK) return rc_; \
+    } while (0)
+
+// Compute units of the current device: the persistent compaction kernel
+// runs one workgroup on each.
+int compute_units(uint32_t *out) {
+    static int cus[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev >= 0 && dev < 64 && cus[dev] > 0) {
+        *out = static_cast<uint32_t>(cus[dev]);
+        return SSC_OK;
+    }
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (c <= 0) return SSC_ERR_DEVICE;
+    if (dev >= 0 && dev < 64) cus[dev] = c;
+    *out = static_cast<uint32_t>(c);
+    return SSC_OK;
+}
+
 // Per-device check that the current device is gfx950 with 64-lane waves.
 int check_device() {
     static int state[64];  // 0 unknown, 1 ok, 2 wrong device
@@ -1057,11 +1259,17 @@ struct LaunchSelect {
                    int32_t pb, void *scratch, uint32_t capacity, int32_t *count, int32_t *ranks,
                    const int32_t *kept, hipStream_t s) {
         const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
+        uint32_t slots = 0;
+        SSC_TRY(compute_units(&slots));
+        const dim3 grid(tiles < slots ? tiles : slots);
         if (partition)
-            hipLaunchKernelGGL((select_kernel<P, VEC, true>), dim3(tiles), dim3(kLbBlock), 0, s, in,
+            hipLaunchKernelGGL((select_kernel<P, VEC, kPartition>), grid, dim3(kLbBlock), 0, s, in,
                                out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
+        else if (ranks != nullptr)
+            hipLaunchKernelGGL((select_kernel<P, VEC, kCompactRanks>), grid, dim3(kLbBlock), 0, s,
+                               in, out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
         else
-            hipLaunchKernelGGL((select_kernel<P, VEC, false>), dim3(tiles), dim3(kLbBlock), 0, s, in,
+            hipLaunchKernelGGL((select_kernel<P, VEC, kCompact>), grid, dim3(kLbBlock), 0, s, in,
                                out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
         return launched();
     }
@@ -1091,12 +1299,6 @@ struct LaunchAtomic {
         return launched();
     }
 };
-
-#define SSC_TRY(expr)                  \
-    do {                               \
-        const int rc_ = (expr);        \
-        if (rc_ != SSC_OK) return rc_; \
-    } while (0)
 
 template <class Op>
 int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename Op::T *total,
