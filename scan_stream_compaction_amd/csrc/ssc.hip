@@ -206,7 +206,7 @@ __device__ __forceinline__ void store_chunk(T *out, int64_t chunk, int lane, uin
 // (uniform).
 template <int P>
 __device__ __forceinline__ uint32_t chunk_ranks(const int32_t (&v)[kLoads][4], int lane,
-                                                uint32_t rem, int32_t pa, int32_t pb,
+                                                uint32_t rem, const PredArgs &pr,
                                                 uint32_t (&lead)[kLoads], uint64_t &mask,
                                                 int bit0) {
     uint32_t running = 0;
@@ -216,7 +216,7 @@ __device__ __forceinline__ uint32_t chunk_ranks(const int32_t (&v)[kLoads][4], i
         uint32_t total = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const bool f = in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pa, pb);
+            const bool f = in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pr);
             mask |= static_cast<uint64_t>(f) << (bit0 + j * 4 + k);
             const uint64_t m = ballot(f);
             below += mbcnt64(m);
@@ -385,7 +385,7 @@ __device__ __forceinline__ void stream_run(const int32_t *run, int32_t *out, uin
 // (j, lane, k), evaluated once. Returns the chunk's flag total (uniform).
 template <int P>
 __device__ __forceinline__ uint32_t chunk_flags(const int32_t (&v)[kSelLoads][4], int lane,
-                                                uint32_t rem, int32_t pa, int32_t pb,
+                                                uint32_t rem, const PredArgs &pr,
                                                 uint32_t &mask) {
     uint32_t total = 0;
     mask = 0;
@@ -396,7 +396,7 @@ __device__ __forceinline__ uint32_t chunk_flags(const int32_t (&v)[kSelLoads][4]
             // element (j, lane, k) is valid iff lane*4 < rem - (j*256 + k): a
             // uniform bound per (j, k) against one per-lane value
             const bool valid = lane * 4 < static_cast<int>(rem) - (j * (kWave * 4) + k);
-            const bool f = valid && pred_eval<P>(v[j][k], pa, pb);
+            const bool f = valid && pred_eval<P>(v[j][k], pr);
             mask |= static_cast<uint32_t>(f) << (j * 4 + k);
             total += static_cast<uint32_t>(__builtin_popcountll(ballot(f)));
         }
@@ -506,8 +506,8 @@ constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
 template <int P, bool VEC, int KIND>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(
-    const int32_t *__restrict__ in, int32_t *__restrict__ out, int64_t n, int32_t pa,
-    int32_t pb, void *scratch, uint32_t num_tiles, uint32_t capacity,
+    const int32_t *__restrict__ in, int32_t *__restrict__ out, int64_t n, PredArgs pr,
+    void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
     const int32_t *__restrict__ kept_total) {
     // one staging region per data wavefront, plus one of padding for run reads
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // publishes T's {aggregate} ({inclusive} for tile 0).
 #define SSC_FLAG_AND_ARRIVE(V, T, R, FM, A, TRI, LN)                                          \
     {                                                                                         \
-        A = uniform(chunk_flags<P>(V, LN, R, pa, pb, FM));                                    \
+        A = uniform(chunk_flags<P>(V, LN, R, pr, FM));                                    \
         if (LN == 0) s_tot[w] = A;                                                            \
         uint32_t before_ = 0;                                                                 \
         if (LN == 0)                                                                          \
@@ -787,7 +787,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 // atomics, so its acquire-release on the done counter orders them.
 template <int P, bool VEC>
 __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t *__restrict__ in, int64_t n,
-                                                       int32_t pa, int32_t pb, uint32_t num_subs,
+                                                       PredArgs pr, uint32_t num_subs,
                                                        void *scratch, int32_t *__restrict__ result) {
     __shared__ uint32_t s_cnt[kWaves];
     const ScratchView sv = view(scratch);
@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t *__restrict
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 acc += static_cast<uint32_t>(__builtin_popcountll(
-                    ballot(in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pa, pb))));
+                    ballot(in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pr))));
     }
     if (lane == 0) s_cnt[w] = acc;
     __syncthreads();
@@ -1040,7 +1040,7 @@ __global__ __launch_bounds__(kBlock) void digit_scatter_kernel(const uint32_t *_
 template <int P, bool VEC, int VARIANT>
 __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *__restrict__ in,
                                                                 int32_t *__restrict__ out,
-                                                                int64_t n, int32_t pa, int32_t pb,
+                                                                int64_t n, PredArgs pr,
                                                                 int32_t *__restrict__ count) {
     __shared__ uint32_t s_tot[kWaves];
     __shared__ uint32_t s_slot;
@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *_
     if constexpr (VARIANT == 0) {
         uint32_t lead[kLoads];
         uint64_t fmask = 0;
-        const uint32_t t = chunk_ranks<P>(v, lane, rem, pa, pb, lead, fmask, 0);
+        const uint32_t t = chunk_ranks<P>(v, lane, rem, pr, lead, fmask, 0);
         if (lane == 0) s_tot[w] = t;
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -1084,7 +1084,7 @@ __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *_
         for (int j = 0; j < kLoads; ++j) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                if (in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pa, pb)) {
+                if (in_chunk(rem, j, lane, k) && pred_eval<P>(v[j][k], pr)) {
                     const int32_t slot = __hip_atomic_fetch_add(count, 1, __ATOMIC_RELAXED,
                                                                 __HIP_MEMORY_SCOPE_AGENT);
                     if (slot < n) out[slot] = v[j][k];
@@ -1197,6 +1197,22 @@ int check_pred(int pred, int32_t pa, int32_t pb) {
     }
 }
 
+// Arguments of a predicate as the kernels take them (see PredArgs); for
+// MOD_LT the constants of division by the invariant modulus a >= 1.
+PredArgs make_pred_args(int pred, int32_t pa, int32_t pb) {
+    PredArgs p{pa, pb, 0u, 0u, 0u, 0u};
+    if (pred == SSC_PRED_MOD_LT) {
+        const uint32_t d = static_cast<uint32_t>(pa);
+        uint32_t l = 0;
+        while ((uint64_t{1} << l) < d) ++l;  // ceil(log2 d)
+        p.magic = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
+        p.sh1 = l < 1u ? l : 1u;
+        p.sh2 = l > 1u ? l - 1u : 0u;
+        p.bias = 0x80000000u % d;
+    }
+    return p;
+}
+
 int check_n(int64_t n) {
     if (n < 0) return SSC_ERR_ARG;
     if (n > INT32_MAX) return SSC_ERR_SIZE;
@@ -1255,8 +1271,8 @@ int dispatch_pred(int pred, bool vec, A... a) {
 
 template <int P, bool VEC>
 struct LaunchSelect {
-    static int run(bool partition, const int32_t *in, int32_t *out, int64_t n, int32_t pa,
-                   int32_t pb, void *scratch, uint32_t capacity, int32_t *count, int32_t *ranks,
+    static int run(bool partition, const int32_t *in, int32_t *out, int64_t n, PredArgs pr,
+                   void *scratch, uint32_t capacity, int32_t *count, int32_t *ranks,
                    const int32_t *kept, hipStream_t s) {
         const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
         uint32_t slots = 0;
@@ -1264,38 +1280,38 @@ struct LaunchSelect {
         const dim3 grid(tiles < slots ? tiles : slots);
         if (partition)
             hipLaunchKernelGGL((select_kernel<P, VEC, kPartition>), grid, dim3(kLbBlock), 0, s, in,
-                               out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
+                               out, n, pr, scratch, tiles, capacity, count, ranks, kept);
         else if (ranks != nullptr)
             hipLaunchKernelGGL((select_kernel<P, VEC, kCompactRanks>), grid, dim3(kLbBlock), 0, s,
-                               in, out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
+                               in, out, n, pr, scratch, tiles, capacity, count, ranks, kept);
         else
             hipLaunchKernelGGL((select_kernel<P, VEC, kCompact>), grid, dim3(kLbBlock), 0, s, in,
-                               out, n, pa, pb, scratch, tiles, capacity, count, ranks, kept);
+                               out, n, pr, scratch, tiles, capacity, count, ranks, kept);
         return launched();
     }
 };
 
 template <int P, bool VEC>
 struct LaunchCount {
-    static int run(const int32_t *in, int64_t n, int32_t pa, int32_t pb, void *scratch,
+    static int run(const int32_t *in, int64_t n, PredArgs pr, void *scratch,
                    int32_t *result, hipStream_t s) {
         hipLaunchKernelGGL((count_kernel<P, VEC>), dim3(reduce_grid(n)), dim3(kBlock), 0, s, in, n,
-                           pa, pb, subs_for(n), scratch, result);
+                           pr, subs_for(n), scratch, result);
         return launched();
     }
 };
 
 template <int P, bool VEC>
 struct LaunchAtomic {
-    static int run(int variant, const int32_t *in, int32_t *out, int64_t n, int32_t pa,
-                   int32_t pb, int32_t *count, hipStream_t s) {
+    static int run(int variant, const int32_t *in, int32_t *out, int64_t n, PredArgs pr,
+                   int32_t *count, hipStream_t s) {
         const uint32_t subs = subs_for(n);
         if (variant == 0)
             hipLaunchKernelGGL((compact_atomic_kernel<P, VEC, 0>), dim3(subs), dim3(kBlock), 0, s,
-                               in, out, n, pa, pb, count);
+                               in, out, n, pr, count);
         else
             hipLaunchKernelGGL((compact_atomic_kernel<P, VEC, 1>), dim3(subs), dim3(kBlock), 0, s,
-                               in, out, n, pa, pb, count);
+                               in, out, n, pr, count);
         return launched();
     }
 };
@@ -1397,7 +1413,8 @@ int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect>(pred, vec, false, in, out, n, pa, pb, scratch,
+    return dispatch_pred<LaunchSelect>(pred, vec, false, in, out, n,
+                                       make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count, ranks,
                                        static_cast<const int32_t *>(nullptr), s);
 }
@@ -1420,8 +1437,9 @@ int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int3
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16);
-    SSC_TRY(dispatch_pred<LaunchCount>(pred, vec, in, n, pa, pb, scratch, count, s));
-    return dispatch_pred<LaunchSelect>(pred, vec, true, in, out, n, pa, pb, scratch,
+    const PredArgs pr = make_pred_args(pred, pa, pb);
+    SSC_TRY(dispatch_pred<LaunchCount>(pred, vec, in, n, pr, scratch, count, s));
+    return dispatch_pred<LaunchSelect>(pred, vec, true, in, out, n, pr, scratch,
                                        capacity_of(scratch_bytes), static_cast<int32_t *>(nullptr),
                                        static_cast<int32_t *>(nullptr),
                                        static_cast<const int32_t *>(count), s);
@@ -1441,7 +1459,8 @@ int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
-    return dispatch_pred<LaunchCount>(pred, aligned(in, 16), in, n, pa, pb, scratch, count, s);
+    return dispatch_pred<LaunchCount>(pred, aligned(in, 16), in, n, make_pred_args(pred, pa, pb),
+                                      scratch, count, s);
 }
 
 int ssc_compact_atomic_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
@@ -1459,7 +1478,8 @@ int ssc_compact_atomic_i32(const int32_t *in, int32_t *out, int64_t n, int pred,
     SSC_TRY(check_device());
     SSC_TRY(clear_words(count, 1, s));
     if (n == 0) return SSC_OK;
-    return dispatch_pred<LaunchAtomic>(pred, aligned(in, 16), variant, in, out, n, pa, pb, count,
+    return dispatch_pred<LaunchAtomic>(pred, aligned(in, 16), variant, in, out, n,
+                                       make_pred_args(pred, pa, pb), count,
                                        s);
 }
 
@@ -1495,11 +1515,13 @@ int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t
         const int32_t *kept = reinterpret_cast<const int32_t *>(sv.kept32 + b);
         if (vec)
             SSC_TRY((LaunchSelect<4, true>::run(true, reinterpret_cast<const int32_t *>(src),
-                                                reinterpret_cast<int32_t *>(dst), n, b, 0, scratch,
+                                                reinterpret_cast<int32_t *>(dst), n,
+                                                make_pred_args(SSC_PRED_BIT_CLEAR, b, 0), scratch,
                                                 cap, nullptr, nullptr, kept, s)));
         else
             SSC_TRY((LaunchSelect<4, false>::run(true, reinterpret_cast<const int32_t *>(src),
-                                                 reinterpret_cast<int32_t *>(dst), n, b, 0,
+                                                 reinterpret_cast<int32_t *>(dst), n,
+                                                 make_pred_args(SSC_PRED_BIT_CLEAR, b, 0),
                                                  scratch, cap, nullptr, nullptr, kept, s)));
         src = dst;
     }

@@ -81,10 +81,26 @@ __device__ __forceinline__ typename Op::T wave_sum(typename Op::T v) {
 }
 
 // ----------------------------------------------------------- predicates ---
-// Numbering matches ssc_pred in ssc.h.
+// Numbering matches ssc_pred in ssc.h. PredArgs carries a predicate's
+// arguments: `a` is the bit of BIT_SET/BIT_CLEAR and the modulus of MOD_LT,
+// `b` the bound of MOD_LT (keep iff mod(x, a) < b, residue in [0, a)).
+//
+// The modulus is invariant over a call, so MOD_LT divides by multiplication
+// (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, the unsigned N = 32 case): with
+// l = ceil(log2 a), magic = floor(2^32 (2^l - a) / a) + 1, sh1 = min(l, 1)
+// and sh2 = max(l - 1, 0), floor(u / a) = (t + ((u - t) >> sh1)) >> sh2 for
+// t = mulhi(magic, u) and every 32-bit u. The host computes the constants
+// (make_pred_args). A signed x is taken as u = x + 2^31, so that
+// mod(x, a) = (u mod a - bias) mod a with bias = 2^31 mod a, a value in
+// (-a, a) before the final correction.
+struct PredArgs {
+    int32_t a, b;
+    uint32_t magic, sh1, sh2, bias;
+};
 
 template <int P>
-__device__ __forceinline__ bool pred_eval(int32_t x, int32_t pa, int32_t pb) {
+__device__ __forceinline__ bool pred_eval(int32_t x, const PredArgs &pr) {
     const uint32_t u = static_cast<uint32_t>(x);
     if constexpr (P == 0) {
         return x != 0;
@@ -93,15 +109,16 @@ __device__ __forceinline__ bool pred_eval(int32_t x, int32_t pa, int32_t pb) {
     } else if constexpr (P == 2) {
         return (u & 1u) == 0u;
     } else if constexpr (P == 3) {
-        return ((u >> pa) & 1u) != 0u;
+        return ((u >> pr.a) & 1u) != 0u;
     } else if constexpr (P == 4) {
-        return ((u >> pa) & 1u) == 0u;
+        return ((u >> pr.a) & 1u) == 0u;
     } else {
-        // Non-negative residue: C's % truncates toward zero, so a negative
-        // remainder is moved up by the modulus (pa >= 1, no overflow).
-        int32_t r = x % pa;
-        if (r < 0) r += pa;
-        return r < pb;
+        const uint32_t v = u ^ 0x80000000u;  // x + 2^31
+        const uint32_t t = __umulhi(pr.magic, v);
+        const uint32_t q = (t + ((v - t) >> pr.sh1)) >> pr.sh2;  // floor(v / a)
+        int32_t r = static_cast<int32_t>(v - q * static_cast<uint32_t>(pr.a) - pr.bias);
+        if (r < 0) r += pr.a;
+        return r < pr.b;
     }
 }
 

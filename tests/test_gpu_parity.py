@@ -279,7 +279,13 @@ def test_edge_sizes_all_ops(n):
 PRED_CASES = [("nonzero", 0, 0), ("odd", 0, 0), ("even", 0, 0), ("bit_set", 0, 0),
               ("bit_set", 13, 0), ("bit_set", 31, 0), ("bit_clear", 0, 0),
               ("bit_clear", 31, 0), ("mod_lt", 100, 50), ("mod_lt", 7, 3), ("mod_lt", 1, 1),
-              ("mod_lt", 2147483647, 5), ("mod_lt", 3, 0)]
+              ("mod_lt", 2147483647, 5), ("mod_lt", 3, 0),
+              # moduli that exercise every shape of the division by an invariant
+              # modulus: powers of two, 2^30 + 1, large primes, bounds <= 0 or >= m
+              ("mod_lt", 2, 1), ("mod_lt", 16, 5), ("mod_lt", 641, 320), ("mod_lt", 65535, 100),
+              ("mod_lt", 1 << 30, 7), ("mod_lt", (1 << 30) + 1, 1 << 29),
+              ("mod_lt", 1000000007, 123456789), ("mod_lt", 2147483646, 1073741823),
+              ("mod_lt", 3, -1), ("mod_lt", 100, 100), ("mod_lt", 5, 2147483647)]
 
 
 @pytest.mark.parametrize("pred,pa,pb", PRED_CASES)
