@@ -381,66 +381,80 @@ __device__ __forceinline__ void stream_run(const int32_t *run, int32_t *out, uin
         __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], r, voff + i * (kWave * 4), 0, 0);
 }
 
-// Flags of one chunk: bit (j*4 + k) of `mask` is the predicate of element
-// (j, lane, k), evaluated once. Returns the chunk's flag total (uniform).
+// Bits of the valid elements (j*256 + lane*4 + k < rem) in the layout of a
+// chunk's flag mask.
+__device__ __forceinline__ uint32_t valid_mask(int lane, uint32_t rem) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j) {
+        int left = static_cast<int>(rem) - (j * (kWave * 4) + lane * 4);
+        left = left < 0 ? 0 : (left > 4 ? 4 : left);
+        m |= ((1u << left) - 1u) << (j * 4);
+    }
+    return m;
+}
+
+// Flags of one chunk as a per-lane mask: bit j*4 + k is the predicate of
+// element (j, lane, k), evaluated once; elements past rem are not flagged.
 template <int P>
-__device__ __forceinline__ uint32_t chunk_flags(const int32_t (&v)[kSelLoads][4], int lane,
-                                                uint32_t rem, const PredArgs &pr,
-                                                uint32_t &mask) {
-    uint32_t total = 0;
-    mask = 0;
+__device__ __forceinline__ uint32_t chunk_mask(const int32_t (&v)[kSelLoads][4], int lane,
+                                               uint32_t rem, const PredArgs &pr) {
+    uint32_t mask = 0;
 #pragma unroll
     for (int j = 0; j < kSelLoads; ++j)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            // element (j, lane, k) is valid iff lane*4 < rem - (j*256 + k): a
-            // uniform bound per (j, k) against one per-lane value
-            const bool valid = lane * 4 < static_cast<int>(rem) - (j * (kWave * 4) + k);
-            const bool f = valid && pred_eval<P>(v[j][k], pr);
-            mask |= static_cast<uint32_t>(f) << (j * 4 + k);
-            total += static_cast<uint32_t>(__builtin_popcountll(ballot(f)));
-        }
-    return total;
+        for (int k = 0; k < 4; ++k)
+            mask |= static_cast<uint32_t>(pred_eval<P>(v[j][k], pr)) << (j * 4 + k);
+    if (rem < static_cast<uint32_t>(kSelChunk)) mask &= valid_mask(lane, rem);
+    return mask;
+}
+
+// The chunk's flag total (uniform): a wavefront sum of the lanes' counts.
+__device__ __forceinline__ uint32_t chunk_total(uint32_t mask) {
+    const uint32_t incl = wave_inclusive_scan<SumU32>(static_cast<uint32_t>(__builtin_popcount(mask)));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
 }
 
 // lead[j] = flagged elements of the chunk before element (j, lane, 0): the
-// flags of earlier loads plus those of load j in lower lanes (ballot +
-// mbcnt, recomputed from the mask rather than kept live across the tile).
-__device__ __forceinline__ void chunk_leads(uint32_t mask, uint32_t (&lead)[kSelLoads]) {
+// flags of loads before j plus those of load j in lower lanes. A lane's
+// eight per-load counts (0..4 each) travel as three words of 10-bit fields,
+// so three wavefront scans rank all eight loads at once (a field's sum over
+// 64 lanes is at most 256). Returns the chunk total (uniform).
+__device__ __forceinline__ uint32_t chunk_leads(uint32_t mask, uint32_t (&lead)[kSelLoads]) {
+    constexpr int kWords = (kSelLoads + 2) / 3;
+    uint32_t word[kWords] = {};
+#pragma unroll
+    for (int j = 0; j < kSelLoads; ++j)
+        word[j / 3] |= static_cast<uint32_t>(__builtin_popcount((mask >> (j * 4)) & 15u))
+                       << (10 * (j % 3));
+    uint32_t excl[kWords], tot[kWords];
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+        const uint32_t incl = wave_inclusive_scan<SumU32>(word[q]);
+        excl[q] = incl - word[q];
+        tot[q] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+    }
     uint32_t running = 0;
 #pragma unroll
     for (int j = 0; j < kSelLoads; ++j) {
-        uint32_t below = 0, total = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint64_t m = ballot((mask >> (j * 4 + k)) & 1u);
-            below += mbcnt64(m);
-            total += static_cast<uint32_t>(__builtin_popcountll(m));
-        }
-        lead[j] = running + below;
-        running += total;
+        const int sh = 10 * (j % 3);
+        lead[j] = running + ((excl[j / 3] >> sh) & 1023u);
+        running += (tot[j / 3] >> sh) & 1023u;
     }
+    return running;
 }
 
 // ranks[i] = seg + (flags before element i in its chunk) for the chunk's rem
-// valid elements, written in the load layout. The lead of load j is built
-// up load by load (as in chunk_leads) so that no array of leads stays live.
+// valid elements, written in the load layout.
 template <bool VEC>
 __device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint32_t rem,
                                             uint32_t seg, uint32_t mask, int lane) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(ranks + chunk, rem * 4u);
-    uint32_t running = seg;
+    uint32_t lead[kSelLoads];
+    chunk_leads(mask, lead);
 #pragma unroll
     for (int j = 0; j < kSelLoads; ++j) {
-        uint32_t below = 0, total = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint64_t m = ballot((mask >> (j * 4 + k)) & 1u);
-            below += mbcnt64(m);
-            total += static_cast<uint32_t>(__builtin_popcountll(m));
-        }
-        uint32_t x = running + below;
-        running += total;
+        uint32_t x = seg + lead[j];
         uint32_t q[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -589,7 +603,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // publishes T's {aggregate} ({inclusive} for tile 0).
 #define SSC_FLAG_AND_ARRIVE(V, T, R, FM, A, TRI, LN)                                          \
     {                                                                                         \
-        A = uniform(chunk_flags<P>(V, LN, R, pr, FM));                                    \
+        FM = chunk_mask<P>(V, LN, R, pr);                                                     \
+        A = chunk_total(FM);                                                                  \
         if (LN == 0) s_tot[w] = A;                                                            \
         uint32_t before_ = 0;                                                                 \
         if (LN == 0)                                                                          \
@@ -619,20 +634,18 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         int ln = lane;                                                                        \
         asm volatile("" : "+v"(ln));                                                          \
         {                                                                                     \
+            /* every element gets a slot of its own, no branches: survivors at    */            \
+            /* their rank, the others after all survivors at a_cur + (index -     */            \
+            /* rank), elements past rem included (they land past the runs)        */            \
             uint32_t lead[kSelLoads];                                                         \
             chunk_leads(fm_cur, lead);                                                        \
             _Pragma("unroll") for (int j = 0; j < kSelLoads; ++j) {                           \
                 uint32_t r = lead[j];                                                         \
+                const uint32_t rej = a_cur + static_cast<uint32_t>(j * (kWave * 4) + ln * 4); \
                 _Pragma("unroll") for (int k = 0; k < 4; ++k) {                               \
-                    const bool f = (fm_cur >> (j * 4 + k)) & 1u;                              \
-                    if (f) {                                                                  \
-                        s_stage[w][r] = CUR[j][k];                                            \
-                    } else if constexpr (KIND == kPartition) {                                \
-                        const uint32_t local =                                                \
-                            static_cast<uint32_t>(j * (kWave * 4) + ln * 4 + k);              \
-                        if (local < rem_cur) s_stage[w][a_cur + local - r] = CUR[j][k];       \
-                    }                                                                         \
-                    r += f ? 1u : 0u;                                                         \
+                    const uint32_t f = (fm_cur >> (j * 4 + k)) & 1u;                          \
+                    s_stage[w][f ? r : rej + k - r] = CUR[j][k];                              \
+                    r += f;                                                                   \
                 }                                                                             \
             }                                                                                 \
         }                                                                                     \
