@@ -63,22 +63,25 @@ def measured_traffic():
 
 
 def timed_calls(fn, steps: int, stream):
-    """Run fn() `steps` times between two synchronizations; event pairs around
-    every call on `stream` (the stream the kernel runs on)."""
+    """Run fn() `steps` times back to back between two synchronizations, with
+    one HIP event pair around the whole region on `stream` (the stream the
+    kernels run on). Returns (region ms, ms per call, wall seconds). Events
+    between the calls are avoided: on this GPU each recorded event writes the
+    caches back, which puts about 10 us between launches that run back to
+    back otherwise."""
     import torch
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         fn()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    region_ms = starts[0].elapsed_time(ends[-1])
-    return region_ms, per, wall
+    region_ms = start.elapsed_time(end)
+    return region_ms, region_ms / steps, wall
 
 
 def cpu_baseline(x_np, target_s: float = 12.0):
@@ -134,10 +137,10 @@ def other_workloads(dev, steps: int, stream) -> dict:
 
     rows = {}
 
-    def timed(name, fn, alg_bytes, **info):
-        fn()
-        _, per, _ = timed_calls(fn, steps, stream)
-        us = sum(per) / len(per) * 1e3
+    def timed(name, op, args, kwargs, alg_bytes, **info):
+        fn = ssc.prepared(op, *args, **kwargs)
+        _, per_ms, _ = timed_calls(fn, steps, stream)
+        us = per_ms * 1e3
         rows[name] = {"us": round(us, 2), "effective_GB/s": round(alg_bytes / (us * 1e-6) / 1e9, 1),
                       "algorithmic_bytes": alg_bytes, **info}
 
@@ -153,8 +156,8 @@ def other_workloads(dev, steps: int, stream) -> dict:
     mask = x != 0
     k = int(mask.sum())
     assert int(cnt.item()) == k and torch.equal(out[:k], x[mask]) and torch.equal(rk, excl(mask.int()))
-    timed("compact_nonzero_ranks_65533", lambda: ssc.compact(x, "nonzero", out=out, count=cnt, ranks=rk,
-                                                             scratch=sc), 4 * n + 4 * k + 4 * n, kept=k)
+    timed("compact_nonzero_ranks_65533", ssc.compact, (x, "nonzero"),
+          dict(out=out, count=cnt, ranks=rk, scratch=sc), 4 * n + 4 * k + 4 * n, kept=k)
 
     # 8,387,997 values in [0, 10): zero removal and even/odd partition
     x = torch.from_numpy(wl.zero_removal_input()).to(dev)
@@ -164,13 +167,13 @@ def other_workloads(dev, steps: int, stream) -> dict:
     mask = x != 0
     k = int(mask.sum())
     assert int(cnt.item()) == k and torch.equal(out[:k], x[mask])
-    timed("compact_nonzero_8387997", lambda: ssc.compact(x, "nonzero", out=out, count=cnt, scratch=sc),
+    timed("compact_nonzero_8387997", ssc.compact, (x, "nonzero"), dict(out=out, count=cnt, scratch=sc),
           4 * n + 4 * k, kept=k)
     out, cnt = ssc.partition(x, "even", scratch=sc)
     ev = (x & 1) == 0
     k = int(ev.sum())
     assert int(cnt.item()) == k and torch.equal(out, torch.cat([x[ev], x[~ev]]))
-    timed("partition_even_8387997", lambda: ssc.partition(x, "even", out=out, count=cnt, scratch=sc),
+    timed("partition_even_8387997", ssc.partition, (x, "even"), dict(out=out, count=cnt, scratch=sc),
           8 * n, kept=k, note="algorithmic 8N; the counting pre-pass adds a 4N read")
 
     # 10^7 scans: int32 (i % 8) + 1 and fp32 uniform [0, 1)
@@ -179,13 +182,13 @@ def other_workloads(dev, steps: int, stream) -> dict:
     sc = ssc.new_scratch(n, dev)
     out, tot = ssc.exclusive_scan(x, scratch=sc)
     assert torch.equal(out, excl(x)) and int(tot.item()) == 45_000_000
-    timed("scan_i32_1e7", lambda: ssc.exclusive_scan(x, out=out, total=tot, scratch=sc), 8 * n)
+    timed("scan_i32_1e7", ssc.exclusive_scan, (x,), dict(out=out, total=tot, scratch=sc), 8 * n)
     x = torch.from_numpy(wl.scan_f32_input()).to(dev)
     outf, totf = ssc.exclusive_scan(x, scratch=sc)
     ref = torch.cumsum(x.to(torch.float64), 0) - x.to(torch.float64)
     rel = ((outf.to(torch.float64) - ref).abs() / ref.abs().clamp_min(1e-300))[1:]
     assert float(rel.max()) <= 1e-5 and float(outf[0]) == 0.0
-    timed("scan_f32_1e7", lambda: ssc.exclusive_scan(x, out=outf, total=totf, scratch=sc), 8 * n,
+    timed("scan_f32_1e7", ssc.exclusive_scan, (x,), dict(out=outf, total=totf, scratch=sc), 8 * n,
           max_rel_err=float(rel.max()))
 
     # 2^24 uint32 keys: 32 chained stable partitions by bit
@@ -197,13 +200,13 @@ def other_workloads(dev, steps: int, stream) -> dict:
     ssc.radix_sort(x, out=out, tmp=tmp, scratch=sc)
     want = torch.sort(x.to(torch.int64) & 0xFFFFFFFF).values
     assert torch.equal(out.to(torch.int64) & 0xFFFFFFFF, want)
-    timed("radix_sort_u32_2p24", lambda: ssc.radix_sort(x, out=out, tmp=tmp, scratch=sc), 32 * 8 * n,
+    timed("radix_sort_u32_2p24", ssc.radix_sort, (x,), dict(out=out, tmp=tmp, scratch=sc), 32 * 8 * n,
           note="32 one-bit passes, 8N algorithmic each; each pass adds a 4N counting read")
     rows["radix_sort_u32_2p24"]["keys_per_s"] = round(n / (rows["radix_sort_u32_2p24"]["us"] * 1e-6), 1)
     sc4 = torch.zeros(ssc.radix_sort4_scratch_bytes(n), dtype=torch.uint8, device=dev)
     ssc.radix_sort4(x, out=out, tmp=tmp, scratch=sc4)
     assert torch.equal(out.to(torch.int64) & 0xFFFFFFFF, want)
-    timed("radix_sort4_u32_2p24", lambda: ssc.radix_sort4(x, out=out, tmp=tmp, scratch=sc4), 8 * 8 * n,
+    timed("radix_sort4_u32_2p24", ssc.radix_sort4, (x,), dict(out=out, tmp=tmp, scratch=sc4), 8 * 8 * n,
           note="8 passes of 4-bit digits, 8N algorithmic each; each pass adds a 4N counting read "
                "and a scan of the 16 x tiles count table")
     rows["radix_sort4_u32_2p24"]["keys_per_s"] = round(n / (rows["radix_sort4_u32_2p24"]["us"] * 1e-6), 1)
@@ -244,8 +247,9 @@ def main():
     scratch = ssc.new_scratch(n, dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        ssc.compact(x, "odd", out=out, count=count, scratch=scratch)
+    # the timed step repeats the library call with its arguments marshalled
+    # once, so that Python work between launches does not leave the GPU idle
+    step = ssc.prepared(ssc.compact, x, "odd", out=out, count=count, scratch=scratch)
 
     # parity before timing
     step()
@@ -262,9 +266,8 @@ def main():
 
     for _ in range(args.warmup):
         step()
-    region_ms, per_ms, wall = timed_calls(step, args.steps, stream)
-    ms_per_step = region_ms / args.steps
-    kernel_ms = sum(per_ms) / len(per_ms)
+    region_ms, ms_per_step, wall = timed_calls(step, args.steps, stream)
+    kernel_ms = ms_per_step  # one launch per step: the average launch duration over the region
     alg_bytes = 4 * n + 4 * m
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
@@ -275,9 +278,8 @@ def main():
     extra = {}
     if args.extra in ("all", "copy"):
         cp = torch.empty_like(x)
-        _, cp_per, _ = timed_calls(lambda: ssc.copy(x, cp), args.steps, stream)
+        _, cp_ms, _ = timed_calls(ssc.prepared(ssc.copy, x, cp), args.steps, stream)
         assert torch.equal(cp, x)
-        cp_ms = sum(cp_per) / len(cp_per)
         cp_gbps = 8 * n / (cp_ms * 1e-3) / 1e9
         extra["copy_i32"] = {"us": round(cp_ms * 1e3, 2), "GB/s": round(cp_gbps, 1),
                              "bytes": 8 * n}
@@ -286,26 +288,23 @@ def main():
     if args.extra == "all":
         for s in wl.SWEEP_KEEP:
             cnt = torch.zeros(1, dtype=torch.int32, device=dev)
-            fn = lambda: ssc.compact(x, "mod_lt", wl.SWEEP_MOD, s, out=out, count=cnt,
-                                     scratch=scratch)
-            fn()
+            fn = ssc.prepared(ssc.compact, x, "mod_lt", wl.SWEEP_MOD, s, out=out, count=cnt,
+                              scratch=scratch)
             torch.cuda.synchronize()
             ms_ = int(cnt.item())
             mask = (torch.remainder(x, wl.SWEEP_MOD) < s)
             assert ms_ == int(mask.sum().item())
             assert torch.equal(out[:ms_], torch.masked_select(x, mask))
             del mask
-            _, per, _ = timed_calls(fn, args.steps, stream)
-            k_ms = sum(per) / len(per)
+            _, k_ms, _ = timed_calls(fn, args.steps, stream)
             b = 4 * n + 4 * ms_
             extra[f"compact_mod100_lt{s}"] = {
                 "kept": ms_, "us": round(k_ms * 1e3, 2), "GB/s": round(b / (k_ms * 1e-3) / 1e9, 1),
                 "pct_hbm_peak": round(b / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS * 100, 1)}
             cnt2 = torch.zeros(1, dtype=torch.int32, device=dev)
-            fa = lambda: ssc.compact_atomic(x, "mod_lt", wl.SWEEP_MOD, s, out=out, count=cnt2)
-            _, per, _ = timed_calls(fa, args.steps, stream)
+            fa = ssc.prepared(ssc.compact_atomic, x, "mod_lt", wl.SWEEP_MOD, s, out=out, count=cnt2)
+            _, k_ms, _ = timed_calls(fa, args.steps, stream)
             assert int(cnt2.item()) == ms_
-            k_ms = sum(per) / len(per)
             extra[f"atomic_mod100_lt{s}"] = {
                 "us": round(k_ms * 1e3, 2), "GB/s": round(b / (k_ms * 1e-3) / 1e9, 1)}
     if args.extra == "all":

@@ -84,6 +84,38 @@ def _check(call: str, rc: int) -> None:
         raise SSCError(call, rc, detail)
 
 
+_recording = None  # list of library calls being recorded by prepared(), or None
+
+
+def _call(name: str, fn, *args) -> None:
+    """Make one library call (and record it while prepared() is recording)."""
+    if _recording is not None:
+        _recording.append((name, fn, args))
+    _check(name, fn(*args))
+
+
+def prepared(op, *args, **kwargs):
+    """Run op(*args, **kwargs) once and return a callable that repeats the
+    same library calls (same buffers, same stream) with their arguments
+    already marshalled: for timing loops, where the per-call Python work of
+    the ops would otherwise leave the GPU waiting between launches. The
+    callable returns what op returned; tensors it allocated stay alive with it.
+    """
+    global _recording
+    calls = []
+    _recording = calls
+    try:
+        result = op(*args, **kwargs)
+    finally:
+        _recording = None
+
+    def run():
+        for name, fn, a in calls:
+            _check(name, fn(*a))
+        return result
+    return run
+
+
 def _pred(p) -> int:
     return PRED[p] if isinstance(p, str) else int(p)
 
@@ -137,8 +169,8 @@ def exclusive_scan(x: torch.Tensor, out: torch.Tensor | None = None,
     if fn is None or out.dtype != x.dtype or total.dtype != x.dtype:
         raise TypeError("exclusive_scan takes int32 or float32 tensors of one dtype")
     _dev(out)
-    _check(fn[0], fn[1](x.data_ptr(), out.data_ptr(), x.numel(), _ptr(total), scratch.data_ptr(),
-                        scratch.numel(), _stream(x)))
+    _call(fn[0], fn[1], x.data_ptr(), out.data_ptr(), x.numel(), _ptr(total), scratch.data_ptr(),
+          scratch.numel(), _stream(x))
     return out, total
 
 
@@ -165,9 +197,9 @@ def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
         rk = ranks
     if scratch is None:
         scratch = new_scratch(n, x.device)
-    _check("ssc_compact_i32", lib().ssc_compact_i32(
-        x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), _ptr(rk),
-        scratch.data_ptr(), scratch.numel(), _stream(x)))
+    _call("ssc_compact_i32", lib().ssc_compact_i32,
+          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), _ptr(rk),
+          scratch.data_ptr(), scratch.numel(), _stream(x))
     return (out, count, rk) if rk is not None else (out, count)
 
 
@@ -185,9 +217,9 @@ def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     if scratch is None:
         scratch = new_scratch(n, x.device)
-    _check("ssc_partition_i32", lib().ssc_partition_i32(
-        x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
-        scratch.data_ptr(), scratch.numel(), _stream(x)))
+    _call("ssc_partition_i32", lib().ssc_partition_i32,
+          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
+          scratch.data_ptr(), scratch.numel(), _stream(x))
     return out, count
 
 
@@ -199,9 +231,9 @@ def count_if(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     if scratch is None:
         scratch = new_scratch(0, x.device)
-    _check("ssc_count_if_i32", lib().ssc_count_if_i32(
-        x.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(), scratch.data_ptr(),
-        scratch.numel(), _stream(x)))
+    _call("ssc_count_if_i32", lib().ssc_count_if_i32,
+          x.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(), scratch.data_ptr(),
+          scratch.numel(), _stream(x))
     return count
 
 
@@ -214,9 +246,9 @@ def compact_atomic(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
         out = torch.empty_like(x)
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=x.device)
-    _check("ssc_compact_atomic_i32", lib().ssc_compact_atomic_i32(
-        x.data_ptr(), out.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(),
-        variant, _stream(x)))
+    _call("ssc_compact_atomic_i32", lib().ssc_compact_atomic_i32,
+          x.data_ptr(), out.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(),
+          variant, _stream(x))
     return out, count
 
 
@@ -231,9 +263,9 @@ def radix_sort(x: torch.Tensor, *, out: torch.Tensor | None = None,
         tmp = torch.empty_like(x)
     if scratch is None:
         scratch = new_scratch(n, x.device, radix=True)
-    _check("ssc_radix_sort_u32", lib().ssc_radix_sort_u32(
-        x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, scratch.data_ptr(), scratch.numel(),
-        _stream(x)))
+    _call("ssc_radix_sort_u32", lib().ssc_radix_sort_u32,
+          x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, scratch.data_ptr(), scratch.numel(),
+          _stream(x))
     return out
 
 
@@ -253,9 +285,9 @@ def radix_sort4(x: torch.Tensor, passes: int = 8, *, out: torch.Tensor | None = 
         tmp = torch.empty_like(x)
     if scratch is None:
         scratch = torch.zeros(radix_sort4_scratch_bytes(n), dtype=torch.uint8, device=x.device)
-    _check("ssc_radix_sort4_u32", lib().ssc_radix_sort4_u32(
-        x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, passes, scratch.data_ptr(),
-        scratch.numel(), _stream(x)))
+    _call("ssc_radix_sort4_u32", lib().ssc_radix_sort4_u32,
+          x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, passes, scratch.data_ptr(),
+          scratch.numel(), _stream(x))
     return out
 
 
@@ -263,6 +295,5 @@ def copy(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     _dev(x)
     if out is None:
         out = torch.empty_like(x)
-    _check("ssc_copy_i32", lib().ssc_copy_i32(x.data_ptr(), out.data_ptr(), x.numel(),
-                                              _stream(x)))
+    _call("ssc_copy_i32", lib().ssc_copy_i32, x.data_ptr(), out.data_ptr(), x.numel(), _stream(x))
     return out

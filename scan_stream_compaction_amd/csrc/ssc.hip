@@ -516,6 +516,7 @@ __device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint3
 // of the workgroup that claimed it (any earlier claim of that workgroup is
 // lower and finished), and its look-back needs only lower, finished tiles.
 enum { kCompact = 0, kCompactRanks = 1, kPartition = 2 };
+constexpr int kSelPollSleep = 32;  // look-back poll interval, s_sleep units (measured)
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
 template <int P, bool VEC, int KIND>
@@ -566,7 +567,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             if (lane == 0 && nxt2 < num_tiles)
                 nxt3 = static_cast<uint32_t>(claim_tile(sv, num_tiles, claims, capacity));
             uint32_t prefix = 0;
-            if (tile != 0) prefix = look_back<SumU32>(sv.desc, tile, tag, sv.timed_out);
+            if (tile != 0)
+                prefix = look_back<SumU32, kSelPollSleep>(sv.desc, tile, tag, sv.timed_out);
             if (lane == 0) {
                 s_base[par] = prefix;
                 s_next[par] = nxt3;
@@ -695,6 +697,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 }
 
 // =========================================================== scan kernel ---
+constexpr int kScanPollSleep = 127;  // look-back poll interval, s_sleep units (measured)
 // Exclusive scan of 32-bit values with the same tile shape, control
 // wavefront and look-back; the tile aggregate is the sum of the values. Per
 // load j a lane sums its 4 values, a DPP wavefront scan gives the lane
@@ -727,7 +730,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 
     if (w == kCtrlWave) {
         T prefix = Op::zero();
-        if (tile != 0) prefix = look_back<Op>(sv.desc, tile, tag, sv.timed_out);
+        if (tile != 0) prefix = look_back<Op, kScanPollSleep>(sv.desc, tile, tag, sv.timed_out);
         if (lane == 0) s_base = Op::bits(prefix);
         __syncthreads();  // B1
         T chunk_before[kLbRounds];

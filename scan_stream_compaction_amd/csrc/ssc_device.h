@@ -152,11 +152,12 @@ __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
 // Decoupled look-back, run by one whole wavefront of the tile's workgroup.
 //
 // Waiting: first the wavefront polls only the immediate predecessor's
-// descriptor (one lane, one 8-byte agent-scope load), sleeping about 3.4 us
-// (s_sleep 127) between polls, until it has published. Measured on MI355X,
-// frequent coherent polling by hundreds of waiting tiles costs more
-// throughput than it saves latency: shorter sleeps and wider polls were
-// slower.
+// descriptor (one lane, one 8-byte agent-scope load), sleeping SLEEP x 64
+// clocks between polls, until it has published. Measured on MI355X: with
+// one workgroup per tile (hundreds of tiles waiting at once), frequent
+// coherent polling costs more throughput than it saves latency, and about
+// 3.4 us (s_sleep 127) is best; the persistent compaction kernel, whose
+// control wavefronts wait on tiles published earlier, is fastest at s_sleep 32.
 //
 // Walking: then each step reads the descriptors of the 64 tiles just below
 // the window end at once (one load, 512 contiguous bytes). The window is
@@ -180,10 +181,8 @@ __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
 // can never leave the kernel spinning.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-#ifndef SSC_POLL_SLEEP
-#define SSC_POLL_SLEEP 127  // s_sleep units of 64 clocks
-#endif
-__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(SSC_POLL_SLEEP); }
+template <int SLEEP>
+__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(SLEEP); }
 
 // Descriptor of tile idx (>= 0) read as base + 32-bit byte offset, so the
 // address needs one VGPR; tiles below 0 read as inclusive with value 0.
@@ -202,7 +201,7 @@ __device__ __forceinline__ uint32_t status_of(uint64_t word, uint32_t tag) {
 // slower on MI355X: the extra coherent traffic costs more than the steps saved.
 constexpr int kLookBackWindows = 1;
 
-template <class Op>
+template <class Op, int SLEEP>
 __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
                                     uint32_t *timed_out) {
     using T = typename Op::T;
@@ -220,7 +219,7 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
                 __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return prefix;
         }
-        poll_pause();
+        poll_pause<SLEEP>();
     }
     spins &= 0x7FFFFFFFu;
     int32_t end = static_cast<int32_t>(tile);
@@ -258,7 +257,7 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
                     __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return prefix;
             }
-            poll_pause();
+            poll_pause<SLEEP>();
         }
         // add the values from the nearest inclusive tile up (everything read
         // when there is none)

@@ -5,8 +5,10 @@ relative of the fp64 oracle (bit-exact where every prefix is an exact
 integer below 2^24). The unordered atomic compaction is checked as a
 multiset. Inputs come from the seeded generators in
 scan_stream_compaction_amd.workloads, at the five workloads' full sizes and
-at edge sizes around the 30720-element tile, its 15360-element rounds and
-1024-element wavefront chunks.
+at edge sizes around the 30720-element tile, the compaction kernel's
+2048-element wavefront chunks, and the scan kernel's 15360-element rounds
+and 1024-element chunks; also at more tiles than the persistent compaction
+kernel has workgroups (one per compute unit).
 """
 from __future__ import annotations
 
@@ -25,7 +27,8 @@ pytestmark = pytest.mark.gpu
 
 T = 30720   # elements per tile (one claim)
 S = 15360   # elements per round (15 data wavefronts x 1024)
-C = 1024    # elements per wavefront chunk
+C = 1024    # elements per wavefront chunk (scan kernel)
+C2 = 2048   # elements per wavefront chunk (compaction kernel)
 SENTINEL = -123456789
 DEV = "cuda"
 
@@ -257,9 +260,9 @@ def test_radix4_unaligned_in_place_and_odd_passes():
 
 # -------------------------------------------------------------- edge cases ---
 
-EDGE_N = [0, 1, 2, 3, 5, 63, 64, 65, 255, 256, 257, C - 1, C, C + 1, 7 * C + 3, S - 1, S,
-          S + 1, T - 1, T, T + 1, 2 * T - 1, 2 * T, 2 * T + 1, 5 * T + 611, 64 * T + 13,
-          65 * T + T - 1]
+EDGE_N = [0, 1, 2, 3, 5, 63, 64, 65, 255, 256, 257, C - 1, C, C + 1, C2 - 1, C2, C2 + 1,
+          7 * C + 3, 14 * C2 - 1, 14 * C2 + 1, S - 1, S, S + 1, T - 1, T, T + 1, 2 * T - 1, 2 * T,
+          2 * T + 1, 3 * T + 2 * C2 + 1, 5 * T + 611, 64 * T + 13, 65 * T + T - 1, 700 * T + 17]
 
 
 @pytest.mark.parametrize("n", EDGE_N)
@@ -417,6 +420,23 @@ def test_runs_on_a_side_stream():
     s.synchronize()
     assert int(cnt.cpu()[0]) == m
     assert checks.first_mismatch(out.cpu().numpy()[:m], want) == -1
+
+
+def test_prepared_call_repeats_the_same_library_call():
+    x = wl.full_int32(91, 3 * T + 5)
+    want, m = oracle.compact_i32(x, oracle.PRED_ODD)
+    xd = dev(x)
+    out = torch.full_like(xd, SENTINEL)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    run = ssc.prepared(ssc.compact, xd, "odd", out=out, count=cnt)
+    for _ in range(3):
+        out.fill_(SENTINEL)
+        cnt.zero_()
+        got_out, got_cnt = run()
+        assert got_out is out and got_cnt is cnt
+        assert int(host(cnt)[0]) == m
+        o = host(out)
+        assert checks.first_mismatch(o[:m], want) == -1 and np.all(o[m:] == SENTINEL)
 
 
 def test_argument_errors_raise_on_gpu():
