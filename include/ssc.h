@@ -79,8 +79,9 @@ typedef enum ssc_pred {
     SSC_PRED_MOD_LT = 5
 } ssc_pred;
 
-/* Elements per tile (one workgroup's share of the single pass, one tile
- * number claimed from the atomic counter). */
+/* Elements per tile: the share of the single pass behind one tile number
+ * claimed from the atomic counter and one look-back descriptor (a workgroup
+ * of the compaction kernel processes several tiles in turn). */
 int64_t ssc_tile_elems(void);
 
 /* Scratch bytes needed by the scan, compaction, partition and counting calls
@@ -177,9 +178,9 @@ int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t
 int ssc_radix_sort4_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t n, int passes,
                         void *scratch, size_t scratch_bytes, void *stream);
 
-/* out[i] = in[i]: the copy kernel with the same tile and load/store width as
- * the single pass, the practical bandwidth ceiling ("Day 33 compaction.cu",
- * copyInts; "Day 32 scan_2.cu", copyFloats). No overlap allowed. */
+/* out[i] = in[i] with 128-bit loads and stores: the bandwidth reference the
+ * single pass is compared with ("Day 33 compaction.cu", copyInts; "Day 32
+ * scan_2.cu", copyFloats). No overlap allowed. */
 int ssc_copy_i32(const int32_t *in, int32_t *out, int64_t n, void *stream);
 
 /* Human-readable name of a status code (static storage). */
