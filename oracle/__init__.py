@@ -62,6 +62,12 @@ def lib() -> ctypes.CDLL:
         L.orc_exclusive_scan_i32.restype = None
         L.orc_exclusive_scan_f32.argtypes = [f32p, f64p, i64, f64p]
         L.orc_exclusive_scan_f32.restype = None
+        L.orc_inclusive_scan_i32.argtypes = [i32p, i32p, i64]
+        L.orc_inclusive_scan_i32.restype = None
+        L.orc_inclusive_scan_f32.argtypes = [f32p, f64p, i64]
+        L.orc_inclusive_scan_f32.restype = None
+        L.orc_select_index_i32.argtypes = [i32p, i32p, i64, c_int, i32, i32]
+        L.orc_select_index_i32.restype = i64
         L.orc_count.argtypes = [i32p, i64, c_int, i32, i32]
         L.orc_count.restype = i64
         L.orc_compact_i32.argtypes = [i32p, i32p, i64, c_int, i32, i32, i32p]
@@ -120,6 +126,31 @@ def exclusive_scan_f32(x):
     lib().orc_exclusive_scan_f32(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_double), x.size,
                                  ctypes.byref(total))
     return out, float(total.value)
+
+
+def inclusive_scan_i32(x) -> np.ndarray:
+    """out[i] = x[0] + ... + x[i] with modulo-2^32 wrap."""
+    x = _i32(x)
+    out = np.empty(x.size, np.int32)
+    lib().orc_inclusive_scan_i32(_ptr(x, ctypes.c_int32), _ptr(out, ctypes.c_int32), x.size)
+    return out
+
+
+def inclusive_scan_f32(x) -> np.ndarray:
+    """out[i] = x[0] + ... + x[i] of fp32 values, accumulated and returned in fp64."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.size, np.float64)
+    lib().orc_inclusive_scan_f32(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_double), x.size)
+    return out
+
+
+def select_index_i32(x, pred: int, pa: int = 0, pb: int = 0):
+    """(indices, count): positions of the elements for which the predicate holds."""
+    x = _i32(x)
+    idx = np.empty(x.size, np.int32)
+    m = lib().orc_select_index_i32(_ptr(x, ctypes.c_int32), _ptr(idx, ctypes.c_int32), x.size,
+                                   pred, pa, pb)
+    return idx[:m].copy(), int(m)
 
 
 def count(x, pred: int, pa: int = 0, pb: int = 0) -> int:

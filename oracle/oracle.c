@@ -20,6 +20,8 @@
  *     predicate is x & 1 (Listing 13-17).
  *   - "Day 32 scan_2.cu", scanExclusiveCpu: exclusive scan with a double
  *     accumulator (partial sums are kept in double precision).
+ *   - "Day 31 scan.cu", scanInclusiveCpu: the inclusive form of the scan,
+ *     out[i] = in[0] + ... + in[i] (whole array here, not restarted per tile).
  *   - "CIS 565 Project 2: Stream Compaction": the printed exclusive-scan and
  *     compaction transcripts fix the exclusive convention and the order.
  *
@@ -130,6 +132,26 @@ void orc_exclusive_scan_f32(const float *in, double *out, int64_t n,
     if (total) *total = running;
 }
 
+/* Inclusive scan of int32 values with modulo-2^32 wrap:
+ * out[i] = in[0] + ... + in[i]. */
+void orc_inclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n) {
+    uint32_t running = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        running += (uint32_t)in[i];
+        out[i] = (int32_t)running;
+    }
+}
+
+/* Inclusive scan of fp32 values, accumulated in fp64 and kept in fp64:
+ * out[i] = sum_{j<=i} (double)in[j]. */
+void orc_inclusive_scan_f32(const float *in, double *out, int64_t n) {
+    double running = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        running += (double)in[i];
+        out[i] = running;
+    }
+}
+
 /* Number of elements for which the predicate holds. */
 int64_t orc_count(const int32_t *in, int64_t n, int pred, int32_t pa,
                   int32_t pb) {
@@ -148,6 +170,22 @@ int64_t orc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred,
         if (ranks) ranks[i] = (int32_t)m;
         if (orc_pred(in[i], pred, pa, pb)) {
             out[m] = in[i];
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* Selection form of compaction ("CUDA Handbook ch. 13": a flag's exclusive-
+ * scan value is the element's output index): the positions i of the
+ * elements for which the predicate holds, in increasing order; returns their
+ * number. */
+int64_t orc_select_index_i32(const int32_t *in, int32_t *idx, int64_t n, int pred,
+                             int32_t pa, int32_t pb) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred(in[i], pred, pa, pb)) {
+            idx[m] = (int32_t)i;
             ++m;
         }
     }

@@ -74,6 +74,21 @@ def test_cis565_scan_transcript(golden_dir):
     assert out2[-6:].tolist() == g["scan_npot_tail"]
 
 
+def test_cis565_scan_transcript_inclusive(golden_dir):
+    """The printed exclusive outputs fix the inclusive ones: inclusive[i] is the
+    printed exclusive entry i + 1, and the last inclusive entry is the total."""
+    g = _read_golden(os.path.join(golden_dir, "cis565_scan_transcript.txt"))
+    x = _cis565_scan_array(g)
+    inc = oracle.inclusive_scan_i32(x)
+    assert inc[:12].tolist() == g["scan_pot_head"][1:13]
+    assert inc[-7:-1].tolist() == g["scan_pot_tail"]
+    assert inc[-1] == g["scan_pot_tail"][-1] + g["input_tail"][-1]   # 6518
+    n_npot = g["size_npot"][0]
+    inc2 = oracle.inclusive_scan_i32(x[:n_npot])
+    assert inc2[:12].tolist() == g["scan_npot_head"][1:13]
+    assert inc2[-7:-1].tolist() == g["scan_npot_tail"]
+
+
 def test_cis565_compaction_transcript(golden_dir):
     g = _read_golden(os.path.join(golden_dir, "cis565_compaction_transcript.txt"))
     head = np.array(g["input_head"], np.int32)
@@ -149,6 +164,64 @@ def test_scan_f32_accumulates_in_double():
         assert abs(out[i] - ref) <= 1e-12 * ref
     ref = math.fsum(xd)
     assert abs(total - ref) <= 1e-12 * ref
+
+
+def test_inclusive_scans_closed_forms():
+    """(i % 8) + 1 gives inclusive[i] = 36*floor((i+1)/8) + r(r+1)/2 with
+    r = (i+1) % 8; every fourth 2.0f gives inclusive[i] = (i+1) + ceil((i+1)/4),
+    exactly in fp64 (all prefixes are integers below 2^24)."""
+    n = 10_000_000
+    x = (np.arange(n, dtype=np.int64) % 8 + 1).astype(np.int32)
+    inc = oracle.inclusive_scan_i32(x)
+    j = np.arange(1, n + 1, dtype=np.int64)
+    r = j % 8
+    assert checks.first_mismatch(inc.astype(np.int64), 36 * (j // 8) + r * (r + 1) // 2) == -1
+    assert inc[-1] == 45_000_000
+    xf = np.ones(n, np.float32)
+    xf[0::4] = 2.0
+    incf = oracle.inclusive_scan_f32(xf)
+    assert np.array_equal(incf, (j + (j + 3) // 4).astype(np.float64))
+
+
+def test_inclusive_scan_f32_accumulates_in_double():
+    from scan_stream_compaction_amd import workloads
+    x = workloads.unit_float32(0x4321, 100_000)
+    inc = oracle.inclusive_scan_f32(x)
+    xd = x.astype(np.float64).tolist()
+    for i in (0, 5, 999, 65_536, 99_999):
+        ref = math.fsum(xd[:i + 1])
+        assert abs(inc[i] - ref) <= 1e-12 * ref
+
+
+def test_inclusive_minus_exclusive_is_the_input():
+    from scan_stream_compaction_amd import workloads
+    x = workloads.full_int32(8, 40_003)
+    inc = oracle.inclusive_scan_i32(x)
+    exc, total = oracle.exclusive_scan_i32(x)
+    assert np.array_equal((inc.astype(np.int64) - exc) % (1 << 32), x.astype(np.int64) % (1 << 32))
+    assert inc[-1] == total
+    inc2 = oracle.inclusive_scan_i32(np.array([2**31 - 1, 1, -5], np.int32))
+    assert inc2.tolist() == [2**31 - 1, -2**31, 2**31 - 5]
+
+
+def test_select_index_transcript_and_library_routine(golden_dir):
+    """The positions of the CIS 565 head's nonzero values, and np.flatnonzero of
+    the flags on a large input; indexing the input by them gives the compaction."""
+    g = _read_golden(os.path.join(golden_dir, "cis565_compaction_transcript.txt"))
+    head = np.array(g["input_head"], np.int32)
+    idx, m = oracle.select_index_i32(head, oracle.PRED_NONZERO)
+    assert idx.tolist() == [0, 1, 2, 5, 6, 7, 9, 10, 12] and m == 9
+    assert head[idx].tolist() == g["compact_pot_head"][:9]
+    from scan_stream_compaction_amd import workloads
+    x = workloads.full_int32(17, 70_001)
+    for pred, pa, pb in ((oracle.PRED_ODD, 0, 0), (oracle.PRED_MOD_LT, 100, 37),
+                         (oracle.PRED_BIT_CLEAR, 31, 0)):
+        idx, m = oracle.select_index_i32(x, pred, pa, pb)
+        assert np.array_equal(idx, np.flatnonzero(oracle.flags(x, pred, pa, pb)))
+        surv, m2 = oracle.compact_i32(x, pred, pa, pb)
+        assert m == m2 and np.array_equal(x[idx], surv)
+    e, m = oracle.select_index_i32(np.zeros(0, np.int32), oracle.PRED_ODD)
+    assert m == 0 and e.size == 0
 
 
 def test_scan_i32_wraps_modulo_2_32():
