@@ -115,6 +115,19 @@ int ssc_exclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *
 int ssc_exclusive_scan_f32(const float *in, float *out, int64_t n, float *total,
                            void *scratch, size_t scratch_bytes, void *stream);
 
+/* Inclusive scan of int32 values: out[i] = in[0] + ... + in[i], with
+ * two's-complement wrap; `total` (nullable) receives out[n-1] (0 for n = 0).
+ * Aliasing rules as for the exclusive scan.
+ * Source: "Day 31 scan.cu" (scanInclusiveCpu and the inclusive block scans;
+ * here over the whole array, not restarted per tile). */
+int ssc_inclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
+                           void *scratch, size_t scratch_bytes, void *stream);
+
+/* Inclusive scan of fp32 values, accumulated as the exclusive fp32 scan is;
+ * same accuracy statement and aliasing rules. Source: "Day 31 scan.cu". */
+int ssc_inclusive_scan_f32(const float *in, float *out, int64_t n, float *total,
+                           void *scratch, size_t scratch_bytes, void *stream);
+
 /* Order-preserving compaction: out[0 .. count) = the elements x with P(x)
  * true, in input order; *count = their number (the top of the scan of the
  * flags). `ranks` (nullable) receives the exclusive scan of the flags for
@@ -126,6 +139,17 @@ int ssc_exclusive_scan_f32(const float *in, float *out, int64_t n, float *total,
 int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
                     int32_t pb, int32_t *count, int32_t *ranks, void *scratch,
                     size_t scratch_bytes, void *stream);
+
+/* Selection (the index form of compaction): idx[0 .. count) = the
+ * positions i, increasing, of the elements with P(in[i]) true; *count =
+ * their number. idx[count .. n) is not written. Same single pass as
+ * ssc_compact_i32, with each survivor's index scattered instead of its
+ * value. No overlap between in, idx and count is allowed.
+ * Source: "CUDA Handbook ch. 13, Stream Compaction" (the exclusive scan of
+ * the flags gives each kept element its output position). */
+int ssc_select_index_i32(const int32_t *in, int32_t *idx, int64_t n, int pred, int32_t pa,
+                         int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
+                         void *stream);
 
 /* Stable partition: out[0 .. K) = the elements with P true, out[K .. n) =
  * the elements with P false, both in input order; *count = K. Kept x[i]

@@ -36,6 +36,9 @@ SIGNATURES = {
     "ssc_scratch_init": (_INT, [_P, _SZ, _P]),
     "ssc_exclusive_scan_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_exclusive_scan_f32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_inclusive_scan_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_inclusive_scan_f32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_select_index_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
     "ssc_compact_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "ssc_partition_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
     "ssc_count_if_i32": (_INT, [_P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
@@ -157,6 +160,16 @@ def new_scratch(n: int, device, radix: bool = False) -> torch.Tensor:
 def exclusive_scan(x: torch.Tensor, out: torch.Tensor | None = None,
                    total: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
     """(out, total): exclusive scan of int32 (wrapping) or float32 values."""
+    return _scan(x, out, total, scratch, "exclusive")
+
+
+def inclusive_scan(x: torch.Tensor, out: torch.Tensor | None = None,
+                   total: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """(out, total): inclusive scan of int32 (wrapping) or float32 values."""
+    return _scan(x, out, total, scratch, "inclusive")
+
+
+def _scan(x, out, total, scratch, form):
     _dev(x)
     if out is None:
         out = torch.empty_like(x)
@@ -164,10 +177,10 @@ def exclusive_scan(x: torch.Tensor, out: torch.Tensor | None = None,
         total = torch.empty(1, dtype=x.dtype, device=x.device)
     if scratch is None:
         scratch = new_scratch(x.numel(), x.device)
-    fn = {torch.int32: ("ssc_exclusive_scan_i32", lib().ssc_exclusive_scan_i32),
-          torch.float32: ("ssc_exclusive_scan_f32", lib().ssc_exclusive_scan_f32)}.get(x.dtype)
-    if fn is None or out.dtype != x.dtype or total.dtype != x.dtype:
-        raise TypeError("exclusive_scan takes int32 or float32 tensors of one dtype")
+    names = {torch.int32: f"ssc_{form}_scan_i32", torch.float32: f"ssc_{form}_scan_f32"}
+    if x.dtype not in names or out.dtype != x.dtype or total.dtype != x.dtype:
+        raise TypeError(f"{form}_scan takes int32 or float32 tensors of one dtype")
+    fn = (names[x.dtype], getattr(lib(), names[x.dtype]))
     _dev(out)
     _call(fn[0], fn[1], x.data_ptr(), out.data_ptr(), x.numel(), _ptr(total), scratch.data_ptr(),
           scratch.numel(), _stream(x))
@@ -201,6 +214,27 @@ def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
           x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), _ptr(rk),
           scratch.data_ptr(), scratch.numel(), _stream(x))
     return (out, count, rk) if rk is not None else (out, count)
+
+
+def select_index(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+                 out: torch.Tensor | None = None, count: torch.Tensor | None = None,
+                 scratch: torch.Tensor | None = None):
+    """(idx, count): idx[:count] holds the positions of the elements for which
+    the predicate holds, increasing; entries past count are not written."""
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("select_index takes int32")
+    n = x.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if scratch is None:
+        scratch = new_scratch(n, x.device)
+    _call("ssc_select_index_i32", lib().ssc_select_index_i32,
+          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
+          scratch.data_ptr(), scratch.numel(), _stream(x))
+    return out, count
 
 
 def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,

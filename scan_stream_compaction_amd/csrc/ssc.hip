@@ -515,7 +515,9 @@ __device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint3
 // tiles + gridDim.x claims. The lowest unfinished tile is the current tile
 // of the workgroup that claimed it (any earlier claim of that workgroup is
 // lower and finished), and its look-back needs only lower, finished tiles.
-enum { kCompact = 0, kCompactRanks = 1, kPartition = 2 };
+// KIND: compaction (survivors' values), compaction that also writes the
+// ranks, stable partition, or selection (survivors' indices).
+enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3 };
 constexpr int kSelPollSleep = 32;  // look-back poll interval, s_sleep units (measured)
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
@@ -641,12 +643,15 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             /* rank), elements past rem included (they land past the runs)        */            \
             uint32_t lead[kSelLoads];                                                         \
             chunk_leads(fm_cur, lead);                                                        \
+            /* (a selection stages each element's index instead of its value)    */            \
+            const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * 4;              \
             _Pragma("unroll") for (int j = 0; j < kSelLoads; ++j) {                           \
                 uint32_t r = lead[j];                                                         \
                 const uint32_t rej = a_cur + static_cast<uint32_t>(j * (kWave * 4) + ln * 4); \
                 _Pragma("unroll") for (int k = 0; k < 4; ++k) {                               \
                     const uint32_t f = (fm_cur >> (j * 4 + k)) & 1u;                          \
-                    s_stage[w][f ? r : rej + k - r] = CUR[j][k];                              \
+                    s_stage[w][f ? r : rej + k - r] =                                         \
+                        KIND == kSelectIndex ? first + (j * (kWave * 4) + k) : CUR[j][k];     \
                     r += f;                                                                   \
                 }                                                                             \
             }                                                                                 \
@@ -698,12 +703,12 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 
 // =========================================================== scan kernel ---
 constexpr int kScanPollSleep = 127;  // look-back poll interval, s_sleep units (measured)
-// Exclusive scan of 32-bit values with the same tile shape, control
-// wavefront and look-back; the tile aggregate is the sum of the values. Per
-// load j a lane sums its 4 values, a DPP wavefront scan gives the lane
-// offsets, and results leave with the same 128-bit layout they were read
-// with. in == out is allowed.
-template <class Op, bool VEC>
+// Exclusive (or, INCL, inclusive) scan of 32-bit values: one tile per
+// workgroup with a control wavefront for the look-back; the tile aggregate is
+// the sum of the values. Per load j a lane sums its 4 values, a DPP wavefront
+// scan gives the lane offsets, and results leave with the same 128-bit layout
+// they were read with. in == out is allowed.
+template <class Op, bool VEC, bool INCL>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void scan_kernel(const typename Op::T *in,
                                                         typename Op::T *out, int64_t n,
                                                         void *scratch, uint32_t num_tiles,
@@ -761,8 +766,13 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const T x = v[q][j][k];
-                v[q][j][k] = s;
-                s = Op::add(s, x);
+                if constexpr (INCL) {
+                    s = Op::add(s, x);
+                    v[q][j][k] = s;
+                } else {
+                    v[q][j][k] = s;
+                    s = Op::add(s, x);
+                }
             }
             const T incl = wave_inclusive_scan<Op>(s);
             const uint32_t up =
@@ -1287,22 +1297,30 @@ int dispatch_pred(int pred, bool vec, A... a) {
 
 template <int P, bool VEC>
 struct LaunchSelect {
-    static int run(bool partition, const int32_t *in, int32_t *out, int64_t n, PredArgs pr,
+    static int run(int kind, const int32_t *in, int32_t *out, int64_t n, PredArgs pr,
                    void *scratch, uint32_t capacity, int32_t *count, int32_t *ranks,
                    const int32_t *kept, hipStream_t s) {
         const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
         uint32_t slots = 0;
         SSC_TRY(compute_units(&slots));
         const dim3 grid(tiles < slots ? tiles : slots);
-        if (partition)
+        switch (kind) {
+        case kPartition:
             hipLaunchKernelGGL((select_kernel<P, VEC, kPartition>), grid, dim3(kLbBlock), 0, s, in,
                                out, n, pr, scratch, tiles, capacity, count, ranks, kept);
-        else if (ranks != nullptr)
+            break;
+        case kCompactRanks:
             hipLaunchKernelGGL((select_kernel<P, VEC, kCompactRanks>), grid, dim3(kLbBlock), 0, s,
                                in, out, n, pr, scratch, tiles, capacity, count, ranks, kept);
-        else
+            break;
+        case kSelectIndex:
+            hipLaunchKernelGGL((select_kernel<P, VEC, kSelectIndex>), grid, dim3(kLbBlock), 0, s,
+                               in, out, n, pr, scratch, tiles, capacity, count, ranks, kept);
+            break;
+        default:
             hipLaunchKernelGGL((select_kernel<P, VEC, kCompact>), grid, dim3(kLbBlock), 0, s, in,
                                out, n, pr, scratch, tiles, capacity, count, ranks, kept);
+        }
         return launched();
     }
 };
@@ -1332,7 +1350,7 @@ struct LaunchAtomic {
     }
 };
 
-template <class Op>
+template <class Op, bool INCL>
 int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename Op::T *total,
               void *scratch, size_t scratch_bytes, hipStream_t s) {
     using T = typename Op::T;
@@ -1352,10 +1370,10 @@ int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename
     const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
     const uint32_t cap = capacity_of(scratch_bytes);
     if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL((scan_kernel<Op, true>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
+        hipLaunchKernelGGL((scan_kernel<Op, true, INCL>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
                            scratch, tiles, cap, total);
     else
-        hipLaunchKernelGGL((scan_kernel<Op, false>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
+        hipLaunchKernelGGL((scan_kernel<Op, false, INCL>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
                            scratch, tiles, cap, total);
     return launched();
 }
@@ -1395,15 +1413,29 @@ int ssc_scratch_init(void *scratch, size_t scratch_bytes, void *stream) {
 
 int ssc_exclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
                            void *scratch, size_t scratch_bytes, void *stream) {
-    return scan_impl<SumU32>(reinterpret_cast<const uint32_t *>(in), reinterpret_cast<uint32_t *>(out),
+    return scan_impl<SumU32, false>(reinterpret_cast<const uint32_t *>(in), reinterpret_cast<uint32_t *>(out),
                              n, reinterpret_cast<uint32_t *>(total), scratch, scratch_bytes,
                              static_cast<hipStream_t>(stream));
 }
 
 int ssc_exclusive_scan_f32(const float *in, float *out, int64_t n, float *total, void *scratch,
                            size_t scratch_bytes, void *stream) {
-    return scan_impl<SumF32>(in, out, n, total, scratch, scratch_bytes,
+    return scan_impl<SumF32, false>(in, out, n, total, scratch, scratch_bytes,
                              static_cast<hipStream_t>(stream));
+}
+
+int ssc_inclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
+                           void *scratch, size_t scratch_bytes, void *stream) {
+    return scan_impl<SumU32, true>(reinterpret_cast<const uint32_t *>(in),
+                                   reinterpret_cast<uint32_t *>(out), n,
+                                   reinterpret_cast<uint32_t *>(total), scratch, scratch_bytes,
+                                   static_cast<hipStream_t>(stream));
+}
+
+int ssc_inclusive_scan_f32(const float *in, float *out, int64_t n, float *total, void *scratch,
+                           size_t scratch_bytes, void *stream) {
+    return scan_impl<SumF32, true>(in, out, n, total, scratch, scratch_bytes,
+                                   static_cast<hipStream_t>(stream));
 }
 
 int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
@@ -1429,9 +1461,34 @@ int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect>(pred, vec, false, in, out, n,
+    return dispatch_pred<LaunchSelect>(pred, vec, ranks ? kCompactRanks : kCompact, in, out, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count, ranks,
+                                       static_cast<const int32_t *>(nullptr), s);
+}
+
+int ssc_select_index_i32(const int32_t *in, int32_t *idx, int64_t n, int pred, int32_t pa,
+                         int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
+                         void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (count == nullptr || (n > 0 && (in == nullptr || idx == nullptr))) return SSC_ERR_ARG;
+    SSC_TRY(check_pred(pred, pa, pb));
+    if (!aligned(in, 4) || !aligned(idx, 4) || !aligned(count, 4)) return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (overlap(in, bytes, idx, bytes) || overlap(count, 4, in, bytes) ||
+        overlap(count, 4, idx, bytes))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, idx, bytes) ||
+        overlap(scratch, scratch_bytes, count, 4))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    return dispatch_pred<LaunchSelect>(pred, aligned(in, 16), kSelectIndex, in, idx, n,
+                                       make_pred_args(pred, pa, pb), scratch,
+                                       capacity_of(scratch_bytes), count,
+                                       static_cast<int32_t *>(nullptr),
                                        static_cast<const int32_t *>(nullptr), s);
 }
 
@@ -1455,7 +1512,7 @@ int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int3
     const bool vec = aligned(in, 16);
     const PredArgs pr = make_pred_args(pred, pa, pb);
     SSC_TRY(dispatch_pred<LaunchCount>(pred, vec, in, n, pr, scratch, count, s));
-    return dispatch_pred<LaunchSelect>(pred, vec, true, in, out, n, pr, scratch,
+    return dispatch_pred<LaunchSelect>(pred, vec, kPartition, in, out, n, pr, scratch,
                                        capacity_of(scratch_bytes), static_cast<int32_t *>(nullptr),
                                        static_cast<int32_t *>(nullptr),
                                        static_cast<const int32_t *>(count), s);
@@ -1530,12 +1587,12 @@ int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t
         uint32_t *dst = (b % 2 == 0) ? tmp : out;  // pass 31 lands in out
         const int32_t *kept = reinterpret_cast<const int32_t *>(sv.kept32 + b);
         if (vec)
-            SSC_TRY((LaunchSelect<4, true>::run(true, reinterpret_cast<const int32_t *>(src),
+            SSC_TRY((LaunchSelect<4, true>::run(kPartition, reinterpret_cast<const int32_t *>(src),
                                                 reinterpret_cast<int32_t *>(dst), n,
                                                 make_pred_args(SSC_PRED_BIT_CLEAR, b, 0), scratch,
                                                 cap, nullptr, nullptr, kept, s)));
         else
-            SSC_TRY((LaunchSelect<4, false>::run(true, reinterpret_cast<const int32_t *>(src),
+            SSC_TRY((LaunchSelect<4, false>::run(kPartition, reinterpret_cast<const int32_t *>(src),
                                                  reinterpret_cast<int32_t *>(dst), n,
                                                  make_pred_args(SSC_PRED_BIT_CLEAR, b, 0),
                                                  scratch, cap, nullptr, nullptr, kept, s)));
@@ -1579,7 +1636,7 @@ int ssc_radix_sort4_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_
             hipLaunchKernelGGL((digit_count_kernel<false>), dim3(tiles), dim3(kBlock), 0, s, src, n,
                                4 * p, cnt, tiles);
         SSC_TRY(launched());
-        SSC_TRY(scan_impl<SumU32>(cnt, cnt, entries, nullptr, scratch, scan_bytes, s));
+        SSC_TRY((scan_impl<SumU32, false>(cnt, cnt, entries, nullptr, scratch, scan_bytes, s)));
         if (vec)
             hipLaunchKernelGGL((digit_scatter_kernel<true>), dim3(tiles), dim3(kBlock), 0, s, src,
                                dst, n, 4 * p, cnt, tiles);

@@ -164,6 +164,20 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     assert L.ssc_radix_sort4_u32(A, B, None, 100, 8, S, big, None) == ARG
     assert L.ssc_radix_sort4_u32(A, B, C, 100, 8, S, 512 + 7, None) == SCRATCH
     assert L.ssc_radix_sort4_u32(A, B, C, 100, 8, A, big, None) == ALIAS
+    # inclusive scans: same rules as the exclusive ones
+    assert L.ssc_inclusive_scan_i32(A, A + 4, 100, None, S, big, None) == ALIAS
+    assert L.ssc_inclusive_scan_f32(A, B, 100, B + 8, S, big, None) == ALIAS
+    assert L.ssc_inclusive_scan_i32(A, None, 100, None, S, big, None) == ARG
+    assert L.ssc_inclusive_scan_i32(A, B, INT32_MAX + 1, None, S, big, None) == SIZE
+    assert L.ssc_inclusive_scan_f32(A, B, 100, None, S, 100, None) == SCRATCH
+    # selection: no overlap, predicate arguments checked, scratch sized
+    assert L.ssc_select_index_i32(A, A + 8, 100, 1, 0, 0, C, S, big, None) == ALIAS
+    assert L.ssc_select_index_i32(A, B, 100, 1, 0, 0, B + 4, S, big, None) == ALIAS
+    assert L.ssc_select_index_i32(A, B, 100, 5, 0, 0, C, S, big, None) == ARG
+    assert L.ssc_select_index_i32(A, B, 100, 1, 0, 0, None, S, big, None) == ARG
+    assert L.ssc_select_index_i32(A, B, -1, 1, 0, 0, C, S, big, None) == ARG
+    assert L.ssc_select_index_i32(A, B, 100, 1, 0, 0, C, S, 100, None) == SCRATCH
+    assert L.ssc_select_index_i32(A, B, 100, 1, 0, 0, C, B, big, None) == ALIAS
     # copy
     assert L.ssc_copy_i32(A, A + 4, 100, None) == ALIAS
     assert L.ssc_copy_i32(A, B, -1, None) == ARG

@@ -97,6 +97,43 @@ def check_scan_f32(x: np.ndarray, exact=False):
     return max_rel
 
 
+def check_inclusive_i32(x: np.ndarray, xd=None, out=None):
+    want = oracle.inclusive_scan_i32(x)
+    xd = dev(x) if xd is None else xd
+    got, tot = ssc.inclusive_scan(xd, out=out)
+    assert checks.first_mismatch(host(got), want) == -1
+    assert int(host(tot)[0]) == (int(want[-1]) if x.size else 0)
+
+
+def check_inclusive_f32(x: np.ndarray, exact=False):
+    ref = oracle.inclusive_scan_f32(x)
+    out, tot = ssc.inclusive_scan(dev(x))
+    got = host(out)
+    if exact:
+        assert checks.first_mismatch(got.astype(np.float64), ref) == -1
+        return 0.0
+    max_rel, max_abs, ok = checks.f32_scan_rel_errors(got, ref)
+    say(f"  inclusive f32 scan n={x.size}: max rel err {max_rel:.3e}, max abs err {max_abs:.3e}")
+    assert ok, (max_rel, max_abs)
+    if x.size:
+        assert abs(float(host(tot)[0]) - ref[-1]) <= checks.F32_SCAN_REL_TOL * abs(ref[-1])
+    return max_rel
+
+
+def check_select_index(x: np.ndarray, pred, pa=0, pb=0, xd=None):
+    """Indices of the survivors against the oracle; idx past count untouched."""
+    p = ssc.PRED[pred] if isinstance(pred, str) else pred
+    want, m = oracle.select_index_i32(x, p, pa, pb)
+    xd = dev(x) if xd is None else xd
+    idx = torch.full_like(xd, SENTINEL)
+    _, cnt = ssc.select_index(xd, p, pa, pb, out=idx)
+    assert int(host(cnt)[0]) == m, (pred, pa, pb)
+    o = host(idx)
+    assert checks.first_mismatch(o[:m], want) == -1
+    assert np.all(o[m:] == SENTINEL), "selection wrote past count"
+    return m
+
+
 # ------------------------------------------------------------ device check ---
 
 def test_device_is_gfx950_wave64():
@@ -155,6 +192,31 @@ def test_scan_f32_every_fourth_two_exact():
     check_scan_f32(wl.every_fourth_two(wl.N_SCAN), exact=True)
 
 
+def test_inclusive_scans_full_size():
+    """10^7 int32 (i % 8) + 1 bit-exact (closed form 36*floor((i+1)/8) + r(r+1)/2,
+    r = (i+1) % 8); fp32 uniform within 1e-5; every fourth 2.0f bit-exact."""
+    x = wl.mod8_plus1(wl.N_SCAN)
+    out, tot = ssc.inclusive_scan(dev(x))
+    j = np.arange(1, x.size + 1, dtype=np.int64)
+    r = j % 8
+    assert checks.first_mismatch(host(out).astype(np.int64), 36 * (j // 8) + r * (r + 1) // 2) == -1
+    assert int(host(tot)[0]) == 45_000_000
+    check_inclusive_i32(x)
+    check_inclusive_f32(wl.scan_f32_input())
+    check_inclusive_f32(wl.every_fourth_two(wl.N_SCAN), exact=True)
+
+
+def test_inclusive_scan_wraps_and_in_place():
+    x = wl.full_int32(5, 3 * T + 17)
+    x[:3] = [2**31 - 1, 1, -5]
+    check_inclusive_i32(x)
+    xd = dev(x)
+    check_inclusive_i32(x, xd=xd.clone(), out=None)
+    y = xd.clone()
+    ssc.inclusive_scan(y, out=y)
+    assert checks.first_mismatch(host(y), oracle.inclusive_scan_i32(x)) == -1
+
+
 @pytest.fixture(scope="module")
 def headline():
     say("  generating 2^28 full-range int32 ...")
@@ -168,6 +230,13 @@ def test_headline_odd_compaction_full_size(headline):
     x, xd = headline
     m = check_compact(x, "odd", xd=xd, ranks=False)
     say(f"  odd kept {m} of {x.size} ({m / x.size:.4f})")
+
+
+def test_headline_odd_selection_full_size(headline):
+    """2^28 int32, predicate odd: the positions of the survivors."""
+    x, xd = headline
+    m = check_select_index(x, "odd", xd=xd)
+    say(f"  odd selected {m} of {x.size}")
 
 
 @pytest.mark.parametrize("keep", wl.SWEEP_KEEP)
@@ -272,6 +341,8 @@ def test_edge_sizes_all_ops(n):
     check_compact(x, "odd")
     check_partition(x, "even")
     check_scan_i32(x)
+    check_inclusive_i32(x)
+    check_select_index(x, "odd")
     check_scan_f32(wl.unit_float32(2000 + n, n))
     got = ssc.count_if(dev(x), "odd")
     assert int(host(got)[0]) == oracle.count(x, oracle.PRED_ODD)
@@ -297,6 +368,7 @@ def test_every_predicate_full_range(pred, pa, pb):
     x[:8] = [0, -1, 1, -2147483648, 2147483647, -3, 4, -100]
     check_compact(x, pred, pa, pb)
     check_partition(x, pred, pa, pb)
+    check_select_index(x, pred, pa, pb)
     want, m = oracle.compact_i32(x, ssc.PRED[pred], pa, pb)
     out, cnt = ssc.compact_atomic(dev(x), pred, pa, pb, variant=1)
     assert int(host(cnt)[0]) == m
@@ -337,6 +409,13 @@ def test_unaligned_arrays_take_the_32bit_path(n):  # noqa: C901
     cp = torch.empty(n + 1, dtype=torch.int32, device=DEV)[1:]
     ssc.copy(xs, cp)
     assert checks.first_mismatch(host(cp), x[1:]) == -1
+    iw, mi = oracle.select_index_i32(x[1:], oracle.PRED_EVEN)
+    iout = torch.full((n + 1,), SENTINEL, dtype=torch.int32, device=DEV)[1:]
+    _, icnt = ssc.select_index(xs, "even", out=iout)
+    assert int(host(icnt)[0]) == mi and checks.first_mismatch(host(iout)[:mi], iw) == -1
+    inc = torch.empty(n + 1, dtype=torch.int32, device=DEV)[1:]
+    ssc.inclusive_scan(xs, out=inc)
+    assert checks.first_mismatch(host(inc), oracle.inclusive_scan_i32(x[1:])) == -1
 
 
 def test_scan_i32_wraps_and_in_place():
