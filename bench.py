@@ -190,6 +190,11 @@ def other_workloads(dev, steps: int, stream) -> dict:
     assert float(rel.max()) <= 1e-5 and float(outf[0]) == 0.0
     timed("scan_f32_1e7", ssc.exclusive_scan, (x,), dict(out=outf, total=totf, scratch=sc), 8 * n,
           max_rel_err=float(rel.max()))
+    xi = torch.from_numpy(wl.mod8_plus1(wl.N_SCAN)).to(dev)
+    outi, toti = ssc.inclusive_scan(xi, scratch=sc)
+    assert torch.equal(outi, torch.cumsum(xi.to(torch.int64), 0).to(torch.int32))
+    timed("inclusive_scan_i32_1e7", ssc.inclusive_scan, (xi,), dict(out=outi, total=toti, scratch=sc),
+          8 * n)
 
     # 2^24 uint32 keys: 32 chained stable partitions by bit
     x = torch.from_numpy(wl.radix_input().view(np.int32)).to(dev)
@@ -308,6 +313,16 @@ def main():
             extra[f"atomic_mod100_lt{s}"] = {
                 "us": round(k_ms * 1e3, 2), "GB/s": round(b / (k_ms * 1e-3) / 1e9, 1)}
     if args.extra == "all":
+        idx = torch.empty_like(x)
+        cnt3 = torch.zeros(1, dtype=torch.int32, device=dev)
+        fi = ssc.prepared(ssc.select_index, x, "odd", out=idx, count=cnt3, scratch=scratch)
+        torch.cuda.synchronize()
+        assert int(cnt3.item()) == m and torch.equal(idx[:m], torch.nonzero(x & 1).flatten().to(torch.int32))
+        _, k_ms, _ = timed_calls(fi, args.steps, stream)
+        extra["select_index_odd_2p28"] = {
+            "us": round(k_ms * 1e3, 2), "GB/s": round(alg_bytes / (k_ms * 1e-3) / 1e9, 1),
+            "note": "positions of the odd elements; same bytes as the compaction"}
+        del idx
         extra["other_workloads"] = other_workloads(dev, max(5, args.steps // 5), stream)
     if extra:
         log("extra: " + json.dumps(extra))

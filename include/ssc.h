@@ -86,7 +86,7 @@ int64_t ssc_tile_elems(void);
 
 /* Scratch bytes needed by the scan, compaction, partition and counting calls
  * for n elements: a 512-byte header (tile counter and epoch, counting-pass
- * accumulators) plus one 8-byte descriptor per tile. */
+ * accumulators) plus 16 bytes of look-back descriptors per tile. */
 size_t ssc_scratch_bytes(int64_t n);
 
 /* Scratch bytes needed by ssc_radix_sort_u32 for n keys. */
@@ -108,10 +108,14 @@ int ssc_scratch_init(void *scratch, size_t scratch_bytes, void *stream);
 int ssc_exclusive_scan_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
                            void *scratch, size_t scratch_bytes, void *stream);
 
-/* Exclusive scan of fp32 values, accumulated in fp32 in a tiled order (not
- * the sequential order): every output is within a relative error of about
- * 1e-5 of the exactly accumulated prefix for the inputs this library is
- * tested on (non-negative values, n up to 10^7). Aliasing rules as above. */
+/* Exclusive scan of fp32 values. The prefix inside a tile (at most 30720
+ * values) is summed in fp32 in a tiled order; the carries between tiles are
+ * fp64, and each output is rounded to fp32 once from the fp64 sum of carry
+ * and in-tile prefix, so the error does not grow with the number of tiles
+ * (the double accumulation of "Day 32 scan_2.cu", scanExclusiveCpu, for the
+ * part that spans tiles). Tested within 1e-6 relative of the exactly
+ * accumulated prefix for non-negative values up to n = 2^27. Aliasing rules
+ * as above. */
 int ssc_exclusive_scan_f32(const float *in, float *out, int64_t n, float *total,
                            void *scratch, size_t scratch_bytes, void *stream);
 

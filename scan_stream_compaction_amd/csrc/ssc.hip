@@ -32,6 +32,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "ssc.h"
 #include "ssc_device.h"
 
@@ -58,12 +60,13 @@ constexpr int kCtrlWave = 15;                  // index of the control wavefront
 constexpr int kLbRounds = 2;                   // chunks per data wavefront per tile
 constexpr int kLbSub = kDataWaves * kChunk;    // 15360 elements per round
 constexpr int kTile = kLbSub * kLbRounds;      // 30720 elements per tile
-constexpr uint32_t kMaxTiles = 1u << 17;       // power of two >= tiles of the largest n
+constexpr uint32_t kMaxTiles = 1u << 18;       // power of two >= descriptor words of the largest n
 constexpr int kReduceGrid = 512;               // workgroups of the grid-stride counting kernels
 constexpr int kSpread = 16;                    // accumulators a counting pass spreads over
 
 static_assert(kLbBlock == (kDataWaves + 1) * kWave, "one control wavefront");
-static_assert(static_cast<int64_t>(kMaxTiles) * kTile >= 2147483647LL, "kMaxTiles");
+// two words per tile for the wide descriptors of the fp32 scans
+static_assert(static_cast<int64_t>(kMaxTiles) * kTile >= 2LL * 2147483647LL, "kMaxTiles");
 
 // Scratch header (bytes). Descriptors follow it, one 64-bit word per tile.
 constexpr size_t kHeaderBytes = 512;
@@ -271,11 +274,11 @@ __device__ __forceinline__ void tile_prefixes(const uint32_t *s_pre, int w,
 // {epoch:32 | tile:32}. A call makes exactly `claims` claims in all; the one
 // that receives the last number resets the counter and advances the epoch
 // (every claim of a call therefore carries the same epoch), and clears one
-// stale descriptor slot: slot (epoch mod kMaxTiles) when this call does not
-// use it. Over any kMaxTiles consecutive calls every slot is thus rewritten
-// or cleared, far within the 2^30-call period of the tag, so no stale
-// descriptor can match a later tag.
-__device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t num_tiles,
+// stale descriptor word: word (epoch mod kMaxTiles) when this call does not
+// use it (it uses words 0 .. words_used - 1). Over any kMaxTiles consecutive
+// calls every word is thus rewritten or cleared, far within the 2^30-call
+// period of the tag, so no stale descriptor can match a later tag.
+__device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t words_used,
                                                uint32_t claims, uint32_t capacity) {
     const uint64_t c =
         __hip_atomic_fetch_add(sv.claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -285,7 +288,7 @@ __device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t n
         __hip_atomic_store(sv.claim, static_cast<uint64_t>(epoch + 1u) << 32, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t slot = epoch & (kMaxTiles - 1u);
-        if (slot >= num_tiles && slot < capacity)
+        if (slot >= words_used && slot < capacity)
             __hip_atomic_store(sv.desc + slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return c;
@@ -298,7 +301,7 @@ __device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t n
 // slow look-back never delays the successors. (If this store ever lands after
 // the control wavefront's later {inclusive} store, successors just walk one
 // tile further: both are valid states.)
-template <class Op>
+template <class Op, bool WIDE>
 __device__ __forceinline__ void arrive_and_publish(uint32_t *s_arrive, const uint32_t *s_tot,
                                                    uint32_t *s_pre, uint64_t *desc, uint32_t tile,
                                                    uint32_t tag, int lane) {
@@ -308,9 +311,14 @@ __device__ __forceinline__ void arrive_and_publish(uint32_t *s_arrive, const uin
                                         __HIP_MEMORY_SCOPE_WORKGROUP);
     if (uniform(before) == kDataWaves - 1) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        const uint32_t agg = Op::bits(scan_chunk_totals<Op>(s_tot, s_pre, lane));
-        if (lane == 0)
-            publish(desc + tile, tag, tile == 0 ? kStatusInclusive : kStatusAggregate, agg);
+        const typename Op::T agg = scan_chunk_totals<Op>(s_tot, s_pre, lane);
+        const uint32_t st = tile == 0 ? kStatusInclusive : kStatusAggregate;
+        if (lane == 0) {
+            if constexpr (WIDE)
+                publish_wide(desc, tile, tag, st, static_cast<double>(agg));
+            else
+                publish(desc + tile, tag, st, Op::bits(agg));
+        }
     }
 }
 
@@ -708,7 +716,13 @@ constexpr int kScanPollSleep = 127;  // look-back poll interval, s_sleep units (
 // the sum of the values. Per load j a lane sums its 4 values, a DPP wavefront
 // scan gives the lane offsets, and results leave with the same 128-bit layout
 // they were read with. in == out is allowed.
-template <class Op, bool VEC, bool INCL>
+//
+// WIDE (fp32 only): carries between tiles travel in fp64 (wide descriptors,
+// fp64 look-back), and each output is rounded to fp32 once, from
+// base + chunk prefix + the value's prefix inside its chunk, all added in
+// fp64. Only the prefix inside a tile (at most 30720 values) is summed in
+// fp32, so the error no longer grows with the number of tiles before.
+template <class Op, bool VEC, bool INCL, bool WIDE>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))) void scan_kernel(const typename Op::T *in,
                                                         typename Op::T *out, int64_t n,
                                                         void *scratch, uint32_t num_tiles,
@@ -717,10 +731,13 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
     __shared__ uint32_t s_tot[kChunksPerTile];
     __shared__ uint32_t s_pre[kChunksPerTile + 1];
     __shared__ uint32_t s_tile, s_tag, s_base, s_arrive;
+    __shared__ double s_base64;
+    static_assert(!WIDE || sizeof(typename Op::T) == 4, "wide carries are for fp32 values");
 
     const ScratchView sv = view(scratch);
     if (threadIdx.x == 0) {
-        const uint64_t c = claim_tile(sv, num_tiles, num_tiles, capacity);
+        // the stale-slot sweep must spare every descriptor word this call uses
+        const uint64_t c = claim_tile(sv, WIDE ? 2 * num_tiles : num_tiles, num_tiles, capacity);
         s_tile = static_cast<uint32_t>(c);
         s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
         s_arrive = 0;
@@ -734,18 +751,33 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
     const int64_t tile_start = static_cast<int64_t>(tile) * kTile;
 
     if (w == kCtrlWave) {
-        T prefix = Op::zero();
-        if (tile != 0) prefix = look_back<Op, kScanPollSleep>(sv.desc, tile, tag, sv.timed_out);
-        if (lane == 0) s_base = Op::bits(prefix);
-        __syncthreads();  // B1
-        T chunk_before[kLbRounds];
-        T round_before[kLbRounds + 1];
-        tile_prefixes<Op>(s_pre, 0, chunk_before, round_before);
-        const T agg = round_before[kLbRounds];
-        if (lane == 0) {
-            if (tile != 0)
-                publish(sv.desc + tile, tag, kStatusInclusive, Op::bits(Op::add(prefix, agg)));
-            if (total != nullptr && tile == num_tiles - 1) *total = Op::add(prefix, agg);
+        if constexpr (WIDE) {
+            double prefix = 0.0;
+            if (tile != 0) prefix = look_back_wide<kScanPollSleep>(sv.desc, tile, tag, sv.timed_out);
+            if (lane == 0) s_base64 = prefix;
+            __syncthreads();  // B1
+            T chunk_before[kLbRounds];
+            T round_before[kLbRounds + 1];
+            tile_prefixes<Op>(s_pre, 0, chunk_before, round_before);
+            const double incl = prefix + static_cast<double>(round_before[kLbRounds]);
+            if (lane == 0) {
+                if (tile != 0) publish_wide(sv.desc, tile, tag, kStatusInclusive, incl);
+                if (total != nullptr && tile == num_tiles - 1) *total = static_cast<T>(incl);
+            }
+        } else {
+            T prefix = Op::zero();
+            if (tile != 0) prefix = look_back<Op, kScanPollSleep>(sv.desc, tile, tag, sv.timed_out);
+            if (lane == 0) s_base = Op::bits(prefix);
+            __syncthreads();  // B1
+            T chunk_before[kLbRounds];
+            T round_before[kLbRounds + 1];
+            tile_prefixes<Op>(s_pre, 0, chunk_before, round_before);
+            const T agg = round_before[kLbRounds];
+            if (lane == 0) {
+                if (tile != 0)
+                    publish(sv.desc + tile, tag, kStatusInclusive, Op::bits(Op::add(prefix, agg)));
+                if (total != nullptr && tile == num_tiles - 1) *total = Op::add(prefix, agg);
+            }
         }
         return;
     }
@@ -786,19 +818,29 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
         }
         if (lane == 0) s_tot[q * kDataWaves + w] = Op::bits(running);
     }
-    arrive_and_publish<Op>(&s_arrive, s_tot, s_pre, sv.desc, tile, tag, lane);
+    arrive_and_publish<Op, WIDE>(&s_arrive, s_tot, s_pre, sv.desc, tile, tag, lane);
     __syncthreads();  // B1
-    const T base = Op::from_bits(uniform(s_base));
     T chunk_before[kLbRounds];
     T round_before[kLbRounds + 1];
     tile_prefixes<Op>(s_pre, w, chunk_before, round_before);
+    const T base = Op::from_bits(uniform(s_base));
+    const double base64 = WIDE ? s_base64 : 0.0;
 #pragma unroll
     for (int q = 0; q < kLbRounds; ++q) {
-        const T chunk_base = Op::add(base, chunk_before[q]);
+        if constexpr (WIDE) {
+            const double chunk_base = base64 + static_cast<double>(chunk_before[q]);
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j)
+            for (int j = 0; j < kLoads; ++j)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[q][j][k] = Op::add(chunk_base, v[q][j][k]);
+                for (int k = 0; k < 4; ++k)
+                    v[q][j][k] = static_cast<T>(chunk_base + static_cast<double>(v[q][j][k]));
+        } else {
+            const T chunk_base = Op::add(base, chunk_before[q]);
+#pragma unroll
+            for (int j = 0; j < kLoads; ++j)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[q][j][k] = Op::add(chunk_base, v[q][j][k]);
+        }
         const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
         store_chunk<VEC>(out, chunk, lane, chunk_rem(n, chunk), v[q]);
     }
@@ -1245,9 +1287,11 @@ int check_n(int64_t n) {
     return SSC_OK;
 }
 
+// Header plus two 64-bit descriptor words per tile (the fp32 scans' wide
+// descriptors; the other kernels use the first half of the array).
 size_t scratch_need(int64_t n) {
     const int64_t t = n > 0 ? tiles_for(n) : 0;
-    return kHeaderBytes + static_cast<size_t>(t) * sizeof(uint64_t);
+    return kHeaderBytes + static_cast<size_t>(t) * 2 * sizeof(uint64_t);
 }
 
 int check_scratch(const void *scratch, size_t bytes, size_t need) {
@@ -1369,11 +1413,12 @@ int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename
     if (n == 0) return total ? clear_words(total, 1, s) : SSC_OK;
     const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
     const uint32_t cap = capacity_of(scratch_bytes);
+    constexpr bool kWide = sizeof(T) == 4 && !std::is_integral<T>::value;  // fp32: fp64 carries
     if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL((scan_kernel<Op, true, INCL>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
+        hipLaunchKernelGGL((scan_kernel<Op, true, INCL, kWide>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
                            scratch, tiles, cap, total);
     else
-        hipLaunchKernelGGL((scan_kernel<Op, false, INCL>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
+        hipLaunchKernelGGL((scan_kernel<Op, false, INCL, kWide>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
                            scratch, tiles, cap, total);
     return launched();
 }

@@ -275,4 +275,97 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
     }
 }
 
+// ------------------------------------------------- wide (fp64) descriptors ---
+// For fp32 scans with fp64 carries a tile's descriptor is two 64-bit words,
+// each laid out as a narrow descriptor ((tag << 2) | status in the high
+// half) holding one half of the double's bits in its low half: word 0 the
+// high 32 bits, word 1 the low 32 bits. The two halves are separate atomic
+// stores, so a reader takes a descriptor as published only when both
+// halves carry this call's tag and the same status; a pair torn between a
+// tile's {aggregate} and {inclusive} stores reads as unpublished and is
+// polled again.
+__device__ __forceinline__ void publish_wide(uint64_t *desc, uint32_t tile, uint32_t tag,
+                                             uint32_t status, double value) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(value));
+    __hip_atomic_store(desc + 2 * static_cast<uint64_t>(tile),
+                       descriptor(tag, status, static_cast<uint32_t>(b >> 32)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(desc + 2 * static_cast<uint64_t>(tile) + 1,
+                       descriptor(tag, status, static_cast<uint32_t>(b)), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Status and value of tile idx's wide descriptor; tiles below 0 read as
+// inclusive with value 0.
+__device__ __forceinline__ uint32_t peek_wide(uint64_t *desc, int32_t idx, uint32_t tag,
+                                              double &value) {
+    const uint32_t off = static_cast<uint32_t>(idx < 0 ? 0 : idx) * 16u;
+    uint64_t *p = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(desc) + off);
+    const uint64_t hi = peek(p);
+    const uint64_t lo = peek(p + 1);
+    if (idx < 0) {
+        value = 0.0;
+        return kStatusInclusive;
+    }
+    const uint32_t sh = status_of(hi, tag), sl = status_of(lo, tag);
+    value = __longlong_as_double(static_cast<long long>((hi << 32) | (lo & 0xFFFFFFFFull)));
+    return sh == sl ? sh : 0u;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// The look-back of `look_back` over wide descriptors: the same waiting,
+// windows, stopping rule and time-out, summing the values in fp64. Returns
+// the exclusive prefix of `tile` in every lane.
+template <int SLEEP>
+__device__ double look_back_wide(uint64_t *desc, uint32_t tile, uint32_t tag,
+                                 uint32_t *timed_out) {
+    const int lane = lane_id();
+    double prefix = 0.0;
+    uint32_t spins = 0;
+    while (true) {
+        uint32_t st = 0;
+        if (lane == 0) {
+            double unused;
+            st = peek_wide(desc, static_cast<int32_t>(tile) - 1, tag, unused);
+        }
+        if (uniform(st) != 0u) break;
+        if (++spins > kSpinLimit) {
+            if (lane == 0)
+                __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return prefix;
+        }
+        poll_pause<SLEEP>();
+    }
+    int32_t end = static_cast<int32_t>(tile);
+    while (true) {
+        double val = 0.0;
+        int top = -1;  // lane of the nearest inclusive tile
+        while (true) {
+            const uint32_t st = peek_wide(desc, end - kWave + lane, tag, val);
+            const uint64_t unpublished = ballot(st == 0u);
+            const uint64_t inclusive = ballot(st == kStatusInclusive);
+            const int ti = inclusive ? 63 - __builtin_clzll(inclusive) : -1;
+            const int tx = unpublished ? 63 - __builtin_clzll(unpublished) : -1;
+            if (tx <= ti) {
+                top = ti;
+                break;
+            }
+            if (++spins > kSpinLimit) {
+                if (lane == 0)
+                    __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return prefix;
+            }
+            poll_pause<SLEEP>();
+        }
+        prefix += wave_sum_f64(lane >= top ? val : 0.0);
+        if (top >= 0) return prefix;
+        end -= kWave;
+    }
+}
+
 }  // namespace ssc

@@ -67,21 +67,23 @@ def test_enum_numbering_agrees_with_oracle_and_binding():
 def test_tile_and_scratch_sizes():
     L = ssc.lib()
     T = L.ssc_tile_elems()
-    assert T == 30720          # 2 rounds x 15 data wavefronts x 1024 elements
+    assert T == 30720          # 15 data wavefronts x 2048 elements (2 rounds of 1024 in a scan)
+    # a 512-byte header, then two 8-byte descriptor words per tile (the fp32
+    # scans' descriptors are two words wide)
     for n in (0, 1, T - 1, T, T + 1, 2**28, INT32_MAX):
         tiles = (n + T - 1) // T
-        assert L.ssc_scratch_bytes(n) == 512 + 8 * tiles
-        assert L.ssc_radix_sort_scratch_bytes(n) == 512 + 8 * tiles
-    assert L.ssc_scratch_bytes(INT32_MAX) == 512 + 8 * 69906
+        assert L.ssc_scratch_bytes(n) == 512 + 16 * tiles
+        assert L.ssc_radix_sort_scratch_bytes(n) == 512 + 16 * tiles
+    assert L.ssc_scratch_bytes(INT32_MAX) == 512 + 16 * 69906
     assert L.ssc_scratch_bytes(-5) == 512
     # 4-bit radix sort: a scan scratch (256-byte rounded) for the 16 x tiles
     # count table, then the table
     for n in (1, 8191, 8192, 8193, 2**24, INT32_MAX):
         rt = (n + 8191) // 8192
-        scan = 512 + 8 * ((16 * rt + T - 1) // T)
+        scan = 512 + 16 * ((16 * rt + T - 1) // T)
         assert L.ssc_radix_sort4_scratch_bytes(n) == (scan + 255) // 256 * 256 + 64 * rt
     assert L.ssc_radix_sort4_scratch_bytes(0) == 512
-    assert L.ssc_radix_sort4_scratch_bytes(INT32_MAX) == 1792 + 64 * 262144
+    assert L.ssc_radix_sort4_scratch_bytes(INT32_MAX) == 2816 + 64 * 262144
 
 
 def test_status_strings():
@@ -120,7 +122,7 @@ def test_compact_argument_errors():
     assert _compact(scratch=None) == SCRATCH
     assert _compact(scratch=S + 4) == SCRATCH  # not 8-byte aligned
     assert _compact(sbytes=511) == SCRATCH
-    assert _compact(n=40000, sbytes=512 + 8) == SCRATCH  # needs two descriptors
+    assert _compact(n=40000, sbytes=512 + 16) == SCRATCH  # needs two tiles' descriptors
     assert _compact(scratch=A) == ALIAS
 
 
