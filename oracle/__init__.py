@@ -23,6 +23,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 # Predicate numbering as the oracle defines it (checked against the C ABI).
 PRED_NONZERO, PRED_ODD, PRED_EVEN, PRED_BIT_SET, PRED_BIT_CLEAR, PRED_MOD_LT = range(6)
+PRED_F32_NONZERO, PRED_F32_GT, PRED_F32_LT, PRED_F32_IN = range(6, 10)
 
 _lib = None
 
@@ -68,6 +69,15 @@ def lib() -> ctypes.CDLL:
         L.orc_inclusive_scan_f32.restype = None
         L.orc_select_index_i32.argtypes = [i32p, i32p, i64, c_int, i32, i32]
         L.orc_select_index_i32.restype = i64
+        f32 = ctypes.c_float
+        L.orc_pred_f32.argtypes = [f32, c_int, f32, f32]
+        L.orc_pred_f32.restype = c_int
+        L.orc_compact_f32.argtypes = [f32p, f32p, i64, c_int, f32, f32]
+        L.orc_compact_f32.restype = i64
+        L.orc_partition_f32.argtypes = [f32p, f32p, i64, c_int, f32, f32]
+        L.orc_partition_f32.restype = i64
+        L.orc_select_index_f32.argtypes = [f32p, i32p, i64, c_int, f32, f32]
+        L.orc_select_index_f32.restype = i64
         L.orc_count.argtypes = [i32p, i64, c_int, i32, i32]
         L.orc_count.restype = i64
         L.orc_compact_i32.argtypes = [i32p, i32p, i64, c_int, i32, i32, i32p]
@@ -150,6 +160,40 @@ def select_index_i32(x, pred: int, pa: int = 0, pb: int = 0):
     idx = np.empty(x.size, np.int32)
     m = lib().orc_select_index_i32(_ptr(x, ctypes.c_int32), _ptr(idx, ctypes.c_int32), x.size,
                                    pred, pa, pb)
+    return idx[:m].copy(), int(m)
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def pred_f32(x: float, pred: int, a: float = 0.0, b: float = 0.0) -> int:
+    """P(x) for one fp32 value."""
+    return int(lib().orc_pred_f32(float(np.float32(x)), pred, a, b))
+
+
+def compact_f32(x, pred: int, a: float = 0.0, b: float = 0.0):
+    """(survivors, count) of fp32 values in input order."""
+    x = _f32(x)
+    out = np.empty(x.size, np.float32)
+    m = lib().orc_compact_f32(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_float), x.size, pred, a, b)
+    return out[:m].copy(), int(m)
+
+
+def partition_f32(x, pred: int, a: float = 0.0, b: float = 0.0):
+    """(out, kept): predicate-true fp32 values first, both halves in input order."""
+    x = _f32(x)
+    out = np.empty(x.size, np.float32)
+    k = lib().orc_partition_f32(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_float), x.size, pred, a, b)
+    return out, int(k)
+
+
+def select_index_f32(x, pred: int, a: float = 0.0, b: float = 0.0):
+    """(indices, count) of the fp32 values for which the predicate holds."""
+    x = _f32(x)
+    idx = np.empty(x.size, np.int32)
+    m = lib().orc_select_index_f32(_ptr(x, ctypes.c_float), _ptr(idx, ctypes.c_int32), x.size,
+                                   pred, a, b)
     return idx[:m].copy(), int(m)
 
 

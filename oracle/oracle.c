@@ -35,6 +35,10 @@
  *   - The radix sort is 32 stable partitions, bit 0 first, keys whose bit is
  *     clear first, which leaves the keys ascending as unsigned integers.
  *   - n == 0 gives a count / total of 0.
+ *   - fp32 arrays ("CUDA Handbook ch. 13": the compaction kernel is a
+ *     template over the element type) take comparison predicates with IEEE
+ *     semantics: NaN compares false (so NaN is nonzero but never above,
+ *     below or inside a range) and -0.0 equals 0.0.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -50,6 +54,14 @@ enum {
     ORC_PRED_MOD_LT = 5     /* mod(x, pa) < pb, pa >= 1    */
 };
 
+/* Predicates on fp32 elements (comparison semantics of IEEE 754). */
+enum {
+    ORC_PRED_F32_NONZERO = 6, /* x != 0                       */
+    ORC_PRED_F32_GT = 7,      /* x > a                        */
+    ORC_PRED_F32_LT = 8,      /* x < a                        */
+    ORC_PRED_F32_IN = 9       /* a <= x && x < b              */
+};
+
 int orc_pred_id(int which) {
     switch (which) {
     case 0: return ORC_PRED_NONZERO;
@@ -58,6 +70,10 @@ int orc_pred_id(int which) {
     case 3: return ORC_PRED_BIT_SET;
     case 4: return ORC_PRED_BIT_CLEAR;
     case 5: return ORC_PRED_MOD_LT;
+    case 6: return ORC_PRED_F32_NONZERO;
+    case 7: return ORC_PRED_F32_GT;
+    case 8: return ORC_PRED_F32_LT;
+    case 9: return ORC_PRED_F32_IN;
     default: return -1;
     }
 }
@@ -100,6 +116,61 @@ int orc_pred(int32_t x, int pred, int32_t pa, int32_t pb) {
     case ORC_PRED_MOD_LT: return euclid_mod(x, pa) < (int64_t)pb;
     default: return 0;
     }
+}
+
+/* The fp32 predicate, element by element. Returns 0 or 1. */
+int orc_pred_f32(float x, int pred, float a, float b) {
+    switch (pred) {
+    case ORC_PRED_F32_NONZERO: return x != 0.0f;
+    case ORC_PRED_F32_GT: return x > a;
+    case ORC_PRED_F32_LT: return x < a;
+    case ORC_PRED_F32_IN: return a <= x && x < b;
+    default: return 0;
+    }
+}
+
+/* Order-preserving compaction of fp32 values (as orc_compact_i32). */
+int64_t orc_compact_f32(const float *in, float *out, int64_t n, int pred, float a, float b) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred_f32(in[i], pred, a, b)) {
+            out[m] = in[i];
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* Stable partition of fp32 values (as orc_partition_i32). */
+int64_t orc_partition_f32(const float *in, float *out, int64_t n, int pred, float a, float b) {
+    int64_t kept = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred_f32(in[i], pred, a, b)) {
+            out[kept] = in[i];
+            ++kept;
+        }
+    }
+    int64_t pos = kept;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!orc_pred_f32(in[i], pred, a, b)) {
+            out[pos] = in[i];
+            ++pos;
+        }
+    }
+    return kept;
+}
+
+/* Positions of the fp32 elements for which the predicate holds. */
+int64_t orc_select_index_f32(const float *in, int32_t *idx, int64_t n, int pred, float a,
+                             float b) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred_f32(in[i], pred, a, b)) {
+            idx[m] = (int32_t)i;
+            ++m;
+        }
+    }
+    return m;
 }
 
 /* flags[i] = P(in[i]). */

@@ -115,6 +115,51 @@ def test_predicate_hand_cases(golden_dir):
     assert rows >= 40
 
 
+F32_PRED_NAMES = {"F32_NONZERO": oracle.PRED_F32_NONZERO, "F32_GT": oracle.PRED_F32_GT,
+                  "F32_LT": oracle.PRED_F32_LT, "F32_IN": oracle.PRED_F32_IN}
+
+
+def test_predicate_f32_hand_cases(golden_dir):
+    rows = 0
+    with open(os.path.join(golden_dir, "predicate_cases_f32.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            xs, name, a, b, want = line.split()
+            got = oracle.pred_f32(float(xs), F32_PRED_NAMES[name], float(a), float(b))
+            assert got == int(want), line
+            rows += 1
+    assert rows >= 30
+
+
+def test_f32_ops_against_numpy_masks():
+    """Compaction, partition and selection of fp32 values against numpy boolean
+    masks (IEEE comparisons), on values that include NaN, +-0, +-inf and
+    denormals."""
+    from scan_stream_compaction_amd import workloads
+    x = (workloads.unit_float32(11, 40_000) * 4 - 2).astype(np.float32)
+    x[:10] = [np.nan, 0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 0.5, 1.0, -1.0]
+    x[-3:] = [np.nan, 0.5, -0.0]
+    cases = [(oracle.PRED_F32_NONZERO, 0.0, 0.0, x != 0),
+             (oracle.PRED_F32_GT, 0.5, 0.0, x > np.float32(0.5)),
+             (oracle.PRED_F32_LT, -0.25, 0.0, x < np.float32(-0.25)),
+             (oracle.PRED_F32_IN, 0.0, 1.0, (x >= 0) & (x < 1)),
+             (oracle.PRED_F32_GT, np.nan, 0.0, np.zeros(x.size, bool))]
+    with np.errstate(invalid="ignore"):
+        for pred, a, b, mask in cases:
+            surv, m = oracle.compact_f32(x, pred, a, b)
+            assert m == int(mask.sum())
+            assert np.array_equal(surv, x[mask], equal_nan=True)
+            assert np.array_equal(surv.view(np.uint32), x[mask].view(np.uint32))  # -0.0 kept as is
+            out, k = oracle.partition_f32(x, pred, a, b)
+            assert k == m
+            assert np.array_equal(out.view(np.uint32),
+                                  np.concatenate([x[mask], x[~mask]]).view(np.uint32))
+            idx, mi = oracle.select_index_f32(x, pred, a, b)
+            assert mi == m and np.array_equal(idx, np.flatnonzero(mask))
+
+
 def test_predicate_arg_rules():
     assert oracle.pred_args_ok(oracle.PRED_BIT_SET, 31)
     assert not oracle.pred_args_ok(oracle.PRED_BIT_SET, 32)
