@@ -69,14 +69,26 @@ typedef enum ssc_status {
  *   BIT_SET    bit pa of x is 1    0 <= pa <= 31 (one split of an LSD radix sort,
  *   BIT_CLEAR  bit pa of x is 0      "CIS 565 Project 2: Stream Compaction")
  *   MOD_LT     r < pb where r is the non-negative residue of x modulo pa, pa >= 1
- * Bit tests use the two's-complement bits, so -3 is odd. */
+ * Bit tests use the two's-complement bits, so -3 is odd.
+ * For fp32 arrays (the *_f32 calls; the compaction kernel of "CUDA Handbook
+ * ch. 13" is a template over the element type), with thresholds a, b and
+ * IEEE comparisons (every comparison with NaN is false, -0.0 == 0.0):
+ *   F32_NONZERO  x != 0          (NaN is nonzero, -0.0 is zero)
+ *   F32_GT       x > a
+ *   F32_LT       x < a
+ *   F32_IN       a <= x && x < b
+ * The int32 calls take predicates 0..5 only and the fp32 calls 6..9. */
 typedef enum ssc_pred {
     SSC_PRED_NONZERO = 0,
     SSC_PRED_ODD = 1,
     SSC_PRED_EVEN = 2,
     SSC_PRED_BIT_SET = 3,
     SSC_PRED_BIT_CLEAR = 4,
-    SSC_PRED_MOD_LT = 5
+    SSC_PRED_MOD_LT = 5,
+    SSC_PRED_F32_NONZERO = 6,
+    SSC_PRED_F32_GT = 7,
+    SSC_PRED_F32_LT = 8,
+    SSC_PRED_F32_IN = 9
 } ssc_pred;
 
 /* Elements per tile: the share of the single pass behind one tile number
@@ -144,6 +156,12 @@ int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_
                     int32_t pb, int32_t *count, int32_t *ranks, void *scratch,
                     size_t scratch_bytes, void *stream);
 
+/* ssc_compact_i32 for fp32 arrays with an fp32 predicate (6..9) and its
+ * thresholds a, b; values move bit for bit (-0.0 and NaN payloads kept). */
+int ssc_compact_f32(const float *in, float *out, int64_t n, int pred, float a, float b,
+                    int32_t *count, int32_t *ranks, void *scratch, size_t scratch_bytes,
+                    void *stream);
+
 /* Selection (the index form of compaction): idx[0 .. count) = the
  * positions i, increasing, of the elements with P(in[i]) true; *count =
  * their number. idx[count .. n) is not written. Same single pass as
@@ -155,6 +173,10 @@ int ssc_select_index_i32(const int32_t *in, int32_t *idx, int64_t n, int pred, i
                          int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
                          void *stream);
 
+/* ssc_select_index_i32 for fp32 arrays with an fp32 predicate (6..9). */
+int ssc_select_index_f32(const float *in, int32_t *idx, int64_t n, int pred, float a, float b,
+                         int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
+
 /* Stable partition: out[0 .. K) = the elements with P true, out[K .. n) =
  * the elements with P false, both in input order; *count = K. Kept x[i]
  * goes to out[rank[i]], rejected x[i] to out[K + i - rank[i]], where rank
@@ -165,6 +187,10 @@ int ssc_select_index_i32(const int32_t *in, int32_t *idx, int64_t n, int pred, i
 int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
                       int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
                       void *stream);
+
+/* ssc_partition_i32 for fp32 arrays with an fp32 predicate (6..9). */
+int ssc_partition_f32(const float *in, float *out, int64_t n, int pred, float a, float b,
+                      int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
 
 /* *count = number of elements with P true (a reduction of the flags; one
  * launch). Needs a scratch buffer of at least ssc_scratch_bytes(0) bytes. */

@@ -19,7 +19,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssc.so")
 
-PRED = {"nonzero": 0, "odd": 1, "even": 2, "bit_set": 3, "bit_clear": 4, "mod_lt": 5}
+PRED = {"nonzero": 0, "odd": 1, "even": 2, "bit_set": 3, "bit_clear": 4, "mod_lt": 5,
+        "f32_nonzero": 6, "f32_gt": 7, "f32_lt": 8, "f32_in": 9}
 STATUS = {0: "SSC_OK", 1: "SSC_ERR_ARG", 2: "SSC_ERR_SIZE", 3: "SSC_ERR_ALIAS",
           4: "SSC_ERR_SCRATCH", 5: "SSC_ERR_HIP", 6: "SSC_ERR_DEVICE"}
 
@@ -29,6 +30,7 @@ _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _INT = ctypes.c_int
 _SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
 SIGNATURES = {
     "ssc_tile_elems": (_I64, []),
     "ssc_scratch_bytes": (_SZ, [_I64]),
@@ -39,6 +41,9 @@ SIGNATURES = {
     "ssc_inclusive_scan_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_inclusive_scan_f32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_select_index_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
+    "ssc_compact_f32": (_INT, [_P, _P, _I64, _INT, _F32, _F32, _P, _P, _P, _SZ, _P]),
+    "ssc_select_index_f32": (_INT, [_P, _P, _I64, _INT, _F32, _F32, _P, _P, _SZ, _P]),
+    "ssc_partition_f32": (_INT, [_P, _P, _I64, _INT, _F32, _F32, _P, _P, _SZ, _P]),
     "ssc_compact_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "ssc_partition_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
     "ssc_count_if_i32": (_INT, [_P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
@@ -119,6 +124,15 @@ def prepared(op, *args, **kwargs):
     return run
 
 
+def _typed(x: torch.Tensor, op: str) -> str:
+    """The library entry point of `op` for x's element type."""
+    if x.dtype == torch.int32:
+        return f"ssc_{op}_i32"
+    if x.dtype == torch.float32:
+        return f"ssc_{op}_f32"
+    raise TypeError(f"{op} takes int32 or float32")
+
+
 def _pred(p) -> int:
     return PRED[p] if isinstance(p, str) else int(p)
 
@@ -190,14 +204,15 @@ def _scan(x, out, total, scratch, form):
 def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
             out: torch.Tensor | None = None, count: torch.Tensor | None = None,
             ranks=False, scratch: torch.Tensor | None = None):
-    """(out, count[, ranks]): order-preserving compaction of int32 values.
+    """(out, count[, ranks]): order-preserving compaction of int32 values
+    (predicates 0..5, int arguments pa, pb) or float32 values (predicates
+    "f32_*", float thresholds pa, pb).
 
     out[:count] holds the survivors; entries past count are not written.
     ranks=True (or a tensor) also returns the exclusive scan of the flags.
     """
     _dev(x)
-    if x.dtype != torch.int32:
-        raise TypeError("compact takes int32")
+    fn = _typed(x, "compact")
     n = x.numel()
     if out is None:
         out = torch.empty_like(x)
@@ -205,12 +220,12 @@ def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     rk = None
     if ranks is True:
-        rk = torch.empty_like(x)
+        rk = torch.empty(n, dtype=torch.int32, device=x.device)
     elif isinstance(ranks, torch.Tensor):
         rk = ranks
     if scratch is None:
         scratch = new_scratch(n, x.device)
-    _call("ssc_compact_i32", lib().ssc_compact_i32,
+    _call(fn, getattr(lib(), fn),
           x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), _ptr(rk),
           scratch.data_ptr(), scratch.numel(), _stream(x))
     return (out, count, rk) if rk is not None else (out, count)
@@ -222,8 +237,7 @@ def select_index(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
     """(idx, count): idx[:count] holds the positions of the elements for which
     the predicate holds, increasing; entries past count are not written."""
     _dev(x)
-    if x.dtype != torch.int32:
-        raise TypeError("select_index takes int32")
+    fn = _typed(x, "select_index")
     n = x.numel()
     if out is None:
         out = torch.empty(n, dtype=torch.int32, device=x.device)
@@ -231,7 +245,7 @@ def select_index(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     if scratch is None:
         scratch = new_scratch(n, x.device)
-    _call("ssc_select_index_i32", lib().ssc_select_index_i32,
+    _call(fn, getattr(lib(), fn),
           x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
           scratch.data_ptr(), scratch.numel(), _stream(x))
     return out, count
@@ -242,8 +256,7 @@ def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,
               scratch: torch.Tensor | None = None):
     """(out, count): stable partition, predicate-true elements first; count = K."""
     _dev(x)
-    if x.dtype != torch.int32:
-        raise TypeError("partition takes int32")
+    fn = _typed(x, "partition")
     n = x.numel()
     if out is None:
         out = torch.empty_like(x)
@@ -251,7 +264,7 @@ def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     if scratch is None:
         scratch = new_scratch(n, x.device)
-    _call("ssc_partition_i32", lib().ssc_partition_i32,
+    _call(fn, getattr(lib(), fn),
           x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
           scratch.data_ptr(), scratch.numel(), _stream(x))
     return out, count

@@ -1265,6 +1265,18 @@ int check_pred(int pred, int32_t pa, int32_t pb) {
     }
 }
 
+// fp32 predicates take any thresholds (NaN included: every comparison with
+// it is false).
+int check_pred_f32(int pred) {
+    return pred >= SSC_PRED_F32_NONZERO && pred <= SSC_PRED_F32_IN ? SSC_OK : SSC_ERR_ARG;
+}
+
+int32_t f32_bits(float f) {
+    int32_t b;
+    memcpy(&b, &f, 4);
+    return b;
+}
+
 // Arguments of a predicate as the kernels take them (see PredArgs); for
 // MOD_LT the constants of division by the invariant modulus a >= 1.
 PredArgs make_pred_args(int pred, int32_t pa, int32_t pb) {
@@ -1327,15 +1339,26 @@ uint32_t reduce_grid(int64_t n) {
 }
 
 // ---- template dispatch on the predicate and the load width ----
-template <template <int, bool> class F, class... A>
+// Predicates 0..5 act on int32 elements, 6..9 on fp32 ones; F32 says which
+// family the (already validated) predicate belongs to.
+template <template <int, bool> class F, bool F32 = false, class... A>
 int dispatch_pred(int pred, bool vec, A... a) {
-    switch (pred) {
-    case 0: return vec ? F<0, true>::run(a...) : F<0, false>::run(a...);
-    case 1: return vec ? F<1, true>::run(a...) : F<1, false>::run(a...);
-    case 2: return vec ? F<2, true>::run(a...) : F<2, false>::run(a...);
-    case 3: return vec ? F<3, true>::run(a...) : F<3, false>::run(a...);
-    case 4: return vec ? F<4, true>::run(a...) : F<4, false>::run(a...);
-    default: return vec ? F<5, true>::run(a...) : F<5, false>::run(a...);
+    if constexpr (F32) {
+        switch (pred) {
+        case SSC_PRED_F32_NONZERO: return vec ? F<6, true>::run(a...) : F<6, false>::run(a...);
+        case SSC_PRED_F32_GT: return vec ? F<7, true>::run(a...) : F<7, false>::run(a...);
+        case SSC_PRED_F32_LT: return vec ? F<8, true>::run(a...) : F<8, false>::run(a...);
+        default: return vec ? F<9, true>::run(a...) : F<9, false>::run(a...);
+        }
+    } else {
+        switch (pred) {
+        case 0: return vec ? F<0, true>::run(a...) : F<0, false>::run(a...);
+        case 1: return vec ? F<1, true>::run(a...) : F<1, false>::run(a...);
+        case 2: return vec ? F<2, true>::run(a...) : F<2, false>::run(a...);
+        case 3: return vec ? F<3, true>::run(a...) : F<3, false>::run(a...);
+        case 4: return vec ? F<4, true>::run(a...) : F<4, false>::run(a...);
+        default: return vec ? F<5, true>::run(a...) : F<5, false>::run(a...);
+        }
     }
 }
 
@@ -1435,6 +1458,88 @@ size_t radix4_scratch_need(int64_t n) {
     return radix4_scan_part(n) + static_cast<size_t>(kRadixDigits * radix_tiles_for(n)) * 4;
 }
 
+template <bool F32>
+int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
+                 int32_t *count, int32_t *ranks, void *scratch, size_t scratch_bytes,
+                 void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (count == nullptr || (n > 0 && (in == nullptr || out == nullptr))) return SSC_ERR_ARG;
+    SSC_TRY(F32 ? check_pred_f32(pred) : check_pred(pred, pa, pb));
+    if (!aligned(in, 4) || !aligned(out, 4) || !aligned(count, 4) || (ranks && !aligned(ranks, 4)))
+        return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (overlap(in, bytes, out, bytes) || overlap(count, 4, in, bytes) ||
+        overlap(count, 4, out, bytes) ||
+        (ranks && (overlap(ranks, bytes, in, bytes) || overlap(ranks, bytes, out, bytes) ||
+                   overlap(ranks, bytes, count, 4))))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        overlap(scratch, scratch_bytes, count, 4) ||
+        (ranks && overlap(scratch, scratch_bytes, ranks, bytes)))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
+    return dispatch_pred<LaunchSelect, F32>(pred, vec, ranks ? kCompactRanks : kCompact, in, out, n,
+                                       make_pred_args(pred, pa, pb), scratch,
+                                       capacity_of(scratch_bytes), count, ranks,
+                                       static_cast<const int32_t *>(nullptr), s);
+}
+
+template <bool F32>
+int select_index_impl(const int32_t *in, int32_t *idx, int64_t n, int pred, int32_t pa, int32_t pb,
+                      int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (count == nullptr || (n > 0 && (in == nullptr || idx == nullptr))) return SSC_ERR_ARG;
+    SSC_TRY(F32 ? check_pred_f32(pred) : check_pred(pred, pa, pb));
+    if (!aligned(in, 4) || !aligned(idx, 4) || !aligned(count, 4)) return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (overlap(in, bytes, idx, bytes) || overlap(count, 4, in, bytes) ||
+        overlap(count, 4, idx, bytes))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, idx, bytes) ||
+        overlap(scratch, scratch_bytes, count, 4))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), kSelectIndex, in, idx, n,
+                                       make_pred_args(pred, pa, pb), scratch,
+                                       capacity_of(scratch_bytes), count,
+                                       static_cast<int32_t *>(nullptr),
+                                       static_cast<const int32_t *>(nullptr), s);
+}
+
+template <bool F32>
+int partition_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
+                   int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (count == nullptr || (n > 0 && (in == nullptr || out == nullptr))) return SSC_ERR_ARG;
+    SSC_TRY(F32 ? check_pred_f32(pred) : check_pred(pred, pa, pb));
+    if (!aligned(in, 4) || !aligned(out, 4) || !aligned(count, 4)) return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (overlap(in, bytes, out, bytes) || overlap(count, 4, in, bytes) ||
+        overlap(count, 4, out, bytes))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        overlap(scratch, scratch_bytes, count, 4))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    const bool vec = aligned(in, 16);
+    const PredArgs pr = make_pred_args(pred, pa, pb);
+    SSC_TRY((dispatch_pred<LaunchCount, F32>(pred, vec, in, n, pr, scratch, count, s)));
+    return dispatch_pred<LaunchSelect, F32>(pred, vec, kPartition, in, out, n, pr, scratch,
+                                       capacity_of(scratch_bytes), static_cast<int32_t *>(nullptr),
+                                       static_cast<int32_t *>(nullptr),
+                                       static_cast<const int32_t *>(count), s);
+}
+
 }  // namespace
 
 // ======================================================================
@@ -1486,81 +1591,40 @@ int ssc_inclusive_scan_f32(const float *in, float *out, int64_t n, float *total,
 int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
                     int32_t *count, int32_t *ranks, void *scratch, size_t scratch_bytes,
                     void *stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    SSC_TRY(check_n(n));
-    if (count == nullptr || (n > 0 && (in == nullptr || out == nullptr))) return SSC_ERR_ARG;
-    SSC_TRY(check_pred(pred, pa, pb));
-    if (!aligned(in, 4) || !aligned(out, 4) || !aligned(count, 4) || (ranks && !aligned(ranks, 4)))
-        return SSC_ERR_ARG;
-    const size_t bytes = static_cast<size_t>(n) * 4;
-    if (overlap(in, bytes, out, bytes) || overlap(count, 4, in, bytes) ||
-        overlap(count, 4, out, bytes) ||
-        (ranks && (overlap(ranks, bytes, in, bytes) || overlap(ranks, bytes, out, bytes) ||
-                   overlap(ranks, bytes, count, 4))))
-        return SSC_ERR_ALIAS;
-    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
-    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
-        overlap(scratch, scratch_bytes, count, 4) ||
-        (ranks && overlap(scratch, scratch_bytes, ranks, bytes)))
-        return SSC_ERR_ALIAS;
-    SSC_TRY(check_device());
-    if (n == 0) return clear_words(count, 1, s);
-    const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect>(pred, vec, ranks ? kCompactRanks : kCompact, in, out, n,
-                                       make_pred_args(pred, pa, pb), scratch,
-                                       capacity_of(scratch_bytes), count, ranks,
-                                       static_cast<const int32_t *>(nullptr), s);
+    return compact_impl<false>(in, out, n, pred, pa, pb, count, ranks, scratch, scratch_bytes,
+                               stream);
+}
+
+int ssc_compact_f32(const float *in, float *out, int64_t n, int pred, float a, float b,
+                    int32_t *count, int32_t *ranks, void *scratch, size_t scratch_bytes,
+                    void *stream) {
+    return compact_impl<true>(reinterpret_cast<const int32_t *>(in), reinterpret_cast<int32_t *>(out),
+                              n, pred, f32_bits(a), f32_bits(b), count, ranks, scratch,
+                              scratch_bytes, stream);
 }
 
 int ssc_select_index_i32(const int32_t *in, int32_t *idx, int64_t n, int pred, int32_t pa,
                          int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
                          void *stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    SSC_TRY(check_n(n));
-    if (count == nullptr || (n > 0 && (in == nullptr || idx == nullptr))) return SSC_ERR_ARG;
-    SSC_TRY(check_pred(pred, pa, pb));
-    if (!aligned(in, 4) || !aligned(idx, 4) || !aligned(count, 4)) return SSC_ERR_ARG;
-    const size_t bytes = static_cast<size_t>(n) * 4;
-    if (overlap(in, bytes, idx, bytes) || overlap(count, 4, in, bytes) ||
-        overlap(count, 4, idx, bytes))
-        return SSC_ERR_ALIAS;
-    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
-    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, idx, bytes) ||
-        overlap(scratch, scratch_bytes, count, 4))
-        return SSC_ERR_ALIAS;
-    SSC_TRY(check_device());
-    if (n == 0) return clear_words(count, 1, s);
-    return dispatch_pred<LaunchSelect>(pred, aligned(in, 16), kSelectIndex, in, idx, n,
-                                       make_pred_args(pred, pa, pb), scratch,
-                                       capacity_of(scratch_bytes), count,
-                                       static_cast<int32_t *>(nullptr),
-                                       static_cast<const int32_t *>(nullptr), s);
+    return select_index_impl<false>(in, idx, n, pred, pa, pb, count, scratch, scratch_bytes, stream);
+}
+
+int ssc_select_index_f32(const float *in, int32_t *idx, int64_t n, int pred, float a, float b,
+                         int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    return select_index_impl<true>(reinterpret_cast<const int32_t *>(in), idx, n, pred, f32_bits(a),
+                                   f32_bits(b), count, scratch, scratch_bytes, stream);
 }
 
 int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
                       int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    SSC_TRY(check_n(n));
-    if (count == nullptr || (n > 0 && (in == nullptr || out == nullptr))) return SSC_ERR_ARG;
-    SSC_TRY(check_pred(pred, pa, pb));
-    if (!aligned(in, 4) || !aligned(out, 4) || !aligned(count, 4)) return SSC_ERR_ARG;
-    const size_t bytes = static_cast<size_t>(n) * 4;
-    if (overlap(in, bytes, out, bytes) || overlap(count, 4, in, bytes) ||
-        overlap(count, 4, out, bytes))
-        return SSC_ERR_ALIAS;
-    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
-    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
-        overlap(scratch, scratch_bytes, count, 4))
-        return SSC_ERR_ALIAS;
-    SSC_TRY(check_device());
-    if (n == 0) return clear_words(count, 1, s);
-    const bool vec = aligned(in, 16);
-    const PredArgs pr = make_pred_args(pred, pa, pb);
-    SSC_TRY(dispatch_pred<LaunchCount>(pred, vec, in, n, pr, scratch, count, s));
-    return dispatch_pred<LaunchSelect>(pred, vec, kPartition, in, out, n, pr, scratch,
-                                       capacity_of(scratch_bytes), static_cast<int32_t *>(nullptr),
-                                       static_cast<int32_t *>(nullptr),
-                                       static_cast<const int32_t *>(count), s);
+    return partition_impl<false>(in, out, n, pred, pa, pb, count, scratch, scratch_bytes, stream);
+}
+
+int ssc_partition_f32(const float *in, float *out, int64_t n, int pred, float a, float b,
+                      int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    return partition_impl<true>(reinterpret_cast<const int32_t *>(in),
+                                reinterpret_cast<int32_t *>(out), n, pred, f32_bits(a), f32_bits(b),
+                                count, scratch, scratch_bytes, stream);
 }
 
 int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t pb,

@@ -83,7 +83,9 @@ __device__ __forceinline__ typename Op::T wave_sum(typename Op::T v) {
 // ----------------------------------------------------------- predicates ---
 // Numbering matches ssc_pred in ssc.h. PredArgs carries a predicate's
 // arguments: `a` is the bit of BIT_SET/BIT_CLEAR and the modulus of MOD_LT,
-// `b` the bound of MOD_LT (keep iff mod(x, a) < b, residue in [0, a)).
+// `b` the bound of MOD_LT (keep iff mod(x, a) < b, residue in [0, a)). The
+// F32 predicates (6..9) read the 32-bit element and a, b as fp32 bits and
+// compare with IEEE semantics (NaN compares false, -0.0 == 0.0).
 //
 // The modulus is invariant over a call, so MOD_LT divides by multiplication
 // (Granlund and Montgomery, "Division by Invariant Integers using
@@ -112,7 +114,17 @@ __device__ __forceinline__ bool pred_eval(int32_t x, const PredArgs &pr) {
         return ((u >> pr.a) & 1u) != 0u;
     } else if constexpr (P == 4) {
         return ((u >> pr.a) & 1u) == 0u;
+    } else if constexpr (P == 6) {
+        return __int_as_float(x) != 0.0f;
+    } else if constexpr (P == 7) {
+        return __int_as_float(x) > __int_as_float(pr.a);
+    } else if constexpr (P == 8) {
+        return __int_as_float(x) < __int_as_float(pr.a);
+    } else if constexpr (P == 9) {
+        const float f = __int_as_float(x);
+        return __int_as_float(pr.a) <= f && f < __int_as_float(pr.b);
     } else {
+        static_assert(P == 5, "predicate numbering");
         const uint32_t v = u ^ 0x80000000u;  // x + 2^31
         const uint32_t t = __umulhi(pr.magic, v);
         const uint32_t q = (t + ((v - t) >> pr.sh1)) >> pr.sh2;  // floor(v / a)

@@ -54,12 +54,16 @@ def test_library_exports_every_declared_symbol():
 def test_enum_numbering_agrees_with_oracle_and_binding():
     preds = _enum("ssc_pred")
     assert preds == {"SSC_PRED_NONZERO": 0, "SSC_PRED_ODD": 1, "SSC_PRED_EVEN": 2,
-                     "SSC_PRED_BIT_SET": 3, "SSC_PRED_BIT_CLEAR": 4, "SSC_PRED_MOD_LT": 5}
+                     "SSC_PRED_BIT_SET": 3, "SSC_PRED_BIT_CLEAR": 4, "SSC_PRED_MOD_LT": 5,
+                     "SSC_PRED_F32_NONZERO": 6, "SSC_PRED_F32_GT": 7, "SSC_PRED_F32_LT": 8,
+                     "SSC_PRED_F32_IN": 9}
     for k, v in preds.items():
         assert ssc.PRED[k[len("SSC_PRED_"):].lower()] == v
         assert oracle.lib().orc_pred_id(v) == v
     assert (oracle.PRED_NONZERO, oracle.PRED_ODD, oracle.PRED_EVEN, oracle.PRED_BIT_SET,
             oracle.PRED_BIT_CLEAR, oracle.PRED_MOD_LT) == tuple(range(6))
+    assert (oracle.PRED_F32_NONZERO, oracle.PRED_F32_GT, oracle.PRED_F32_LT,
+            oracle.PRED_F32_IN) == tuple(range(6, 10))
     st = _enum("ssc_status")
     assert {v: k for k, v in st.items()} == ssc.STATUS
 
@@ -180,6 +184,18 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     assert L.ssc_select_index_i32(A, B, -1, 1, 0, 0, C, S, big, None) == ARG
     assert L.ssc_select_index_i32(A, B, 100, 1, 0, 0, C, S, 100, None) == SCRATCH
     assert L.ssc_select_index_i32(A, B, 100, 1, 0, 0, C, B, big, None) == ALIAS
+    # fp32 calls take predicates 6..9 only, int32 calls 0..5 only
+    for p in (0, 5, 10, -1):
+        assert L.ssc_compact_f32(A, B, 100, p, 0.0, 0.0, C, None, S, big, None) == ARG
+        assert L.ssc_partition_f32(A, B, 100, p, 0.0, 0.0, C, S, big, None) == ARG
+        assert L.ssc_select_index_f32(A, B, 100, p, 0.0, 0.0, C, S, big, None) == ARG
+    for p in (6, 9):
+        assert L.ssc_compact_i32(A, B, 100, p, 0, 0, C, None, S, big, None) == ARG
+        assert L.ssc_partition_i32(A, B, 100, p, 0, 0, C, S, big, None) == ARG
+        assert L.ssc_count_if_i32(A, 100, p, 0, 0, C, S, big, None) == ARG
+    assert L.ssc_compact_f32(A, A + 8, 100, 7, 0.5, 0.0, C, None, S, big, None) == ALIAS
+    assert L.ssc_partition_f32(A, B, 100, 9, 0.0, 1.0, None, S, big, None) == ARG
+    assert L.ssc_select_index_f32(A, B, 100, 6, 0.0, 0.0, C, S, 100, None) == SCRATCH
     # copy
     assert L.ssc_copy_i32(A, A + 4, 100, None) == ALIAS
     assert L.ssc_copy_i32(A, B, -1, None) == ARG

@@ -395,6 +395,62 @@ def test_every_predicate_full_range(pred, pa, pb):
     assert checks.same_multiset(host(out)[:m], want)
 
 
+def f32_input(seed: int, n: int) -> np.ndarray:
+    """fp32 values in [-2, 2) with NaN, +-0, +-inf and denormals planted."""
+    x = (wl.unit_float32(seed, n) * 4 - 2).astype(np.float32)
+    special = np.array([np.nan, 0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 0.5, 1.0, -1.0],
+                       np.float32)
+    x[:min(n, special.size)] = special[:min(n, special.size)]
+    if n > 100:
+        x[n // 2: n // 2 + special.size] = special
+        x[-3:] = [np.nan, -0.0, 0.25]
+    return x
+
+
+F32_CASES = [("f32_nonzero", 0.0, 0.0), ("f32_gt", 0.5, 0.0), ("f32_lt", -0.25, 0.0),
+             ("f32_in", 0.0, 1.0), ("f32_gt", float("nan"), 0.0), ("f32_in", -float("inf"), 0.0)]
+
+
+def bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a).view(np.uint32)
+
+
+@pytest.mark.parametrize("pred,a,b", F32_CASES)
+@pytest.mark.parametrize("n", [1, 7, C2 + 3, 3 * T + 611])
+def test_f32_compact_partition_select(pred, a, b, n):
+    """fp32 elements, IEEE predicates: bit-exact against the oracle (values move
+    bit for bit, so -0.0 and NaN come out as they went in)."""
+    x = f32_input(n + 3, n)
+    p = ssc.PRED[pred]
+    xd = dev(x)
+    want, m = oracle.compact_f32(x, p, a, b)
+    out = torch.full_like(xd, float("nan"))
+    _, cnt, rk = ssc.compact(xd, pred, a, b, out=out, ranks=True)
+    assert int(host(cnt)[0]) == m
+    assert checks.first_mismatch(bits(host(out)[:m]), bits(want)) == -1
+    flags = np.array([oracle.pred_f32(float(v), p, a, b) for v in x[:2000]], np.int32)
+    assert checks.first_mismatch(host(rk)[:flags.size], np.cumsum(flags) - flags) == -1
+    pw, k = oracle.partition_f32(x, p, a, b)
+    pout, kc = ssc.partition(xd, pred, a, b)
+    assert int(host(kc)[0]) == k
+    assert checks.first_mismatch(bits(host(pout)), bits(pw)) == -1
+    iw, mi = oracle.select_index_f32(x, p, a, b)
+    idx = torch.full((n,), SENTINEL, dtype=torch.int32, device=DEV)
+    _, ic = ssc.select_index(xd, pred, a, b, out=idx)
+    assert int(host(ic)[0]) == mi
+    o = host(idx)
+    assert checks.first_mismatch(o[:mi], iw) == -1 and np.all(o[mi:] == SENTINEL)
+
+
+def test_f32_compaction_large():
+    """2^26 fp32 values, keep 0 <= x < 1 (about a quarter)."""
+    x = f32_input(99, 1 << 26)
+    want, m = oracle.compact_f32(x, oracle.PRED_F32_IN, 0.0, 1.0)
+    out, cnt = ssc.compact(dev(x), "f32_in", 0.0, 1.0)
+    assert int(host(cnt)[0]) == m
+    assert checks.first_mismatch(bits(host(out)[:m]), bits(want)) == -1
+
+
 def test_keep_all_is_copy_and_keep_none_writes_nothing():
     x = wl.uniform_below(5, 7 * T + 77, 9) + 1
     out, cnt = ssc.compact(dev(x), "nonzero")
