@@ -124,6 +124,38 @@ def cpu_baseline(x_np, target_s: float = 12.0):
     }
 
 
+def pipeline_rows(x, m: int, stream, steps: int, copy_us: float) -> dict:
+    """The pages' "where the time goes" rows on this hardware: the
+    multi-launch compaction (mark, tree scan of the flags, scatter) and its
+    parts against the single pass, each as a multiple of the copy kernel's
+    time. Each result is checked first."""
+    import torch
+
+    import scan_stream_compaction_amd as ssc
+    n = x.numel()
+    out = torch.empty_like(x)
+    ranks = torch.empty_like(x)
+    cnt = torch.zeros(1, dtype=torch.int32, device=x.device)
+    sc = ssc.multipass_scratch(n, x.device)
+    mp = ssc.prepared(ssc.compact_multipass, x, "odd", out=out, count=cnt, ranks=ranks, scratch=sc)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == m and torch.equal(out[:m], torch.masked_select(x, (x & 1).bool()))
+    scan = ssc.prepared(ssc.exclusive_scan_multipass, ranks, out=ranks, scratch=sc)
+    rows = {}
+
+    def row(name, fn, launches):
+        _, ms, _ = timed_calls(fn, steps, stream)
+        rows[name] = {"launches": launches, "us": round(ms * 1e3, 2),
+                      "x_copy": round(ms * 1e3 / copy_us, 3)}
+
+    row("compaction, multi-launch (mark, scan, scatter)", mp, 7)
+    row("scan of 2^28 flags, multi-launch", scan, 5)
+    single = ssc.prepared(ssc.compact, x, "odd", out=out, count=cnt)
+    row("compaction, single pass (this library)", single, 1)
+    rows["copy in to out"] = {"launches": 1, "us": copy_us, "x_copy": 1.0}
+    return rows
+
+
 def other_workloads(dev, steps: int, stream) -> dict:
     """The other workloads of the method, each checked against torch before it
     is timed: per-launch time from HIP events and effective GB/s over the
@@ -192,6 +224,12 @@ def other_workloads(dev, steps: int, stream) -> dict:
           max_rel_err=float(rel.max()))
     xi = torch.from_numpy(wl.mod8_plus1(wl.N_SCAN)).to(dev)
     outi, toti = ssc.inclusive_scan(xi, scratch=sc)
+    outm, totm = ssc.exclusive_scan_multipass(xi)
+    assert torch.equal(outm, excl(xi)) and int(totm.item()) == 45_000_000
+    msc = ssc.multipass_scratch(xi.numel(), dev)
+    timed("scan_i32_1e7_multilaunch", ssc.exclusive_scan_multipass, (xi,),
+          dict(out=outm, total=totm, scratch=msc), 8 * n,
+          note="3 launches: tile scan, scan of the tile sums, add the offsets")
     assert torch.equal(outi, torch.cumsum(xi.to(torch.int64), 0).to(torch.int32))
     timed("inclusive_scan_i32_1e7", ssc.inclusive_scan, (xi,), dict(out=outi, total=toti, scratch=sc),
           8 * n)
@@ -323,6 +361,7 @@ def main():
             "us": round(k_ms * 1e3, 2), "GB/s": round(alg_bytes / (k_ms * 1e-3) / 1e9, 1),
             "note": "positions of the odd elements; same bytes as the compaction"}
         del idx
+        extra["pipelines_x_copy"] = pipeline_rows(x, m, stream, args.steps, extra["copy_i32"]["us"])
         extra["other_workloads"] = other_workloads(dev, max(5, args.steps // 5), stream)
     if extra:
         log("extra: " + json.dumps(extra))

@@ -232,6 +232,27 @@ int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t
 int ssc_radix_sort4_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t n, int passes,
                         void *scratch, size_t scratch_bytes, void *stream);
 
+/* Comparison only: the multi-launch structure of the pages, ported so that
+ * the single pass can be measured against it on this hardware. A scan is a
+ * tree of tile scans (8192-element tiles; each level writes its tiles'
+ * exclusive prefixes and one sum per tile, and the next level scans the
+ * sums) with the carries added back level by level: 3 launches up to
+ * 8192^2 elements ("Day 32 scan_2.cu": tile scan, scan of the tile sums,
+ * add the offsets). A compaction marks the flags into `ranks`, scans them
+ * there with that tree and scatters the survivors to out[rank], recomputing
+ * the predicate: 7 launches at 2^28 elements ("Day 33 compaction.cu": mark,
+ * scan, scatter). `ranks` (required, n words) ends as the exclusive scan of
+ * the flags. Results equal those of ssc_exclusive_scan_i32 and
+ * ssc_compact_i32; scratch (16-byte aligned, ssc_multipass_scratch_bytes
+ * bytes) holds the tile sums; no overlap of the arrays is allowed, except
+ * in == out for the scan. */
+size_t ssc_multipass_scratch_bytes(int64_t n);
+int ssc_exclusive_scan_multipass_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
+                                     void *scratch, size_t scratch_bytes, void *stream);
+int ssc_compact_multipass_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
+                              int32_t pb, int32_t *count, int32_t *ranks, void *scratch,
+                              size_t scratch_bytes, void *stream);
+
 /* out[i] = in[i] with 128-bit loads and stores: the bandwidth reference the
  * single pass is compared with ("Day 33 compaction.cu", copyInts; "Day 32
  * scan_2.cu", copyFloats). No overlap allowed. */

@@ -51,6 +51,9 @@ SIGNATURES = {
     "ssc_radix_sort_u32": (_INT, [_P, _P, _P, _I64, _P, _SZ, _P]),
     "ssc_radix_sort4_scratch_bytes": (_SZ, [_I64]),
     "ssc_radix_sort4_u32": (_INT, [_P, _P, _P, _I64, _INT, _P, _SZ, _P]),
+    "ssc_multipass_scratch_bytes": (_SZ, [_I64]),
+    "ssc_exclusive_scan_multipass_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_compact_multipass_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "ssc_copy_i32": (_INT, [_P, _P, _I64, _P]),
     "ssc_status_str": (ctypes.c_char_p, [_INT]),
     "ssc_last_hip_error": (_INT, []),
@@ -336,6 +339,52 @@ def radix_sort4(x: torch.Tensor, passes: int = 8, *, out: torch.Tensor | None = 
           x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, passes, scratch.data_ptr(),
           scratch.numel(), _stream(x))
     return out
+
+
+def multipass_scratch(n: int, device) -> torch.Tensor:
+    return torch.zeros(int(lib().ssc_multipass_scratch_bytes(n)), dtype=torch.uint8, device=device)
+
+
+def exclusive_scan_multipass(x: torch.Tensor, out: torch.Tensor | None = None,
+                             total: torch.Tensor | None = None,
+                             scratch: torch.Tensor | None = None):
+    """(out, total): the multi-launch int32 scan (comparison with the single pass)."""
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("exclusive_scan_multipass takes int32")
+    if out is None:
+        out = torch.empty_like(x)
+    if total is None:
+        total = torch.empty(1, dtype=torch.int32, device=x.device)
+    if scratch is None:
+        scratch = multipass_scratch(x.numel(), x.device)
+    _call("ssc_exclusive_scan_multipass_i32", lib().ssc_exclusive_scan_multipass_i32,
+          x.data_ptr(), out.data_ptr(), x.numel(), total.data_ptr(), scratch.data_ptr(),
+          scratch.numel(), _stream(x))
+    return out, total
+
+
+def compact_multipass(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+                      out: torch.Tensor | None = None, count: torch.Tensor | None = None,
+                      ranks: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """(out, count, ranks): the multi-launch int32 compaction (mark, scan,
+    scatter), for comparison with the single pass."""
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("compact_multipass takes int32")
+    n = x.numel()
+    if out is None:
+        out = torch.empty_like(x)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if ranks is None:
+        ranks = torch.empty_like(x)
+    if scratch is None:
+        scratch = multipass_scratch(n, x.device)
+    _call("ssc_compact_multipass_i32", lib().ssc_compact_multipass_i32,
+          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), ranks.data_ptr(),
+          scratch.data_ptr(), scratch.numel(), _stream(x))
+    return out, count, ranks
 
 
 def copy(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

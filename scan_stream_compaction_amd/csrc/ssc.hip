@@ -1176,6 +1176,119 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const int32_t *__restrict_
     store_chunk<VEC>(out, chunk, lane, rem, v);
 }
 
+// ============================== multi-launch pipelines (comparison only) ---
+// The pages' own structure, ported to this hardware to measure what the
+// single pass saves: the flags are written out, scanned by a tree of tile
+// scans (each writes its tiles' exclusive prefixes and one total per tile;
+// the totals are scanned by the next level) whose carries are added back
+// level by level, and a last kernel scatters the survivors to out[rank]
+// ("Day 33 compaction.cu": mark, scan, scatter in seven launches at its
+// size; "Day 32 scan_2.cu": tile scan, scan of the tile sums, add the
+// offsets). Tiles are 8192 elements: one 512-thread workgroup, 16 per lane
+// in the (load, lane, component) layout of the streaming kernels.
+
+// flags[i] = P(in[i]).
+template <int P, bool VEC>
+__global__ __launch_bounds__(kBlock) void mark_kernel(const int32_t *__restrict__ in,
+                                                      int32_t *__restrict__ flags, int64_t n,
+                                                      PredArgs pr) {
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
+    const int64_t chunk =
+        static_cast<int64_t>(blockIdx.x) * kSub + static_cast<int64_t>(w) * kChunk;
+    const uint32_t rem = chunk_rem(n, chunk);
+    int32_t v[kLoads][4];
+    load_chunk<VEC>(in, chunk, lane, rem, v);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[j][k] = pred_eval<P>(v[j][k], pr) ? 1 : 0;
+    store_chunk<VEC>(flags, chunk, lane, rem, v);
+}
+
+// Exclusive scan inside each 8192-element tile of `in` (uint32 wrap) into
+// `out` (in == out allowed); sums[tile] = the tile's total.
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void tile_scan_kernel(const uint32_t *in, uint32_t *out,
+                                                           int64_t n, uint32_t *__restrict__ sums,
+                                                           uint32_t *__restrict__ total) {
+    __shared__ uint32_t s_wave[kWaves];
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
+    const int64_t chunk =
+        static_cast<int64_t>(blockIdx.x) * kSub + static_cast<int64_t>(w) * kChunk;
+    const uint32_t rem = chunk_rem(n, chunk);
+    uint32_t v[kLoads][4];
+    load_chunk<VEC>(in, chunk, lane, rem, v);
+    uint32_t running = 0;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t x = v[j][k];
+            v[j][k] = s;
+            s += x;
+        }
+        const uint32_t incl = wave_inclusive_scan<SumU32>(s);
+        const uint32_t lead = running + incl - s;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[j][k] += lead;
+        running += static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+    }
+    if (lane == 0) s_wave[w] = running;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int i = 0; i < w; ++i) before += s_wave[i];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[j][k] += before;
+    store_chunk<VEC>(out, chunk, lane, rem, v);
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int i = 0; i < kWaves; ++i) t += s_wave[i];
+        sums[blockIdx.x] = t;
+        if (total != nullptr && gridDim.x == 1) *total = t;  // the top level: the grand total
+    }
+}
+
+// out[i] += carries[i / 8192] (uint32 wrap).
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void add_carry_kernel(uint32_t *__restrict__ out, int64_t n,
+                                                           const uint32_t *__restrict__ carries) {
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
+    const int64_t chunk =
+        static_cast<int64_t>(blockIdx.x) * kSub + static_cast<int64_t>(w) * kChunk;
+    const uint32_t rem = chunk_rem(n, chunk);
+    const uint32_t c = carries[blockIdx.x];
+    uint32_t v[kLoads][4];
+    load_chunk<VEC>(out, chunk, lane, rem, v);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[j][k] += c;
+    store_chunk<VEC>(out, chunk, lane, rem, v);
+}
+
+// out[rank[i]] = in[i] where P(in[i]) (the predicate evaluated again rather
+// than read back); the element n - 1 also writes the count.
+template <int P>
+__global__ __launch_bounds__(kBlock) void scatter_kernel(const int32_t *__restrict__ in,
+                                                         const int32_t *__restrict__ rank,
+                                                         int32_t *__restrict__ out, int64_t n,
+                                                         PredArgs pr, int32_t *__restrict__ count) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+        const int32_t x = in[i];
+        const bool f = pred_eval<P>(x, pr);
+        const int32_t r = rank[i];
+        if (f && r >= 0 && static_cast<int64_t>(r) < n) out[r] = x;
+        if (i == n - 1) *count = r + (f ? 1 : 0);
+    }
+}
+
 // Clears `words` 32-bit words (a kernel rather than a memset node).
 __global__ __launch_bounds__(kBlock) void clear_kernel(uint32_t *__restrict__ p, int64_t words) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < words;
@@ -1413,6 +1526,65 @@ struct LaunchAtomic {
         else
             hipLaunchKernelGGL((compact_atomic_kernel<P, VEC, 1>), dim3(subs), dim3(kBlock), 0, s,
                                in, out, n, pr, count);
+        return launched();
+    }
+};
+
+// ---- multi-launch pipelines (comparison) ----
+// Words of tile sums for every level of the tile-scan tree over n values,
+// each level rounded up to 4 words so that every level starts 16-byte aligned.
+int64_t multipass_level_words(int64_t tiles) { return (tiles + 3) & ~int64_t{3}; }
+
+int64_t multipass_sum_words(int64_t n) {
+    int64_t words = 0;
+    for (int64_t m = n; m > 1;) {
+        const int64_t tiles = (m + kSub - 1) / kSub;
+        words += multipass_level_words(tiles);
+        m = tiles;
+    }
+    return words < 4 ? 4 : words;
+}
+
+// Exclusive scan of n uint32 values by levels: tile scans down the tree of
+// tile sums, then the carries added back on the way up. The top level's
+// total goes to *total when given. Launches: 2 * levels - 1.
+int multipass_scan(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *sums, uint32_t *total,
+                   bool vec, hipStream_t s) {
+    const uint32_t tiles = static_cast<uint32_t>((n + kSub - 1) / kSub);
+    if (vec)
+        hipLaunchKernelGGL((tile_scan_kernel<true>), dim3(tiles), dim3(kBlock), 0, s, in, out, n,
+                           sums, total);
+    else
+        hipLaunchKernelGGL((tile_scan_kernel<false>), dim3(tiles), dim3(kBlock), 0, s, in, out, n,
+                           sums, total);
+    SSC_TRY(launched());
+    if (tiles == 1) return SSC_OK;
+    // the sums are scanned in place by the next level (aligned: scratch is)
+    SSC_TRY(multipass_scan(sums, sums, tiles, sums + multipass_level_words(tiles), total, true, s));
+    if (vec)
+        hipLaunchKernelGGL((add_carry_kernel<true>), dim3(tiles), dim3(kBlock), 0, s, out, n, sums);
+    else
+        hipLaunchKernelGGL((add_carry_kernel<false>), dim3(tiles), dim3(kBlock), 0, s, out, n, sums);
+    return launched();
+}
+
+template <int P, bool VEC>
+struct LaunchMark {
+    static int run(const int32_t *in, int32_t *flags, int64_t n, PredArgs pr, hipStream_t s) {
+        hipLaunchKernelGGL((mark_kernel<P, VEC>), dim3(subs_for(n)), dim3(kBlock), 0, s, in, flags,
+                           n, pr);
+        return launched();
+    }
+};
+
+template <int P, bool VEC>
+struct LaunchScatter {
+    static int run(const int32_t *in, const int32_t *rank, int32_t *out, int64_t n, PredArgs pr,
+                   int32_t *count, hipStream_t s) {
+        const int64_t blocks = (n + kBlock - 1) / kBlock;
+        const dim3 grid(static_cast<unsigned>(blocks < 8192 ? blocks : 8192));
+        hipLaunchKernelGGL((scatter_kernel<P>), grid, dim3(kBlock), 0, s, in, rank, out, n, pr,
+                           count);
         return launched();
     }
 };
@@ -1756,6 +1928,66 @@ int ssc_radix_sort4_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_
         src = dst;
     }
     return SSC_OK;
+}
+
+size_t ssc_multipass_scratch_bytes(int64_t n) {
+    return static_cast<size_t>(multipass_sum_words(n < 0 ? 0 : n)) * 4 + 256;
+}
+
+int ssc_exclusive_scan_multipass_i32(const int32_t *in, int32_t *out, int64_t n, int32_t *total,
+                                     void *scratch, size_t scratch_bytes, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (n > 0 && (in == nullptr || out == nullptr)) return SSC_ERR_ARG;
+    if (!aligned(in, 4) || !aligned(out, 4) || (total && !aligned(total, 4))) return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (in != out && overlap(in, bytes, out, bytes)) return SSC_ERR_ALIAS;
+    if (total && (overlap(total, 4, in, bytes) || overlap(total, 4, out, bytes)))
+        return SSC_ERR_ALIAS;
+    if (scratch == nullptr || !aligned(scratch, 16) ||
+        scratch_bytes < ssc_multipass_scratch_bytes(n))
+        return SSC_ERR_SCRATCH;
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        (total && overlap(scratch, scratch_bytes, total, 4)))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return total ? clear_words(total, 1, s) : SSC_OK;
+    return multipass_scan(reinterpret_cast<const uint32_t *>(in), reinterpret_cast<uint32_t *>(out),
+                          n, static_cast<uint32_t *>(scratch), reinterpret_cast<uint32_t *>(total),
+                          aligned(in, 16) && aligned(out, 16), s);
+}
+
+int ssc_compact_multipass_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
+                              int32_t pb, int32_t *count, int32_t *ranks, void *scratch,
+                              size_t scratch_bytes, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (count == nullptr || ranks == nullptr || (n > 0 && (in == nullptr || out == nullptr)))
+        return SSC_ERR_ARG;
+    SSC_TRY(check_pred(pred, pa, pb));
+    if (!aligned(in, 4) || !aligned(out, 4) || !aligned(count, 4) || !aligned(ranks, 4))
+        return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (overlap(in, bytes, out, bytes) || overlap(ranks, bytes, in, bytes) ||
+        overlap(ranks, bytes, out, bytes) || overlap(count, 4, in, bytes) ||
+        overlap(count, 4, out, bytes) || overlap(count, 4, ranks, bytes))
+        return SSC_ERR_ALIAS;
+    if (scratch == nullptr || !aligned(scratch, 16) ||
+        scratch_bytes < ssc_multipass_scratch_bytes(n))
+        return SSC_ERR_SCRATCH;
+    if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
+        overlap(scratch, scratch_bytes, ranks, bytes) || overlap(scratch, scratch_bytes, count, 4))
+        return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    const PredArgs pr = make_pred_args(pred, pa, pb);
+    const bool vec = aligned(in, 16) && aligned(ranks, 16);
+    SSC_TRY(dispatch_pred<LaunchMark>(pred, vec, in, ranks, n, pr, s));
+    SSC_TRY(multipass_scan(reinterpret_cast<const uint32_t *>(ranks),
+                           reinterpret_cast<uint32_t *>(ranks), n, static_cast<uint32_t *>(scratch),
+                           nullptr, aligned(ranks, 16), s));
+    return dispatch_pred<LaunchScatter>(pred, true, in, static_cast<const int32_t *>(ranks), out, n,
+                                        pr, count, s);
 }
 
 int ssc_copy_i32(const int32_t *in, int32_t *out, int64_t n, void *stream) {

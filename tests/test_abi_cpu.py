@@ -196,6 +196,15 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     assert L.ssc_compact_f32(A, A + 8, 100, 7, 0.5, 0.0, C, None, S, big, None) == ALIAS
     assert L.ssc_partition_f32(A, B, 100, 9, 0.0, 1.0, None, S, big, None) == ARG
     assert L.ssc_select_index_f32(A, B, 100, 6, 0.0, 0.0, C, S, 100, None) == SCRATCH
+    # multi-launch comparison pipelines
+    # levels of 8193, 2 and 1 tile sums, each rounded up to 4 words
+    assert L.ssc_multipass_scratch_bytes(8192 * 8192 + 1) == 4 * (8196 + 4 + 4) + 256
+    assert L.ssc_exclusive_scan_multipass_i32(A, A + 4, 100, None, S, big, None) == ALIAS
+    assert L.ssc_exclusive_scan_multipass_i32(A, B, 100, None, S + 8, big, None) == SCRATCH
+    assert L.ssc_exclusive_scan_multipass_i32(A, B, 100, None, S, 100, None) == SCRATCH
+    assert L.ssc_compact_multipass_i32(A, B, 100, 1, 0, 0, C, None, S, big, None) == ARG
+    assert L.ssc_compact_multipass_i32(A, B, 100, 1, 0, 0, C, B + 8, S, big, None) == ALIAS
+    assert L.ssc_compact_multipass_i32(A, B, 100, 7, 0, 0, C, C + 64, S, big, None) == ARG
     # copy
     assert L.ssc_copy_i32(A, A + 4, 100, None) == ALIAS
     assert L.ssc_copy_i32(A, B, -1, None) == ARG

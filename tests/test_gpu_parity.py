@@ -451,6 +451,27 @@ def test_f32_compaction_large():
     assert checks.first_mismatch(bits(host(out)[:m]), bits(want)) == -1
 
 
+@pytest.mark.parametrize("n", [1, 5, 8191, 8192, 8193, 3 * T + 611, 8192 * 8192 + 77, 10_000_000])
+def test_multipass_pipelines_match_the_oracle(n):
+    """The multi-launch comparison pipelines (one, two and three levels of tile
+    sums) give the oracle's results, like the single pass."""
+    x = wl.uniform_below(n + 5, n, 7) - 2
+    xd = dev(x)
+    want, total = oracle.exclusive_scan_i32(x)
+    out, tot = ssc.exclusive_scan_multipass(xd)
+    assert checks.first_mismatch(host(out), want) == -1 and int(host(tot)[0]) == total
+    y = xd.clone()
+    ssc.exclusive_scan_multipass(y, out=y)
+    assert checks.first_mismatch(host(y), want) == -1
+    surv, m, ranks = oracle.compact_i32(x, oracle.PRED_NONZERO, want_ranks=True)
+    o = torch.full_like(xd, SENTINEL)
+    _, cnt, rk = ssc.compact_multipass(xd, "nonzero", out=o)
+    assert int(host(cnt)[0]) == m
+    got = host(o)
+    assert checks.first_mismatch(got[:m], surv) == -1 and np.all(got[m:] == SENTINEL)
+    assert checks.first_mismatch(host(rk), ranks) == -1
+
+
 def test_keep_all_is_copy_and_keep_none_writes_nothing():
     x = wl.uniform_below(5, 7 * T + 77, 9) + 1
     out, cnt = ssc.compact(dev(x), "nonzero")
