@@ -73,6 +73,7 @@ constexpr size_t kHeaderBytes = 512;
 constexpr size_t kOffClaim = 0;      // uint64 {epoch:32 | next tile:32}
 constexpr size_t kOffTimedOut = 8;   // uint32 look-back time-out flag
 constexpr size_t kOffDone = 12;      // uint32 workgroups finished (counting passes)
+constexpr size_t kOffClaimed = 16;   // uint32 workgroups done claiming (persistent kernels)
 constexpr size_t kOffAcc = 64;       // uint32[kSpread] partial counts
 constexpr size_t kOffAcc32 = 128;    // uint32[32] per-bit clear counts being summed
 constexpr size_t kOffKept32 = 256;   // uint32[32] per-bit clear counts of the current sort
@@ -97,6 +98,7 @@ struct ScratchView {
     uint64_t *claim;
     uint32_t *timed_out;
     uint32_t *done;
+    uint32_t *claimed;
     uint32_t *acc;
     uint32_t *acc32;
     uint32_t *kept32;
@@ -109,6 +111,7 @@ __host__ __device__ inline ScratchView view(void *scratch) {
     v.claim = reinterpret_cast<uint64_t *>(b + kOffClaim);
     v.timed_out = reinterpret_cast<uint32_t *>(b + kOffTimedOut);
     v.done = reinterpret_cast<uint32_t *>(b + kOffDone);
+    v.claimed = reinterpret_cast<uint32_t *>(b + kOffClaimed);
     v.acc = reinterpret_cast<uint32_t *>(b + kOffAcc);
     v.acc32 = reinterpret_cast<uint32_t *>(b + kOffAcc32);
     v.kept32 = reinterpret_cast<uint32_t *>(b + kOffKept32);
@@ -278,20 +281,49 @@ __device__ __forceinline__ void tile_prefixes(const uint32_t *s_pre, int w,
 // use it (it uses words 0 .. words_used - 1). Over any kMaxTiles consecutive
 // calls every word is thus rewritten or cleared, far within the 2^30-call
 // period of the tag, so no stale descriptor can match a later tag.
+__device__ __forceinline__ void end_epoch(const ScratchView &sv, uint32_t epoch,
+                                          uint32_t words_used, uint32_t capacity) {
+    __hip_atomic_store(sv.claim, static_cast<uint64_t>(epoch + 1u) << 32, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t slot = epoch & (kMaxTiles - 1u);
+    if (slot >= words_used && slot < capacity)
+        __hip_atomic_store(sv.desc + slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t words_used,
                                                uint32_t claims, uint32_t capacity) {
     const uint64_t c =
         __hip_atomic_fetch_add(sv.claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t tile = static_cast<uint32_t>(c);
-    const uint32_t epoch = static_cast<uint32_t>(c >> 32);
-    if (tile == claims - 1) {
-        __hip_atomic_store(sv.claim, static_cast<uint64_t>(epoch + 1u) << 32, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t slot = epoch & (kMaxTiles - 1u);
-        if (slot >= words_used && slot < capacity)
-            __hip_atomic_store(sv.desc + slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (static_cast<uint32_t>(c) == claims - 1)
+        end_epoch(sv, static_cast<uint32_t>(c >> 32), words_used, capacity);
     return c;
+}
+
+// The persistent kernel's claims: a workgroup claims its first tile, then
+// its second and third together (two consecutive numbers, one atomic), then
+// one per tile, and stops claiming once it holds a number past the end. Its
+// first tile is claimed alone so that first tiles interleave across
+// workgroups: were the first three consecutive, each workgroup's first
+// look-back would wait for the previous workgroup's third tile, a chain
+// through the whole grid. How many
+// claims a call makes then depends on timing, so the counter is reset by the
+// last workgroup to finish claiming instead: each one counts itself in
+// *claimed once, after its last claim has returned, and the one that
+// completes the count ends the epoch. Every claim of the call has been
+// performed by then, so all carry one epoch.
+__device__ __forceinline__ uint64_t claim_tiles(const ScratchView &sv, uint64_t k) {
+    return __hip_atomic_fetch_add(sv.claim, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void finish_claims(const ScratchView &sv, uint32_t epoch,
+                                              uint32_t workgroups, uint32_t words_used,
+                                              uint32_t capacity) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(sv.claimed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == workgroups - 1u) {
+        __hip_atomic_store(sv.claimed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        end_epoch(sv, epoch, words_used, capacity);
+    }
 }
 
 // Arrival of a data wavefront (whole wavefront) after writing its chunk
@@ -488,7 +520,8 @@ __device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint3
 // ===================================================== compaction kernel ---
 // Persistent form: one 1024-thread workgroup per compute unit (its LDS and
 // 128 VGPRs per lane fill the unit) loops over tiles of 30720 elements whose
-// numbers come from the atomic counter, claimed three ahead. A tile is one
+// numbers come from the atomic counter, claimed three ahead (the second and
+// third with one atomic, while the first is loading). A tile is one
 // chunk of 2048 elements (eight 128-bit loads per lane) for each of the 15
 // data wavefronts; the 16th is the control wavefront.
 //
@@ -518,11 +551,13 @@ __device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint3
 // the loop, folded into instruction offsets, instead of being hoisted into
 // registers held across it.
 //
-// Forward progress: a workgroup processes its claims in increasing order and
-// stops claiming after its first claim past the end, so a call makes exactly
-// tiles + gridDim.x claims. The lowest unfinished tile is the current tile
-// of the workgroup that claimed it (any earlier claim of that workgroup is
-// lower and finished), and its look-back needs only lower, finished tiles.
+// Forward progress: only running workgroups hold tiles (every tile number
+// comes from a claim), a workgroup processes its claims in increasing order,
+// and it stops claiming after its first number past the end. The lowest
+// unfinished tile is the current tile of the workgroup that claimed it (any
+// earlier claim of that workgroup is lower and finished), and its look-back
+// needs only lower, finished tiles; so the kernel finishes whichever of its
+// workgroups are resident at once.
 // KIND: compaction (survivors' values), compaction that also writes the
 // ranks, stable partition, or selection (survivors' indices).
 enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3 };
@@ -540,42 +575,48 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     __shared__ uint32_t s_tot[kDataWaves];
     __shared__ uint32_t s_pre[3][kDataWaves + 1];  // chunk prefixes + aggregate, by tile mod 3
     __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
-    __shared__ uint32_t s_first[3], s_tag, s_arrive;
+    __shared__ uint32_t s_first[3], s_epoch, s_arrive;
 
     const ScratchView sv = view(scratch);
-    const uint32_t claims = num_tiles + gridDim.x;  // one claim past the end per workgroup
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
     if (threadIdx.x == 0) {
-        // up to three claims, stopping at the first one past the end
-        const uint64_t c = claim_tile(sv, num_tiles, claims, capacity);
-        uint32_t t = static_cast<uint32_t>(c);
-        s_first[0] = t;
-        s_first[1] = s_first[2] = kNoTile;
-        if (t < num_tiles) {
-            t = static_cast<uint32_t>(claim_tile(sv, num_tiles, claims, capacity));
-            s_first[1] = t;
-            if (t < num_tiles)
-                s_first[2] = static_cast<uint32_t>(claim_tile(sv, num_tiles, claims, capacity));
-        }
-        s_tag = static_cast<uint32_t>(c >> 32) & kTagMask;
+        const uint64_t c = claim_tiles(sv, 1);
+        s_first[0] = static_cast<uint32_t>(c);
+        s_epoch = static_cast<uint32_t>(c >> 32);
         s_arrive = 0;
     }
-    __syncthreads();  // B0
+    __syncthreads();  // B0: the first tile
     uint32_t tile = uniform(s_first[0]);
-    uint32_t nxt = uniform(s_first[1]);
-    uint32_t nxt2 = uniform(s_first[2]);
-    const uint32_t tag = uniform(s_tag);
-    if (tile >= num_tiles) return;  // this workgroup's one claim past the end
+    const uint32_t epoch = uniform(s_epoch);
+    const uint32_t tag = epoch & kTagMask;
+    if (tile >= num_tiles) {  // nothing left for this workgroup
+        if (w == kCtrlWave && lane == 0) finish_claims(sv, epoch, gridDim.x, num_tiles, capacity);
+        return;
+    }
+    bool last_claim = false;  // control lane 0: the claims just made reached the end
+    if (w == kCtrlWave && lane == 0) {
+        // the second and third tiles, one atomic round trip while the data
+        // wavefronts load the first tile
+        const uint32_t c1 = static_cast<uint32_t>(claim_tiles(sv, 2));
+        s_first[1] = c1;
+        s_first[2] = c1 + 1u;
+        last_claim = c1 + 1u >= num_tiles;
+    }
     uint32_t par = 0;  // tile parity within the workgroup: s_base, s_next
     uint32_t tri = 0;  // tile number within the workgroup mod 3: s_pre
 
     if (w == kCtrlWave) {
+        __syncthreads();  // B0b: the second and third tiles
+        uint32_t nxt = uniform(s_first[1]);
+        uint32_t nxt2 = uniform(s_first[2]);
         __syncthreads();  // B0': the first tile's arrivals are in
         while (true) {
             uint32_t nxt3 = kNoTile;
-            if (lane == 0 && nxt2 < num_tiles)
-                nxt3 = static_cast<uint32_t>(claim_tile(sv, num_tiles, claims, capacity));
+            if (lane == 0 && nxt2 < num_tiles) {
+                nxt3 = static_cast<uint32_t>(claim_tiles(sv, 1));
+                last_claim = nxt3 >= num_tiles;
+            }
             uint32_t prefix = 0;
             if (tile != 0)
                 prefix = look_back<SumU32, kSelPollSleep>(sv.desc, tile, tag, sv.timed_out);
@@ -589,6 +630,10 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
                 if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, prefix + agg);
                 if (KIND != kPartition && tile == num_tiles - 1)
                     *count = static_cast<int32_t>(prefix + agg);
+                // after the barrier: the count's atomic round trip stays off
+                // the path to this tile's base
+                if (last_claim) finish_claims(sv, epoch, gridDim.x, num_tiles, capacity);
+                last_claim = false;
             }
             if (nxt >= num_tiles) return;
             tile = nxt;
@@ -694,6 +739,9 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 
     rem_cur = rem_of(tile);
     load_chunk_rsrc<VEC>(in, chunk_of(tile), rem_cur, lane, va);
+    __syncthreads();  // B0b: the second and third tiles
+    uint32_t nxt = uniform(s_first[1]);
+    uint32_t nxt2 = uniform(s_first[2]);
     load_chunk_rsrc<VEC>(in, chunk_of(nxt), rem_of(nxt), lane, vb);
     SSC_FLAG_AND_ARRIVE(va, tile, rem_cur, fm_cur, a_cur, tri, lane)
     // B0': without it a fast wavefront could arrive for the next tile
