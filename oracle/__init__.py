@@ -86,6 +86,24 @@ def lib() -> ctypes.CDLL:
         L.orc_partition_i32.restype = i64
         L.orc_radix_sort_u32.argtypes = [u32p, u32p, u32p, i64, c_int]
         L.orc_radix_sort_u32.restype = None
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.orc_compact_flags_b32.argtypes = [u32p, u8p, u32p, i64]
+        L.orc_compact_flags_b32.restype = i64
+        L.orc_select_flags.argtypes = [u8p, i32p, i64]
+        L.orc_select_flags.restype = i64
+        L.orc_compact_kv_i32.argtypes = [i32p, u32p, i32p, u32p, i64, c_int, i32, i32]
+        L.orc_compact_kv_i32.restype = i64
+        L.orc_compact_kv_f32.argtypes = [f32p, u32p, f32p, u32p, i64, c_int, f32, f32]
+        L.orc_compact_kv_f32.restype = i64
+        L.orc_pred_args_ok_i64.argtypes = [c_int, i32]
+        L.orc_pred_args_ok_i64.restype = c_int
+        L.orc_pred_i64.argtypes = [i64, c_int, i32]
+        L.orc_pred_i64.restype = c_int
+        L.orc_compact_i64.argtypes = [i64p, i64p, i64, c_int, i32]
+        L.orc_compact_i64.restype = i64
+        L.orc_select_index_i64.argtypes = [i64p, i32p, i64, c_int, i32]
+        L.orc_select_index_i64.restype = i64
         _lib = L
     return _lib
 
@@ -232,3 +250,97 @@ def radix_sort_u32(x, passes: int = 32) -> np.ndarray:
     lib().orc_radix_sort_u32(_ptr(x, ctypes.c_uint32), _ptr(out, ctypes.c_uint32),
                              _ptr(tmp, ctypes.c_uint32), x.size, passes)
     return out
+
+
+def _b32(a) -> np.ndarray:
+    """32-bit words of an int32, uint32 or float32 array (bits unchanged)."""
+    a = np.ascontiguousarray(a)
+    assert a.dtype.itemsize == 4, a.dtype
+    return a.view(np.uint32)
+
+
+def _flag_bytes(f) -> np.ndarray:
+    f = np.ascontiguousarray(f)
+    assert f.dtype.itemsize == 1, f.dtype
+    return f.view(np.uint8)
+
+
+def compact_flags(x, f):
+    """(survivors, count): the 32-bit elements of x whose flag byte is nonzero,
+    in input order, with x's dtype."""
+    x = np.ascontiguousarray(x)
+    w = _b32(x)
+    fb = _flag_bytes(f)
+    assert fb.size == w.size
+    out = np.empty(w.size, np.uint32)
+    m = lib().orc_compact_flags_b32(_ptr(w, ctypes.c_uint32), _ptr(fb, ctypes.c_uint8),
+                                    _ptr(out, ctypes.c_uint32), w.size)
+    return out[:m].view(x.dtype).copy(), int(m)
+
+
+def select_flags(f):
+    """(indices, count): positions whose flag byte is nonzero."""
+    fb = _flag_bytes(f)
+    idx = np.empty(fb.size, np.int32)
+    m = lib().orc_select_flags(_ptr(fb, ctypes.c_uint8), _ptr(idx, ctypes.c_int32), fb.size)
+    return idx[:m].copy(), int(m)
+
+
+def compact_kv(keys, vals, pred: int, a=0, b=0):
+    """(keys_out, vals_out, count): the pairs whose key satisfies the predicate,
+    in input order. int32 keys take the integer predicates, float32 keys the
+    fp32 ones; values are any 32-bit type, moved bit for bit."""
+    keys = np.ascontiguousarray(keys)
+    vals = np.ascontiguousarray(vals)
+    vw = _b32(vals)
+    assert keys.size == vw.size
+    ok = np.empty(keys.size, keys.dtype)
+    ov = np.empty(vw.size, np.uint32)
+    if keys.dtype == np.int32:
+        m = lib().orc_compact_kv_i32(_ptr(keys, ctypes.c_int32), _ptr(vw, ctypes.c_uint32),
+                                     _ptr(ok, ctypes.c_int32), _ptr(ov, ctypes.c_uint32),
+                                     keys.size, pred, int(a), int(b))
+    elif keys.dtype == np.float32:
+        m = lib().orc_compact_kv_f32(_ptr(keys, ctypes.c_float), _ptr(vw, ctypes.c_uint32),
+                                     _ptr(ok, ctypes.c_float), _ptr(ov, ctypes.c_uint32),
+                                     keys.size, pred, float(a), float(b))
+    else:
+        raise TypeError(keys.dtype)
+    return ok[:m].copy(), ov[:m].view(vals.dtype).copy(), int(m)
+
+
+def _i64(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint64:
+        return a.view(np.int64)
+    if a.dtype != np.int64:
+        a = a.astype(np.int64)
+    return a
+
+
+def pred_args_ok_i64(pred: int, pa: int = 0) -> bool:
+    return bool(lib().orc_pred_args_ok_i64(pred, pa))
+
+
+def pred_i64(x: int, pred: int, pa: int = 0) -> int:
+    """P(x) for one 64-bit value (given as a Python int in int64 or uint64 range)."""
+    return int(lib().orc_pred_i64(int(np.array(x, dtype=np.uint64 if x >= 2**63 else np.int64)
+                                      .view(np.int64)), pred, pa))
+
+
+def compact_i64(x, pred: int, pa: int = 0):
+    """(survivors, count) of 64-bit elements in input order."""
+    x = _i64(x)
+    out = np.empty(x.size, np.int64)
+    m = lib().orc_compact_i64(_ptr(x, ctypes.c_int64), _ptr(out, ctypes.c_int64), x.size,
+                              pred, pa)
+    return out[:m].copy(), int(m)
+
+
+def select_index_i64(x, pred: int, pa: int = 0):
+    """(indices, count) of the 64-bit elements for which the predicate holds."""
+    x = _i64(x)
+    idx = np.empty(x.size, np.int32)
+    m = lib().orc_select_index_i64(_ptr(x, ctypes.c_int64), _ptr(idx, ctypes.c_int32), x.size,
+                                   pred, pa)
+    return idx[:m].copy(), int(m)

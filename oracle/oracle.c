@@ -39,6 +39,15 @@
  *     template over the element type) take comparison predicates with IEEE
  *     semantics: NaN compares false (so NaN is nonzero but never above,
  *     below or inside a range) and -0.0 equals 0.0.
+ *   - 64-bit elements (the same template) take the bit predicates on all 64
+ *     bits of the two's-complement value: nonzero, odd, even, bit b set or
+ *     clear for 0 <= b <= 63. The residue predicate is not defined for them.
+ *   - A caller's own predicate ("Day 33 compaction.cu": the predicate is the
+ *     only part that changes, everything after it reads an array of ones and
+ *     zeros) arrives as one flag byte per element; any nonzero byte keeps
+ *     the element.
+ *   - Key-value compaction: the predicate is taken on the key and each value
+ *     travels with its key, so both outputs hold the same positions.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -298,4 +307,119 @@ void orc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp,
                           ORC_PRED_BIT_CLEAR, b, 0);
         memcpy(out, tmp, (size_t)n * sizeof(uint32_t));
     }
+}
+
+/* ---- a caller's predicate as flag bytes ---- */
+
+/* Order-preserving compaction of 32-bit words (int32 or fp32 bits, moved
+ * unchanged) whose flag byte is nonzero; returns their number. */
+int64_t orc_compact_flags_b32(const uint32_t *in, const uint8_t *flags, uint32_t *out,
+                              int64_t n) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (flags[i] != 0) {
+            out[m] = in[i];
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* Positions i whose flag byte is nonzero, in increasing order. */
+int64_t orc_select_flags(const uint8_t *flags, int32_t *idx, int64_t n) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (flags[i] != 0) {
+            idx[m] = (int32_t)i;
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* ---- key-value pairs ---- */
+
+/* Pairs (keys[i], vals[i]) whose key satisfies the int32 predicate, in input
+ * order; values are 32-bit words moved unchanged. Returns their number. */
+int64_t orc_compact_kv_i32(const int32_t *keys, const uint32_t *vals, int32_t *okeys,
+                           uint32_t *ovals, int64_t n, int pred, int32_t pa, int32_t pb) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred(keys[i], pred, pa, pb)) {
+            okeys[m] = keys[i];
+            ovals[m] = vals[i];
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* As orc_compact_kv_i32 with fp32 keys and the fp32 predicates. */
+int64_t orc_compact_kv_f32(const float *keys, const uint32_t *vals, float *okeys,
+                           uint32_t *ovals, int64_t n, int pred, float a, float b) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred_f32(keys[i], pred, a, b)) {
+            okeys[m] = keys[i];
+            ovals[m] = vals[i];
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* ---- 64-bit elements ---- */
+
+/* 1 if the predicate and its argument are usable on 64-bit elements. */
+int orc_pred_args_ok_i64(int pred, int32_t pa) {
+    switch (pred) {
+    case ORC_PRED_NONZERO:
+    case ORC_PRED_ODD:
+    case ORC_PRED_EVEN:
+        return 1;
+    case ORC_PRED_BIT_SET:
+    case ORC_PRED_BIT_CLEAR:
+        return pa >= 0 && pa <= 63;
+    default:
+        return 0;
+    }
+}
+
+/* The predicate on a 64-bit element, taken on its two's-complement bits. */
+int orc_pred_i64(int64_t x, int pred, int32_t pa) {
+    uint64_t u = (uint64_t)x;
+    switch (pred) {
+    case ORC_PRED_NONZERO: return x != 0;
+    case ORC_PRED_ODD: return (u & 1u) == 1u;
+    case ORC_PRED_EVEN: return (u & 1u) == 0u;
+    case ORC_PRED_BIT_SET: return ((u >> pa) & 1u) == 1u;
+    case ORC_PRED_BIT_CLEAR: return ((u >> pa) & 1u) == 0u;
+    default: return 0;
+    }
+}
+
+/* Order-preserving compaction of 64-bit elements; returns the survivors'
+ * number. */
+int64_t orc_compact_i64(const int64_t *in, int64_t *out, int64_t n, int pred, int32_t pa) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred_i64(in[i], pred, pa)) {
+            out[m] = in[i];
+            ++m;
+        }
+    }
+    return m;
+}
+
+/* Positions of the 64-bit elements for which the predicate holds. */
+int64_t orc_select_index_i64(const int64_t *in, int32_t *idx, int64_t n, int pred,
+                             int32_t pa) {
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (orc_pred_i64(in[i], pred, pa)) {
+            idx[m] = (int32_t)i;
+            ++m;
+        }
+    }
+    return m;
 }

@@ -441,6 +441,115 @@ def test_radix_matches_sort_and_stable_prefix_sorts():
     assert oracle.radix_sort_u32(small).tolist() == sorted(small.tolist())
 
 
+# --- a caller's predicate as flag bytes, key-value pairs, 64-bit elements -------
+
+def test_flag_compaction_against_numpy_and_brute_force():
+    """Compaction by flag bytes ("Day 33 compaction.cu": everything after the
+    predicate reads an array of ones and zeros): against numpy boolean
+    indexing with any nonzero byte as true, against a k-th-survivor linear
+    search for every flag vector of length <= 10, and selection against
+    numpy's flatnonzero."""
+    from scan_stream_compaction_amd import workloads
+    rng = np.random.default_rng(5)
+    x = workloads.full_int32(7, 20_011)
+    f = rng.integers(0, 4, x.size).astype(np.uint8) * np.uint8(85)  # 0, 85, 170, 255
+    f[:6] = [0, 1, 2, 128, 255, 0]
+    surv, m = oracle.compact_flags(x, f)
+    assert m == int((f != 0).sum())
+    assert np.array_equal(surv, x[f != 0])
+    xf = x.view(np.float32)
+    survf, mf = oracle.compact_flags(xf, f)
+    assert mf == m and np.array_equal(survf.view(np.uint32), xf[f != 0].view(np.uint32))
+    idx, mi = oracle.select_flags(f)
+    assert mi == m and np.array_equal(idx, np.flatnonzero(f))
+    assert np.array_equal(oracle.compact_flags(np.arange(x.size, dtype=np.int32), f)[0], idx)
+    for n in range(0, 11):
+        xs = list(range(100, 100 + n))
+        for mask in range(1 << n):
+            keep = [(mask >> i) & 1 for i in range(n)]
+            fb = np.array([k * (1 + 7 * i) for i, k in enumerate(keep)], np.uint8)
+            got, mm = oracle.compact_flags(np.array(xs, np.int32), fb)
+            assert mm == sum(keep)
+            for k in range(mm):
+                assert got[k] == _kth_survivor(xs, keep, k)
+            assert oracle.select_flags(fb)[0].tolist() == [i for i in range(n) if keep[i]]
+    assert oracle.compact_flags(np.zeros(0, np.int32), np.zeros(0, np.uint8))[1] == 0
+
+
+def test_key_value_pairs_stay_together():
+    """Key-value compaction: the keys compacted are the keys numpy's mask keeps,
+    and every value is the one that sat beside its key (values are a
+    one-to-one function of the position, so a value out of place shows)."""
+    from scan_stream_compaction_amd import workloads
+    keys = workloads.full_int32(9, 30_001)
+    vals = (np.arange(keys.size, dtype=np.uint32) * np.uint32(2654435761)).view(np.float32)
+    cases = [(oracle.PRED_ODD, 0, 0, (keys & 1) == 1),
+             (oracle.PRED_BIT_CLEAR, 30, 0, ((keys.view(np.uint32) >> 30) & 1) == 0),
+             (oracle.PRED_MOD_LT, 100, 37, np.mod(keys.astype(np.int64), 100) < 37)]
+    for pred, a, b, mask in cases:
+        ok, ov, m = oracle.compact_kv(keys, vals, pred, a, b)
+        assert m == int(mask.sum())
+        assert np.array_equal(ok, keys[mask])
+        assert np.array_equal(ov.view(np.uint32), vals[mask].view(np.uint32))
+    fk = (workloads.unit_float32(4, 10_000) * 2 - 1).astype(np.float32)
+    fk[:4] = [np.nan, -0.0, 0.0, 0.5]
+    iv = np.arange(fk.size, dtype=np.int32)
+    with np.errstate(invalid="ignore"):
+        for pred, a, b, mask in [(oracle.PRED_F32_GT, 0.25, 0.0, fk > np.float32(0.25)),
+                                 (oracle.PRED_F32_NONZERO, 0.0, 0.0, fk != 0)]:
+            ok, ov, m = oracle.compact_kv(fk, iv, pred, a, b)
+            assert m == int(mask.sum())
+            assert np.array_equal(ok.view(np.uint32), fk[mask].view(np.uint32))
+            assert np.array_equal(ov, np.flatnonzero(mask))
+
+
+I64_PRED_NAMES = {"NONZERO": oracle.PRED_NONZERO, "ODD": oracle.PRED_ODD,
+                  "EVEN": oracle.PRED_EVEN, "BIT_SET": oracle.PRED_BIT_SET,
+                  "BIT_CLEAR": oracle.PRED_BIT_CLEAR}
+
+
+def test_predicate_i64_hand_cases(golden_dir):
+    rows = 0
+    with open(os.path.join(golden_dir, "predicate_cases_i64.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            xs, name, b, want = line.split()
+            got = oracle.pred_i64(int(xs), I64_PRED_NAMES[name], int(b))
+            assert got == int(want), line
+            rows += 1
+    assert rows >= 35
+    assert oracle.pred_args_ok_i64(oracle.PRED_BIT_SET, 63)
+    assert not oracle.pred_args_ok_i64(oracle.PRED_BIT_SET, 64)
+    assert not oracle.pred_args_ok_i64(oracle.PRED_BIT_CLEAR, -1)
+    assert not oracle.pred_args_ok_i64(oracle.PRED_MOD_LT, 100)
+
+
+def test_i64_ops_against_numpy_bits():
+    """64-bit compaction and selection against numpy's bit arithmetic on the
+    unsigned view, for bits on both sides of the 32-bit boundary; values in
+    int32 range with bits below 31 agree with the (pinned) int32 oracle."""
+    rng = np.random.default_rng(8)
+    x = rng.integers(-2**63, 2**63 - 1, 25_000, dtype=np.int64, endpoint=True)
+    x[:5] = [-2**63, -1, 0, 2**63 - 1, 2**32]
+    u = x.view(np.uint64)
+    cases = [(oracle.PRED_NONZERO, 0, x != 0), (oracle.PRED_ODD, 0, (u & 1) == 1),
+             (oracle.PRED_EVEN, 0, (u & 1) == 0)]
+    for b in (0, 5, 31, 32, 33, 47, 62, 63):
+        cases.append((oracle.PRED_BIT_SET, b, ((u >> np.uint64(b)) & 1) == 1))
+        cases.append((oracle.PRED_BIT_CLEAR, b, ((u >> np.uint64(b)) & 1) == 0))
+    for pred, b, mask in cases:
+        surv, m = oracle.compact_i64(x, pred, b)
+        assert m == int(mask.sum()) and np.array_equal(surv, x[mask])
+        idx, mi = oracle.select_index_i64(x, pred, b)
+        assert mi == m and np.array_equal(idx, np.flatnonzero(mask))
+    small = rng.integers(-2**31, 2**31, 5_000, dtype=np.int64)
+    for pred, b in [(oracle.PRED_ODD, 0), (oracle.PRED_BIT_SET, 7), (oracle.PRED_BIT_CLEAR, 30)]:
+        assert np.array_equal(oracle.compact_i64(small, pred, b)[0],
+                              oracle.compact_i32(small.astype(np.int32), pred, b)[0])
+
+
 # --- the checkers themselves fail on planted mistakes ---------------------------
 
 def test_checkers_catch_planted_mistakes():
