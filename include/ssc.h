@@ -98,7 +98,9 @@ int64_t ssc_tile_elems(void);
 
 /* Scratch bytes needed by the scan, compaction, partition and counting calls
  * for n elements: a 512-byte header (tile counter and epoch, counting-pass
- * accumulators) plus 16 bytes of look-back descriptors per tile. */
+ * accumulators) plus 16 bytes of look-back descriptors per ssc_tile_elems()
+ * elements (one 8-byte descriptor per tile; the fp32 scans use two, the
+ * key-value and 64-bit compactions have tiles of half the size). */
 size_t ssc_scratch_bytes(int64_t n);
 
 /* Scratch bytes needed by ssc_radix_sort_u32 for n keys. */
@@ -191,6 +193,60 @@ int ssc_partition_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int3
 /* ssc_partition_i32 for fp32 arrays with an fp32 predicate (6..9). */
 int ssc_partition_f32(const float *in, float *out, int64_t n, int pred, float a, float b,
                       int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
+
+/* Compaction by a caller's own predicate, given as one flag byte per
+ * element: out[0 .. count) = the 32-bit elements in[i] (int32, fp32 or any
+ * 4-byte type, moved bit for bit) whose flags[i] is nonzero, in input
+ * order; *count = their number; out[count .. n) is not written. Same single
+ * pass as ssc_compact_i32, the flags read in place of a predicate.
+ * flags must be 4-byte aligned: the library reads it in 32-bit words,
+ * including the whole word that holds flags[n - 1] (never past that word).
+ * No overlap between in, flags, out and count is allowed.
+ * Source: "Day 33 compaction.cu" (the predicate is the only part that
+ * changes; everything after it reads an array of ones and zeros). */
+int ssc_compact_flags_b32(const void *in, const uint8_t *flags, void *out, int64_t n,
+                          int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
+
+/* Positions of the nonzero flag bytes: idx[0 .. count) = the i, increasing,
+ * with flags[i] != 0; *count = their number (the flag-byte form of
+ * ssc_select_index_i32; same alignment rule for flags). No overlap between
+ * flags, idx and count is allowed. Source: as ssc_compact_flags_b32. */
+int ssc_select_flags(const uint8_t *flags, int32_t *idx, int64_t n, int32_t *count,
+                     void *scratch, size_t scratch_bytes, void *stream);
+
+/* Key-value compaction: the pairs (keys[i], vals[i]) whose key satisfies the
+ * predicate (pred 0..5 with pa, pb as in ssc_compact_i32), in input order:
+ * keys_out[0 .. count) and vals_out[0 .. count) hold the same positions;
+ * *count = their number. Values are 4-byte words moved bit for bit. One
+ * single pass over both arrays (1024 pairs per wavefront and tile). No
+ * overlap between any two of keys, vals, keys_out, vals_out and count.
+ * Source: the element-type template of "CUDA Handbook ch. 13, Stream
+ * Compaction", with a value carried beside each kept key. */
+int ssc_compact_kv_i32(const int32_t *keys, const void *vals, int32_t *keys_out, void *vals_out,
+                       int64_t n, int pred, int32_t pa, int32_t pb, int32_t *count,
+                       void *scratch, size_t scratch_bytes, void *stream);
+
+/* ssc_compact_kv_i32 with fp32 keys and an fp32 predicate (6..9). */
+int ssc_compact_kv_f32(const float *keys, const void *vals, float *keys_out, void *vals_out,
+                       int64_t n, int pred, float a, float b, int32_t *count, void *scratch,
+                       size_t scratch_bytes, void *stream);
+
+/* Compaction of 64-bit elements (int64 or uint64 bits): out[0 .. count) =
+ * the elements with P true in input order; *count = their number. P is
+ * NONZERO, ODD, EVEN, BIT_SET or BIT_CLEAR on the 64 bits of the value, the
+ * bit 0..63 given in `bit`; MOD_LT and the fp32 predicates give
+ * SSC_ERR_ARG. in and out must be 8-byte aligned. One single pass (1024
+ * elements per wavefront and tile). No overlap between in, out and count.
+ * Source: "CUDA Handbook ch. 13, Stream Compaction" (Listing 13-17 is a
+ * template over the element type; isOdd is x & 1). */
+int ssc_compact_i64(const int64_t *in, int64_t *out, int64_t n, int pred, int32_t bit,
+                    int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
+
+/* Selection over 64-bit elements: idx[0 .. count) = the positions i with
+ * P(in[i]) true (predicates as ssc_compact_i64). No overlap between in, idx
+ * and count. */
+int ssc_select_index_i64(const int64_t *in, int32_t *idx, int64_t n, int pred, int32_t bit,
+                         int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
 
 /* *count = number of elements with P true (a reduction of the flags; one
  * launch). Needs a scratch buffer of at least ssc_scratch_bytes(0) bytes. */

@@ -55,6 +55,12 @@ SIGNATURES = {
     "ssc_exclusive_scan_multipass_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_compact_multipass_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "ssc_copy_i32": (_INT, [_P, _P, _I64, _P]),
+    "ssc_compact_flags_b32": (_INT, [_P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_select_flags": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "ssc_compact_kv_i32": (_INT, [_P, _P, _P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
+    "ssc_compact_kv_f32": (_INT, [_P, _P, _P, _P, _I64, _INT, _F32, _F32, _P, _P, _SZ, _P]),
+    "ssc_compact_i64": (_INT, [_P, _P, _I64, _INT, _I32, _P, _P, _SZ, _P]),
+    "ssc_select_index_i64": (_INT, [_P, _P, _I64, _INT, _I32, _P, _P, _SZ, _P]),
     "ssc_status_str": (ctypes.c_char_p, [_INT]),
     "ssc_last_hip_error": (_INT, []),
 }
@@ -208,15 +214,22 @@ def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
             out: torch.Tensor | None = None, count: torch.Tensor | None = None,
             ranks=False, scratch: torch.Tensor | None = None):
     """(out, count[, ranks]): order-preserving compaction of int32 values
-    (predicates 0..5, int arguments pa, pb) or float32 values (predicates
-    "f32_*", float thresholds pa, pb).
+    (predicates 0..5, int arguments pa, pb), float32 values (predicates
+    "f32_*", float thresholds pa, pb) or int64 values (nonzero, odd, even,
+    bit_set, bit_clear; the bit 0..63 in pa).
 
     out[:count] holds the survivors; entries past count are not written.
-    ranks=True (or a tensor) also returns the exclusive scan of the flags.
+    ranks=True (or a tensor) also returns the exclusive scan of the flags
+    (32-bit elements only).
     """
     _dev(x)
-    fn = _typed(x, "compact")
     n = x.numel()
+    if x.dtype == torch.int64:
+        if ranks is not False:
+            raise ValueError("ranks are for 32-bit elements")
+        return _i64_op("ssc_compact_i64", x, pred, pa, torch.empty_like(x) if out is None else out,
+                       count, scratch)
+    fn = _typed(x, "compact")
     if out is None:
         out = torch.empty_like(x)
     if count is None:
@@ -238,10 +251,14 @@ def select_index(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
                  out: torch.Tensor | None = None, count: torch.Tensor | None = None,
                  scratch: torch.Tensor | None = None):
     """(idx, count): idx[:count] holds the positions of the elements for which
-    the predicate holds, increasing; entries past count are not written."""
+    the predicate holds, increasing; entries past count are not written.
+    int64 values take nonzero, odd, even, bit_set and bit_clear (bit in pa)."""
     _dev(x)
-    fn = _typed(x, "select_index")
     n = x.numel()
+    if x.dtype == torch.int64:
+        idx = torch.empty(n, dtype=torch.int32, device=x.device) if out is None else out
+        return _i64_op("ssc_select_index_i64", x, pred, pa, idx, count, scratch)
+    fn = _typed(x, "select_index")
     if out is None:
         out = torch.empty(n, dtype=torch.int32, device=x.device)
     if count is None:
@@ -393,3 +410,92 @@ def copy(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         out = torch.empty_like(x)
     _call("ssc_copy_i32", lib().ssc_copy_i32, x.data_ptr(), out.data_ptr(), x.numel(), _stream(x))
     return out
+
+
+def _i64_op(fn: str, x: torch.Tensor, pred, bit: int, out: torch.Tensor,
+            count: torch.Tensor | None, scratch: torch.Tensor | None):
+    n = x.numel()
+    _dev(out)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if scratch is None:
+        scratch = new_scratch(n, x.device)
+    _call(fn, getattr(lib(), fn), x.data_ptr(), out.data_ptr(), n, _pred(pred), bit,
+          count.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(x))
+    return out, count
+
+
+def _flag_bytes(flags: torch.Tensor) -> torch.Tensor:
+    _dev(flags)
+    if flags.dtype == torch.bool:
+        return flags.view(torch.uint8)
+    if flags.dtype not in (torch.uint8, torch.int8):
+        raise TypeError("flags are one byte per element (bool, uint8 or int8)")
+    return flags
+
+
+def compact_flags(x: torch.Tensor, flags: torch.Tensor, *, out: torch.Tensor | None = None,
+                  count: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """(out, count): the 32-bit elements of x (any 4-byte dtype, moved bit for
+    bit) whose flag byte is nonzero, in input order -- compaction by a
+    predicate the caller has already evaluated (e.g. a torch.bool mask).
+    flags must start 4-byte aligned; out[count:] is not written."""
+    _dev(x)
+    if x.element_size() != 4:
+        raise TypeError("compact_flags takes 4-byte elements")
+    fb = _flag_bytes(flags)
+    n = x.numel()
+    if fb.numel() != n:
+        raise ValueError("one flag byte per element")
+    if out is None:
+        out = torch.empty_like(x)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if scratch is None:
+        scratch = new_scratch(n, x.device)
+    _call("ssc_compact_flags_b32", lib().ssc_compact_flags_b32, x.data_ptr(), fb.data_ptr(),
+          out.data_ptr(), n, count.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(x))
+    return out, count
+
+
+def select_flags(flags: torch.Tensor, *, out: torch.Tensor | None = None,
+                 count: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """(idx, count): positions of the nonzero flag bytes, increasing (the
+    one-pass form of torch.nonzero on a bool mask)."""
+    fb = _flag_bytes(flags)
+    n = fb.numel()
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=fb.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=fb.device)
+    if scratch is None:
+        scratch = new_scratch(n, fb.device)
+    _call("ssc_select_flags", lib().ssc_select_flags, fb.data_ptr(), out.data_ptr(), n,
+          count.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(fb))
+    return out, count
+
+
+def compact_kv(keys: torch.Tensor, vals: torch.Tensor, pred="nonzero", pa=0, pb=0, *,
+               keys_out: torch.Tensor | None = None, vals_out: torch.Tensor | None = None,
+               count: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
+    """(keys_out, vals_out, count): the pairs whose key satisfies the
+    predicate, in input order. int32 keys take predicates 0..5, float32 keys
+    the "f32_*" ones; values are any 4-byte dtype, moved bit for bit."""
+    _dev(keys)
+    _dev(vals)
+    if vals.element_size() != 4 or vals.numel() != keys.numel():
+        raise ValueError("one 4-byte value per key")
+    fn = _typed(keys, "compact_kv")
+    n = keys.numel()
+    if keys_out is None:
+        keys_out = torch.empty_like(keys)
+    if vals_out is None:
+        vals_out = torch.empty_like(vals)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=keys.device)
+    if scratch is None:
+        scratch = new_scratch(n, keys.device)
+    _call(fn, getattr(lib(), fn), keys.data_ptr(), vals.data_ptr(), keys_out.data_ptr(),
+          vals_out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), scratch.data_ptr(),
+          scratch.numel(), _stream(keys))
+    return keys_out, vals_out, count

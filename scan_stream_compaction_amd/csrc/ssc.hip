@@ -82,6 +82,7 @@ __host__ __device__ constexpr int64_t tiles_for(int64_t n) { return (n + kTile -
 
 // Four 32-bit lanes moved by one 128-bit global load or store.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 32-bit reinterpretation through a scalar value (bit_cast of a vector
 // element lvalue is avoided: it does not read the element it names).
@@ -361,33 +362,45 @@ __device__ __forceinline__ void arrive_and_publish(uint32_t *s_arrive, const uin
 // straddles the end keeps its in-range dwords). Partial chunks and
 // variable-length runs then need no branches, and every wavefront issues the
 // same memory instructions on every tile.
-constexpr int kSelLoads = 8;                       // 128-bit loads per data lane per tile
-constexpr int kSelChunk = kWave * kSelLoads * 4;   // 2048 elements per data wavefront
-static_assert(kDataWaves * kSelChunk == kTile, "a tile is one chunk per data wavefront");
-static_assert(kSelLoads * 4 <= 32, "a chunk's flags fit a 32-bit lane mask");
 constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, no swizzle
 constexpr int kNT = 2;                  // nontemporal cache policy
+constexpr int kStageWords = 2048;       // LDS staging words per data wavefront (8 KiB)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), static_cast<short>(0),
                                              static_cast<int>(bytes), kRsrcWord3);
 }
 
-__device__ __forceinline__ uint32_t sel_chunk_rem(int64_t n, int64_t chunk) {
+// The shape of one data wavefront's chunk: L loads per lane of K elements
+// each. Element (j, lane, k) is element j*64*K + lane*K + k of the chunk and
+// bit j*K + k of the lane's 32-bit flag mask; a tile is one chunk per data
+// wavefront.
+template <int L, int K>
+struct ChunkShape {
+    static constexpr int kLoads = L;
+    static constexpr int kPer = K;
+    static constexpr int kChunk = kWave * L * K;
+    static constexpr int kTileElems = kDataWaves * kChunk;
+    static_assert(L * K <= 32, "a lane's flags fit one 32-bit mask");
+    static_assert(K <= 4, "a load's flag count fits the packed 10-bit fields");
+};
+
+template <int C>
+__device__ __forceinline__ uint32_t chunk_rem(int64_t n, int64_t chunk) {
     const int64_t r = n - chunk;
-    return r <= 0 ? 0u : (r >= kSelChunk ? static_cast<uint32_t>(kSelChunk) : static_cast<uint32_t>(r));
+    return r <= 0 ? 0u : (r >= C ? static_cast<uint32_t>(C) : static_cast<uint32_t>(r));
 }
 
-// Loads a chunk (rem valid elements) in the (j, lane, k) layout: element
-// j*256 + lane*4 + k; missing elements read as 0. VEC: eight 128-bit loads
-// per lane, else 32 loads of 32 bits. Nontemporal: every byte is read once.
-template <bool VEC>
-__device__ __forceinline__ void load_chunk_rsrc(const int32_t *in, int64_t chunk, uint32_t rem,
-                                                int lane, int32_t (&v)[kSelLoads][4]) {
+// Loads L x 4 32-bit elements per lane (rem valid in the chunk) in the
+// (j, lane, k) layout; missing elements read as 0. VEC: 128-bit loads, else
+// 32-bit ones. Nontemporal: every byte is read once.
+template <int L, bool VEC>
+__device__ __forceinline__ void load_b32x4(const int32_t *in, int64_t chunk, uint32_t rem,
+                                           int lane, int32_t (&v)[L][4]) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(in + chunk, rem * 4u);
     const int lane_off = lane * 16;
 #pragma unroll
-    for (int j = 0; j < kSelLoads; ++j) {
+    for (int j = 0; j < L; ++j) {
         if constexpr (VEC) {
             const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, j * (kWave * 16) + lane_off, 0, kNT);
 #pragma unroll
@@ -401,51 +414,74 @@ __device__ __forceinline__ void load_chunk_rsrc(const int32_t *in, int64_t chunk
     }
 }
 
-// Writes run[0 .. len) (LDS) to out[at .. at + len) with kSelChunk / 64
-// stores per lane whatever len is: slots past len fall outside the resource
-// and are dropped, so up to kSelChunk - 1 slots past the run are read (the
+// Writes run[0 .. len) (LDS words) to out[at .. at + len) with C / 64
+// 32-bit stores per lane whatever len is: slots past len fall outside the
+// resource and are dropped, so up to C - 1 words past the run are read (the
 // staging array is padded for that). The run is also cut at n: a correct
 // look-back never needs it, a broken one then gives wrong results instead of
 // stray writes. Default cache policy (measured faster than nontemporal for
-// these 4-byte runs).
-__device__ __forceinline__ void stream_run(const int32_t *run, int32_t *out, uint32_t at,
+// these runs).
+template <int C>
+__device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, uint32_t at,
                                            uint32_t len, int64_t n, int lane) {
     len = uniform(len);
     const int64_t room = n - static_cast<int64_t>(at);
     if (static_cast<int64_t>(len) > room) len = room > 0 ? static_cast<uint32_t>(room) : 0u;
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(out + at, len * 4u);
-    const int32_t *src = run + lane;
+    const uint32_t *src = run + lane;
     const int voff = lane * 4;
 #pragma unroll
-    for (int i = 0; i < kSelChunk / kWave; ++i)
+    for (int i = 0; i < C / kWave; ++i)
         __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], r, voff + i * (kWave * 4), 0, 0);
 }
 
-// Bits of the valid elements (j*256 + lane*4 + k < rem) in the layout of a
+// As stream_run for 64-bit elements (C / 64 64-bit stores per lane).
+template <int C>
+__device__ __forceinline__ void stream_run64(const uint64_t *run, uint64_t *out, uint32_t at,
+                                             uint32_t len, int64_t n, int lane) {
+    len = uniform(len);
+    const int64_t room = n - static_cast<int64_t>(at);
+    if (static_cast<int64_t>(len) > room) len = room > 0 ? static_cast<uint32_t>(room) : 0u;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(out + at, len * 8u);
+    const uint64_t *src = run + lane;
+    const int voff = lane * 8;
+#pragma unroll
+    for (int i = 0; i < C / kWave; ++i) {
+        const uint64_t x = src[i * kWave];
+        u32x2 d;
+        d[0] = static_cast<uint32_t>(x);
+        d[1] = static_cast<uint32_t>(x >> 32);
+        __builtin_amdgcn_raw_buffer_store_b64(d, r, voff + i * (kWave * 8), 0, 0);
+    }
+}
+
+// Bits of the valid elements (j*64*K + lane*K + k < rem) in the layout of a
 // chunk's flag mask.
+template <int L, int K>
 __device__ __forceinline__ uint32_t valid_mask(int lane, uint32_t rem) {
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < kSelLoads; ++j) {
-        int left = static_cast<int>(rem) - (j * (kWave * 4) + lane * 4);
-        left = left < 0 ? 0 : (left > 4 ? 4 : left);
-        m |= ((1u << left) - 1u) << (j * 4);
+    for (int j = 0; j < L; ++j) {
+        int left = static_cast<int>(rem) - (j * (kWave * K) + lane * K);
+        left = left < 0 ? 0 : (left > K ? K : left);
+        m |= ((1u << left) - 1u) << (j * K);
     }
     return m;
 }
 
-// Flags of one chunk as a per-lane mask: bit j*4 + k is the predicate of
-// element (j, lane, k), evaluated once; elements past rem are not flagged.
-template <int P>
-__device__ __forceinline__ uint32_t chunk_mask(const int32_t (&v)[kSelLoads][4], int lane,
-                                               uint32_t rem, const PredArgs &pr) {
+// Flags of L x 4 32-bit elements as a per-lane mask: bit j*4 + k is the
+// predicate of element (j, lane, k), evaluated once; elements past rem are
+// not flagged.
+template <int P, int L>
+__device__ __forceinline__ uint32_t mask_b32(const int32_t (&v)[L][4], int lane, uint32_t rem,
+                                             const PredArgs &pr) {
     uint32_t mask = 0;
 #pragma unroll
-    for (int j = 0; j < kSelLoads; ++j)
+    for (int j = 0; j < L; ++j)
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             mask |= static_cast<uint32_t>(pred_eval<P>(v[j][k], pr)) << (j * 4 + k);
-    if (rem < static_cast<uint32_t>(kSelChunk)) mask &= valid_mask(lane, rem);
+    if (rem < static_cast<uint32_t>(kWave * L * 4)) mask &= valid_mask<L, 4>(lane, rem);
     return mask;
 }
 
@@ -457,15 +493,17 @@ __device__ __forceinline__ uint32_t chunk_total(uint32_t mask) {
 
 // lead[j] = flagged elements of the chunk before element (j, lane, 0): the
 // flags of loads before j plus those of load j in lower lanes. A lane's
-// eight per-load counts (0..4 each) travel as three words of 10-bit fields,
-// so three wavefront scans rank all eight loads at once (a field's sum over
+// per-load counts (0..K each) travel as words of three 10-bit fields, so
+// ceil(L / 3) wavefront scans rank all L loads at once (a field's sum over
 // 64 lanes is at most 256). Returns the chunk total (uniform).
-__device__ __forceinline__ uint32_t chunk_leads(uint32_t mask, uint32_t (&lead)[kSelLoads]) {
-    constexpr int kWords = (kSelLoads + 2) / 3;
+template <int L, int K>
+__device__ __forceinline__ uint32_t chunk_leads(uint32_t mask, uint32_t (&lead)[L]) {
+    constexpr int kWords = (L + 2) / 3;
+    constexpr uint32_t kLoadBits = (1u << K) - 1u;
     uint32_t word[kWords] = {};
 #pragma unroll
-    for (int j = 0; j < kSelLoads; ++j)
-        word[j / 3] |= static_cast<uint32_t>(__builtin_popcount((mask >> (j * 4)) & 15u))
+    for (int j = 0; j < L; ++j)
+        word[j / 3] |= static_cast<uint32_t>(__builtin_popcount((mask >> (j * K)) & kLoadBits))
                        << (10 * (j % 3));
     uint32_t excl[kWords], tot[kWords];
 #pragma unroll
@@ -476,7 +514,7 @@ __device__ __forceinline__ uint32_t chunk_leads(uint32_t mask, uint32_t (&lead)[
     }
     uint32_t running = 0;
 #pragma unroll
-    for (int j = 0; j < kSelLoads; ++j) {
+    for (int j = 0; j < L; ++j) {
         const int sh = 10 * (j % 3);
         lead[j] = running + ((excl[j / 3] >> sh) & 1023u);
         running += (tot[j / 3] >> sh) & 1023u;
@@ -485,15 +523,15 @@ __device__ __forceinline__ uint32_t chunk_leads(uint32_t mask, uint32_t (&lead)[
 }
 
 // ranks[i] = seg + (flags before element i in its chunk) for the chunk's rem
-// valid elements, written in the load layout.
-template <bool VEC>
+// valid elements, written in the load layout of L x 4 32-bit elements.
+template <int L, bool VEC>
 __device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint32_t rem,
                                             uint32_t seg, uint32_t mask, int lane) {
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(ranks + chunk, rem * 4u);
-    uint32_t lead[kSelLoads];
-    chunk_leads(mask, lead);
+    uint32_t lead[L];
+    chunk_leads<L, 4>(mask, lead);
 #pragma unroll
-    for (int j = 0; j < kSelLoads; ++j) {
+    for (int j = 0; j < L; ++j) {
         uint32_t x = seg + lead[j];
         uint32_t q[4];
 #pragma unroll
@@ -517,13 +555,193 @@ __device__ __forceinline__ void write_ranks(int32_t *ranks, int64_t chunk, uint3
     }
 }
 
+// ------------------------------------------------- element formats ---
+// What a chunk is made of, for the persistent kernel below: how its loads
+// are issued, how an element's flag is taken, and how a survivor is staged
+// in the data wavefront's 8 KiB LDS region and written out. The kernel's
+// pipeline (claims, arrivals, look-back, barrier) is the same for all.
+
+// Arrays the kernel reads and writes; which ones a format uses is its own.
+struct SelArgs {
+    const void *in;   // elements (the keys of key-value pairs)
+    const void *aux;  // flag bytes (flag formats) or the values of pairs
+    void *out;        // compacted elements or keys, or the survivors' positions
+    void *out_aux;    // compacted values of pairs
+};
+
+// 32-bit elements (int32, or fp32 bits); the predicate reads the element.
+// Eight 128-bit loads per lane: 2048 elements per data wavefront.
+template <bool VEC>
+struct FmtB32 {
+    using Shape = ChunkShape<8, 4>;
+    static constexpr bool kVec = VEC;
+    struct Regs {
+        int32_t v[8][4];
+    };
+    __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
+        load_b32x4<8, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.v);
+    }
+    template <int P>
+    __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &pr) {
+        return mask_b32<P, 8>(r.v, lane, rem, pr);
+    }
+    __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
+        region[slot] = static_cast<uint32_t>(r.v[j][k]);
+    }
+    __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
+                                 uint32_t len, int64_t n, int lane) {
+        stream_run<Shape::kChunk>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+    }
+};
+
+// A caller's predicate as one flag byte per element (nonzero keeps), with
+// 32-bit elements (VALUES) or without them (selection: positions only).
+// The flags of load j arrive as one 32-bit load per lane, four bytes for the
+// lane's four elements; the array must be 4-byte aligned, and the word that
+// holds the last flag is read whole (never anything past that word).
+template <bool VEC, bool VALUES>
+struct FmtFlags {
+    using Shape = ChunkShape<8, 4>;
+    static constexpr bool kVec = VEC;
+    struct Regs {
+        int32_t v[8][4];
+        uint32_t f[8];
+    };
+    __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
+        if constexpr (VALUES)
+            load_b32x4<8, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.v);
+        const __amdgpu_buffer_rsrc_t fr =
+            buffer_rsrc(static_cast<const uint8_t *>(a.aux) + chunk, (rem + 3u) & ~3u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            r.f[j] = __builtin_amdgcn_raw_buffer_load_b32(fr, j * (kWave * 4) + lane * 4, 0, kNT);
+    }
+    template <int P>
+    __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &) {
+        uint32_t mask = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                mask |= static_cast<uint32_t>(((r.f[j] >> (8 * k)) & 0xFFu) != 0u) << (j * 4 + k);
+        if (rem < static_cast<uint32_t>(Shape::kChunk)) mask &= valid_mask<8, 4>(lane, rem);
+        return mask;
+    }
+    __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
+        region[slot] = static_cast<uint32_t>(r.v[j][k]);
+    }
+    __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
+                                 uint32_t len, int64_t n, int lane) {
+        stream_run<Shape::kChunk>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+    }
+};
+
+// Key-value pairs: 32-bit keys (the predicate reads them) and 32-bit values
+// that travel with them. Four 128-bit loads per lane of each array: 1024
+// pairs per data wavefront, keys staged in the first half of the region and
+// values in the second.
+template <bool VEC>
+struct FmtPairs {
+    using Shape = ChunkShape<4, 4>;
+    static constexpr bool kVec = VEC;
+    struct Regs {
+        int32_t k[4][4];
+        int32_t v[4][4];
+    };
+    __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
+        load_b32x4<4, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.k);
+        load_b32x4<4, VEC>(static_cast<const int32_t *>(a.aux), chunk, rem, lane, r.v);
+    }
+    template <int P>
+    __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &pr) {
+        return mask_b32<P, 4>(r.k, lane, rem, pr);
+    }
+    __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
+        region[slot] = static_cast<uint32_t>(r.k[j][k]);
+        region[Shape::kChunk + slot] = static_cast<uint32_t>(r.v[j][k]);
+    }
+    __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
+                                 uint32_t len, int64_t n, int lane) {
+        stream_run<Shape::kChunk>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+        stream_run<Shape::kChunk>(region + Shape::kChunk, static_cast<uint32_t *>(a.out_aux), at,
+                                  len, n, lane);
+    }
+};
+
+// The predicates on a 64-bit element's two's-complement bits: nonzero, odd,
+// even, bit pa (0..63) set or clear.
+template <int P>
+__device__ __forceinline__ bool pred_eval64(uint64_t u, const PredArgs &pr) {
+    if constexpr (P == 0) {
+        return u != 0u;
+    } else if constexpr (P == 1) {
+        return (u & 1u) != 0u;
+    } else if constexpr (P == 2) {
+        return (u & 1u) == 0u;
+    } else if constexpr (P == 3) {
+        return ((u >> pr.a) & 1u) != 0u;
+    } else {
+        static_assert(P == 4, "64-bit predicates: nonzero, odd, even, bit set, bit clear");
+        return ((u >> pr.a) & 1u) == 0u;
+    }
+}
+
+// 64-bit elements: eight 128-bit loads per lane of two elements each, 1024
+// elements per data wavefront (8-byte aligned arrays take 64-bit loads).
+template <bool VEC>
+struct FmtB64 {
+    using Shape = ChunkShape<8, 2>;
+    static constexpr bool kVec = VEC;
+    struct Regs {
+        uint64_t v[8][2];
+    };
+    __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc(static_cast<const uint64_t *>(a.in) + chunk, rem * 8u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int off = j * (kWave * 16) + lane * 16;
+            if constexpr (VEC) {
+                const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
+                r.v[j][0] = static_cast<uint64_t>(q[0]) | (static_cast<uint64_t>(q[1]) << 32);
+                r.v[j][1] = static_cast<uint64_t>(q[2]) | (static_cast<uint64_t>(q[3]) << 32);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8 * k, 0, kNT);
+                    r.v[j][k] = static_cast<uint64_t>(d[0]) | (static_cast<uint64_t>(d[1]) << 32);
+                }
+            }
+        }
+    }
+    template <int P>
+    __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &pr) {
+        uint32_t mask = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                mask |= static_cast<uint32_t>(pred_eval64<P>(r.v[j][k], pr)) << (j * 2 + k);
+        if (rem < static_cast<uint32_t>(Shape::kChunk)) mask &= valid_mask<8, 2>(lane, rem);
+        return mask;
+    }
+    __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
+        reinterpret_cast<uint64_t *>(region)[slot] = r.v[j][k];
+    }
+    __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
+                                 uint32_t len, int64_t n, int lane) {
+        stream_run64<Shape::kChunk>(reinterpret_cast<const uint64_t *>(region),
+                                    static_cast<uint64_t *>(a.out), at, len, n, lane);
+    }
+};
+
 // ===================================================== compaction kernel ---
 // Persistent form: one 1024-thread workgroup per compute unit (its LDS and
-// 128 VGPRs per lane fill the unit) loops over tiles of 30720 elements whose
-// numbers come from the atomic counter, claimed three ahead (the second and
-// third with one atomic, while the first is loading). A tile is one
-// chunk of 2048 elements (eight 128-bit loads per lane) for each of the 15
-// data wavefronts; the 16th is the control wavefront.
+// 128 VGPRs per lane fill the unit) loops over tiles whose numbers come from
+// the atomic counter, claimed three ahead (the second and third with one
+// atomic, while the first is loading). A tile is one chunk for each of the
+// 15 data wavefronts (for 32-bit elements 2048 of them, eight 128-bit loads
+// per lane: 30720 per tile); the 16th is the control wavefront.
 //
 // Per tile, a data wavefront holds two chunks in registers: the current
 // tile's, already flagged and ranked, and the next tile's, in flight. It
@@ -564,14 +782,18 @@ enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3 };
 constexpr int kSelPollSleep = 32;  // look-back poll interval, s_sleep units (measured)
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
-template <int P, bool VEC, int KIND>
+// F is the element format (what a chunk holds and how survivors are staged
+// and written); partition and ranks are defined for 32-bit elements.
+template <class F, int P, int KIND>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(
-    const int32_t *__restrict__ in, int32_t *__restrict__ out, int64_t n, PredArgs pr,
-    void *scratch, uint32_t num_tiles, uint32_t capacity,
+    SelArgs a, int64_t n, PredArgs pr, void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
     const int32_t *__restrict__ kept_total) {
+    using S = typename F::Shape;
+    static_assert(KIND == kCompact || KIND == kSelectIndex || __is_same(F, FmtB32<F::kVec>),
+                  "partition and ranks take 32-bit elements");
     // one staging region per data wavefront, plus one of padding for run reads
-    __shared__ int32_t s_stage[kDataWaves + 1][kSelChunk];
+    __shared__ __attribute__((aligned(16))) uint32_t s_stage[kDataWaves + 1][kStageWords];
     __shared__ uint32_t s_tot[kDataWaves];
     __shared__ uint32_t s_pre[3][kDataWaves + 1];  // chunk prefixes + aggregate, by tile mod 3
     __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
@@ -645,22 +867,24 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
 
     const uint32_t kept = KIND == kPartition ? static_cast<uint32_t>(*kept_total) : 0u;
-    int32_t va[kSelLoads][4], vb[kSelLoads][4];
+    typename F::Regs va, vb;
     uint32_t fm_cur = 0, fm_nxt = 0;  // flags of the current / next chunk
     uint32_t a_cur = 0, a_nxt = 0;    // their totals
     uint32_t rem_cur = 0, rem_nxt = 0;
     const auto chunk_of = [&](uint32_t t) {
-        return static_cast<int64_t>(t) * kTile + static_cast<int64_t>(w) * kSelChunk;
+        return static_cast<int64_t>(t) * S::kTileElems + static_cast<int64_t>(w) * S::kChunk;
     };
     // a tile past the end has no valid elements: its loads touch nothing
-    const auto rem_of = [&](uint32_t t) { return t < num_tiles ? sel_chunk_rem(n, chunk_of(t)) : 0u; };
+    const auto rem_of = [&](uint32_t t) {
+        return t < num_tiles ? chunk_rem<S::kChunk>(n, chunk_of(t)) : 0u;
+    };
 
     // Flags of chunk V (tile T, R valid) into FM and A, then the arrival: the
     // last data wavefront to arrive scans the 15 totals into s_pre[TRI] and
     // publishes T's {aggregate} ({inclusive} for tile 0).
 #define SSC_FLAG_AND_ARRIVE(V, T, R, FM, A, TRI, LN)                                          \
     {                                                                                         \
-        FM = chunk_mask<P>(V, LN, R, pr);                                                     \
+        FM = F::template flags<P>(V, LN, R, pr);                                              \
         A = chunk_total(FM);                                                                  \
         if (LN == 0) s_tot[w] = A;                                                            \
         uint32_t before_ = 0;                                                                 \
@@ -694,22 +918,26 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             /* every element gets a slot of its own, no branches: survivors at    */            \
             /* their rank, the others after all survivors at a_cur + (index -     */            \
             /* rank), elements past rem included (they land past the runs)        */            \
-            uint32_t lead[kSelLoads];                                                         \
-            chunk_leads(fm_cur, lead);                                                        \
+            uint32_t lead[S::kLoads];                                                         \
+            chunk_leads<S::kLoads, S::kPer>(fm_cur, lead);                                    \
             /* (a selection stages each element's index instead of its value)    */            \
-            const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * 4;              \
-            _Pragma("unroll") for (int j = 0; j < kSelLoads; ++j) {                           \
+            const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * S::kPer;        \
+            _Pragma("unroll") for (int j = 0; j < S::kLoads; ++j) {                           \
                 uint32_t r = lead[j];                                                         \
-                const uint32_t rej = a_cur + static_cast<uint32_t>(j * (kWave * 4) + ln * 4); \
-                _Pragma("unroll") for (int k = 0; k < 4; ++k) {                               \
-                    const uint32_t f = (fm_cur >> (j * 4 + k)) & 1u;                          \
-                    s_stage[w][f ? r : rej + k - r] =                                         \
-                        KIND == kSelectIndex ? first + (j * (kWave * 4) + k) : CUR[j][k];     \
+                const uint32_t rej =                                                          \
+                    a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);      \
+                _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                         \
+                    const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                    \
+                    const uint32_t slot = f ? r : rej + k - r;                                \
+                    if constexpr (KIND == kSelectIndex)                                       \
+                        s_stage[w][slot] = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
+                    else                                                                      \
+                        F::stage(s_stage[w], slot, CUR, j, k);                                \
                     r += f;                                                                   \
                 }                                                                             \
             }                                                                                 \
         }                                                                                     \
-        load_chunk_rsrc<VEC>(in, chunk_of(nxt2), rem_of(nxt2), ln, CUR);                      \
+        F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, CUR);                                    \
         const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                     \
         rem_nxt = rem_of(nxt);                                                                \
         SSC_FLAG_AND_ARRIVE(NX, nxt, rem_nxt, fm_nxt, a_nxt, tri_n, ln)                       \
@@ -718,14 +946,17 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         const uint32_t nxt3 = uniform(s_next[par]);                                           \
         const int64_t chunk_now = chunk_of(tile);                                             \
         const uint32_t seg = base + uniform(s_pre[tri][w]); /* kept before this chunk */      \
-        stream_run(s_stage[w], out, seg, a_cur, n, ln);                                       \
+        if constexpr (KIND == kSelectIndex)                                                   \
+            stream_run<S::kChunk>(s_stage[w], static_cast<uint32_t *>(a.out), seg, a_cur, n, ln); \
+        else                                                                                  \
+            F::write(s_stage[w], a, seg, a_cur, n, ln);                                       \
         if constexpr (KIND == kPartition) {                                                   \
             /* rejected before this chunk = elements before it - kept before it */            \
             const uint32_t rej = static_cast<uint32_t>(chunk_now) - seg;                      \
-            stream_run(s_stage[w] + a_cur, out, kept + rej, rem_cur - a_cur, n, ln);          \
+            F::write(s_stage[w] + a_cur, a, kept + rej, rem_cur - a_cur, n, ln);              \
         }                                                                                     \
         if constexpr (KIND == kCompactRanks)                                                  \
-            write_ranks<VEC>(ranks, chunk_now, rem_cur, seg, fm_cur, ln);                     \
+            write_ranks<S::kLoads, F::kVec>(ranks, chunk_now, rem_cur, seg, fm_cur, ln);      \
         /* advance on every path; the caller leaves once tile is past the end */              \
         tile = nxt;                                                                           \
         nxt = nxt2;                                                                           \
@@ -738,11 +969,11 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
 
     rem_cur = rem_of(tile);
-    load_chunk_rsrc<VEC>(in, chunk_of(tile), rem_cur, lane, va);
+    F::load(a, chunk_of(tile), rem_cur, lane, va);
     __syncthreads();  // B0b: the second and third tiles
     uint32_t nxt = uniform(s_first[1]);
     uint32_t nxt2 = uniform(s_first[2]);
-    load_chunk_rsrc<VEC>(in, chunk_of(nxt), rem_of(nxt), lane, vb);
+    F::load(a, chunk_of(nxt), rem_of(nxt), lane, vb);
     SSC_FLAG_AND_ARRIVE(va, tile, rem_cur, fm_cur, a_cur, tri, lane)
     // B0': without it a fast wavefront could arrive for the next tile
     // before a slow one has arrived for this one
@@ -1523,35 +1754,78 @@ int dispatch_pred(int pred, bool vec, A... a) {
     }
 }
 
+// One launch of the persistent kernel for element format F and kind KIND:
+// one workgroup per compute unit, at most one per tile.
+template <class F, int P, int KIND>
+int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint32_t capacity,
+                  int32_t *count, int32_t *ranks, const int32_t *kept, hipStream_t s) {
+    constexpr int64_t kTileElems = F::Shape::kTileElems;
+    const uint32_t tiles = static_cast<uint32_t>((n + kTileElems - 1) / kTileElems);
+    uint32_t slots = 0;
+    SSC_TRY(compute_units(&slots));
+    const dim3 grid(tiles < slots ? tiles : slots);
+    hipLaunchKernelGGL((select_kernel<F, P, KIND>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
+                       tiles, capacity, count, ranks, kept);
+    return launched();
+}
+
+// 32-bit elements, predicate P on the element.
 template <int P, bool VEC>
 struct LaunchSelect {
     static int run(int kind, const int32_t *in, int32_t *out, int64_t n, PredArgs pr,
                    void *scratch, uint32_t capacity, int32_t *count, int32_t *ranks,
                    const int32_t *kept, hipStream_t s) {
-        const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
-        uint32_t slots = 0;
-        SSC_TRY(compute_units(&slots));
-        const dim3 grid(tiles < slots ? tiles : slots);
+        using F = FmtB32<VEC>;
+        const SelArgs a{in, nullptr, out, nullptr};
         switch (kind) {
         case kPartition:
-            hipLaunchKernelGGL((select_kernel<P, VEC, kPartition>), grid, dim3(kLbBlock), 0, s, in,
-                               out, n, pr, scratch, tiles, capacity, count, ranks, kept);
-            break;
+            return launch_select<F, P, kPartition>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         case kCompactRanks:
-            hipLaunchKernelGGL((select_kernel<P, VEC, kCompactRanks>), grid, dim3(kLbBlock), 0, s,
-                               in, out, n, pr, scratch, tiles, capacity, count, ranks, kept);
-            break;
+            return launch_select<F, P, kCompactRanks>(a, n, pr, scratch, capacity, count, ranks,
+                                                      kept, s);
         case kSelectIndex:
-            hipLaunchKernelGGL((select_kernel<P, VEC, kSelectIndex>), grid, dim3(kLbBlock), 0, s,
-                               in, out, n, pr, scratch, tiles, capacity, count, ranks, kept);
-            break;
+            return launch_select<F, P, kSelectIndex>(a, n, pr, scratch, capacity, count, ranks,
+                                                     kept, s);
         default:
-            hipLaunchKernelGGL((select_kernel<P, VEC, kCompact>), grid, dim3(kLbBlock), 0, s, in,
-                               out, n, pr, scratch, tiles, capacity, count, ranks, kept);
+            return launch_select<F, P, kCompact>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         }
-        return launched();
     }
 };
+
+// Key-value pairs, predicate P on the key.
+template <int P, bool VEC>
+struct LaunchPairs {
+    static int run(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint32_t capacity,
+                   int32_t *count, hipStream_t s) {
+        return launch_select<FmtPairs<VEC>, P, kCompact>(a, n, pr, scratch, capacity, count,
+                                                         nullptr, nullptr, s);
+    }
+};
+
+// 64-bit elements, predicate P (0..4) on the element's bits.
+template <int P, bool VEC>
+struct LaunchSelect64 {
+    static int run(int kind, const SelArgs &a, int64_t n, PredArgs pr, void *scratch,
+                   uint32_t capacity, int32_t *count, hipStream_t s) {
+        if (kind == kSelectIndex)
+            return launch_select<FmtB64<VEC>, P, kSelectIndex>(a, n, pr, scratch, capacity, count,
+                                                               nullptr, nullptr, s);
+        return launch_select<FmtB64<VEC>, P, kCompact>(a, n, pr, scratch, capacity, count, nullptr,
+                                                       nullptr, s);
+    }
+};
+
+// The 64-bit predicates: nonzero, odd, even, bit set, bit clear.
+template <template <int, bool> class F, class... A>
+int dispatch_pred64(int pred, bool vec, A... a) {
+    switch (pred) {
+    case 0: return vec ? F<0, true>::run(a...) : F<0, false>::run(a...);
+    case 1: return vec ? F<1, true>::run(a...) : F<1, false>::run(a...);
+    case 2: return vec ? F<2, true>::run(a...) : F<2, false>::run(a...);
+    case 3: return vec ? F<3, true>::run(a...) : F<3, false>::run(a...);
+    default: return vec ? F<4, true>::run(a...) : F<4, false>::run(a...);
+    }
+}
 
 template <int P, bool VEC>
 struct LaunchCount {
@@ -1760,6 +2034,122 @@ int partition_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t
                                        static_cast<const int32_t *>(count), s);
 }
 
+// Arrays of one call with their byte extents: any two that overlap, or a
+// pointer below the required alignment, make the call fail.
+struct Span {
+    const void *p;
+    size_t bytes;
+};
+
+template <size_t N>
+bool spans_overlap(const Span (&a)[N]) {
+    for (size_t i = 0; i < N; ++i)
+        for (size_t j = i + 1; j < N; ++j)
+            if (overlap(a[i].p, a[i].bytes, a[j].p, a[j].bytes)) return true;
+    return false;
+}
+
+// The scratch checks of every persistent-kernel call: large enough, and
+// apart from each array of the call.
+template <size_t N>
+int check_scratch_apart(void *scratch, size_t scratch_bytes, int64_t n, const Span (&a)[N]) {
+    SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
+    for (size_t i = 0; i < N; ++i)
+        if (overlap(scratch, scratch_bytes, a[i].p, a[i].bytes)) return SSC_ERR_ALIAS;
+    return SSC_OK;
+}
+
+// Compaction or selection by flag bytes (values == nullptr: positions).
+int flags_impl(const void *in, const uint8_t *flags, void *out, int64_t n, int32_t *count,
+               void *scratch, size_t scratch_bytes, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool values = in != nullptr;
+    SSC_TRY(check_n(n));
+    if (count == nullptr || (n > 0 && (flags == nullptr || out == nullptr))) return SSC_ERR_ARG;
+    if (!aligned(flags, 4) || !aligned(out, 4) || !aligned(count, 4) || (values && !aligned(in, 4)))
+        return SSC_ERR_ARG;
+    const size_t words = static_cast<size_t>(n) * 4;
+    const Span arrays[] = {{flags, static_cast<size_t>(n)}, {out, words}, {count, 4},
+                           {in, values ? words : 0}};
+    if (spans_overlap(arrays)) return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch_apart(scratch, scratch_bytes, n, arrays));
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    const SelArgs a{in, flags, out, nullptr};
+    const PredArgs pr{0, 0, 0u, 0u, 0u, 0u};
+    const uint32_t cap = capacity_of(scratch_bytes);
+    if (!values)
+        return launch_select<FmtFlags<true, false>, 0, kSelectIndex>(a, n, pr, scratch, cap, count,
+                                                                     nullptr, nullptr, s);
+    if (aligned(in, 16))
+        return launch_select<FmtFlags<true, true>, 0, kCompact>(a, n, pr, scratch, cap, count,
+                                                                nullptr, nullptr, s);
+    return launch_select<FmtFlags<false, true>, 0, kCompact>(a, n, pr, scratch, cap, count,
+                                                             nullptr, nullptr, s);
+}
+
+template <bool F32>
+int kv_impl(const int32_t *keys, const void *vals, int32_t *keys_out, void *vals_out, int64_t n,
+            int pred, int32_t pa, int32_t pb, int32_t *count, void *scratch, size_t scratch_bytes,
+            void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (count == nullptr ||
+        (n > 0 && (keys == nullptr || vals == nullptr || keys_out == nullptr || vals_out == nullptr)))
+        return SSC_ERR_ARG;
+    SSC_TRY(F32 ? check_pred_f32(pred) : check_pred(pred, pa, pb));
+    if (!aligned(keys, 4) || !aligned(vals, 4) || !aligned(keys_out, 4) || !aligned(vals_out, 4) ||
+        !aligned(count, 4))
+        return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    const Span arrays[] = {{keys, bytes}, {vals, bytes}, {keys_out, bytes}, {vals_out, bytes},
+                           {count, 4}};
+    if (spans_overlap(arrays)) return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch_apart(scratch, scratch_bytes, n, arrays));
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    const bool vec = aligned(keys, 16) && aligned(vals, 16);
+    return dispatch_pred<LaunchPairs, F32>(pred, vec, SelArgs{keys, vals, keys_out, vals_out}, n,
+                                           make_pred_args(pred, pa, pb), scratch,
+                                           capacity_of(scratch_bytes), count, s);
+}
+
+int check_pred64(int pred, int32_t bit) {
+    switch (pred) {
+    case SSC_PRED_NONZERO:
+    case SSC_PRED_ODD:
+    case SSC_PRED_EVEN:
+        return SSC_OK;
+    case SSC_PRED_BIT_SET:
+    case SSC_PRED_BIT_CLEAR:
+        return (bit >= 0 && bit <= 63) ? SSC_OK : SSC_ERR_ARG;
+    default:
+        return SSC_ERR_ARG;
+    }
+}
+
+// Compaction (kind kCompact, out = elements) or selection (kSelectIndex,
+// out = int32 positions) of 64-bit elements.
+int i64_impl(int kind, const int64_t *in, void *out, int64_t n, int pred, int32_t bit,
+             int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(check_n(n));
+    if (count == nullptr || (n > 0 && (in == nullptr || out == nullptr))) return SSC_ERR_ARG;
+    SSC_TRY(check_pred64(pred, bit));
+    const size_t out_elem = kind == kSelectIndex ? 4 : 8;
+    if (!aligned(in, 8) || !aligned(out, out_elem) || !aligned(count, 4)) return SSC_ERR_ARG;
+    const Span arrays[] = {{in, static_cast<size_t>(n) * 8},
+                           {out, static_cast<size_t>(n) * out_elem}, {count, 4}};
+    if (spans_overlap(arrays)) return SSC_ERR_ALIAS;
+    SSC_TRY(check_scratch_apart(scratch, scratch_bytes, n, arrays));
+    SSC_TRY(check_device());
+    if (n == 0) return clear_words(count, 1, s);
+    return dispatch_pred64<LaunchSelect64>(pred, aligned(in, 16), kind,
+                                           SelArgs{in, nullptr, out, nullptr}, n,
+                                           make_pred_args(pred, bit, 0), scratch,
+                                           capacity_of(scratch_bytes), count, s);
+}
+
 }  // namespace
 
 // ======================================================================
@@ -1845,6 +2235,42 @@ int ssc_partition_f32(const float *in, float *out, int64_t n, int pred, float a,
     return partition_impl<true>(reinterpret_cast<const int32_t *>(in),
                                 reinterpret_cast<int32_t *>(out), n, pred, f32_bits(a), f32_bits(b),
                                 count, scratch, scratch_bytes, stream);
+}
+
+int ssc_compact_flags_b32(const void *in, const uint8_t *flags, void *out, int64_t n,
+                          int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    if (n > 0 && in == nullptr) return SSC_ERR_ARG;
+    return flags_impl(in, flags, out, n, count, scratch, scratch_bytes, stream);
+}
+
+int ssc_select_flags(const uint8_t *flags, int32_t *idx, int64_t n, int32_t *count,
+                     void *scratch, size_t scratch_bytes, void *stream) {
+    return flags_impl(nullptr, flags, idx, n, count, scratch, scratch_bytes, stream);
+}
+
+int ssc_compact_kv_i32(const int32_t *keys, const void *vals, int32_t *keys_out, void *vals_out,
+                       int64_t n, int pred, int32_t pa, int32_t pb, int32_t *count,
+                       void *scratch, size_t scratch_bytes, void *stream) {
+    return kv_impl<false>(keys, vals, keys_out, vals_out, n, pred, pa, pb, count, scratch,
+                          scratch_bytes, stream);
+}
+
+int ssc_compact_kv_f32(const float *keys, const void *vals, float *keys_out, void *vals_out,
+                       int64_t n, int pred, float a, float b, int32_t *count, void *scratch,
+                       size_t scratch_bytes, void *stream) {
+    return kv_impl<true>(reinterpret_cast<const int32_t *>(keys), vals,
+                         reinterpret_cast<int32_t *>(keys_out), vals_out, n, pred, f32_bits(a),
+                         f32_bits(b), count, scratch, scratch_bytes, stream);
+}
+
+int ssc_compact_i64(const int64_t *in, int64_t *out, int64_t n, int pred, int32_t bit,
+                    int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    return i64_impl(kCompact, in, out, n, pred, bit, count, scratch, scratch_bytes, stream);
+}
+
+int ssc_select_index_i64(const int64_t *in, int32_t *idx, int64_t n, int pred, int32_t bit,
+                         int32_t *count, void *scratch, size_t scratch_bytes, void *stream) {
+    return i64_impl(kSelectIndex, in, idx, n, pred, bit, count, scratch, scratch_bytes, stream);
 }
 
 int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t pb,

@@ -8,11 +8,15 @@ Generator: the splitmix64 output function (Steele, Lea and Flood, "Fast
 splittable pseudorandom number generators", OOPSLA 2014; Vigna's public-domain
 splitmix64.c) evaluated on a counter, so any element can be produced
 independently: ``z_i = mix64(seed + (i + 1) * 0x9E3779B97F4A7C15)``. Only the
-high 32 bits ``h`` of ``z_i`` are used. Derived values:
+high 32 bits ``h`` of ``z_i`` are used, except for 64-bit elements. Derived
+values:
 
 * uniform integer in ``[0, k)``: ``(h * k) >> 32``;
 * full-range int32: ``h`` reinterpreted as two's complement;
-* uniform fp32 in ``[0, 1)``: ``(h >> 8) * 2**-24`` (exact in fp32).
+* uniform fp32 in ``[0, 1)``: ``(h >> 8) * 2**-24`` (exact in fp32);
+* full-range int64: all 64 bits of ``z_i``;
+* flag bytes kept with probability p/100: ``0`` unless ``(h * 100) >> 32 < p``,
+  else ``(h >> 24) | 1`` (any nonzero byte, odd so never 0).
 
 The workloads follow the pages' own synthetic kinds: small uniform integers
 with zeros to remove ("Day 33 compaction.cu"; "CIS 565 Project 2", whose
@@ -60,6 +64,34 @@ def splitmix64(seed: int, n: int) -> np.ndarray:
         return z
 
 
+def _mix64(seed: int, start: int, count: int) -> np.ndarray:
+    """splitmix64 outputs start .. start+count-1 (uint64)."""
+    with np.errstate(over="ignore"):
+        i = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+        z = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + i * GOLDEN_GAMMA
+        z ^= z >> np.uint64(30)
+        z *= _M1
+        z ^= z >> np.uint64(27)
+        z *= _M2
+        z ^= z >> np.uint64(31)
+        return z
+
+
+def full_int64(seed: int, n: int, threads: int | None = None) -> np.ndarray:
+    """int64 values over the whole range: all 64 bits of each output."""
+    out = np.empty(n, np.uint64)
+    starts = range(0, n, _CHUNK)
+
+    def work(s):
+        c = min(_CHUNK, n - s)
+        out[s:s + c] = _mix64(seed, s, c)
+
+    workers = threads or min(8, os.cpu_count() or 1)
+    with _cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(work, starts))
+    return out.view(np.int64)
+
+
 def hi32(seed: int, n: int, threads: int | None = None) -> np.ndarray:
     """High 32 bits of the first n splitmix64 outputs for `seed`, as uint32."""
     out = np.empty(n, np.uint32)
@@ -97,6 +129,13 @@ def unit_float32(seed: int, n: int) -> np.ndarray:
     """fp32 values uniform in [0, 1): (h >> 8) * 2^-24, exactly representable."""
     h = hi32(seed, n)
     return ((h >> np.uint32(8)).astype(np.float32) * np.float32(2.0 ** -24)).astype(np.float32)
+
+
+def flag_bytes(seed: int, n: int, keep_pct: int) -> np.ndarray:
+    """uint8 flags, nonzero with probability keep_pct / 100 (values 1..255)."""
+    h = hi32(seed, n)
+    keep = ((h.astype(np.uint64) * np.uint64(100)) >> np.uint64(32)) < np.uint64(keep_pct)
+    return np.where(keep, (h >> np.uint32(24)) | np.uint32(1), np.uint32(0)).astype(np.uint8)
 
 
 def mod8_plus1(n: int) -> np.ndarray:

@@ -210,6 +210,49 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     assert L.ssc_copy_i32(A, B, -1, None) == ARG
 
 
+def test_flag_pair_and_64bit_argument_errors():
+    L = ssc.lib()
+    big = 1 << 20
+    D = 0x7F4000000000
+    # flag bytes: 4-byte aligned flags, no overlap, scratch sized
+    assert L.ssc_compact_flags_b32(A, B + 2, C, 100, D, S, big, None) == ARG
+    assert L.ssc_compact_flags_b32(None, B, C, 100, D, S, big, None) == ARG
+    assert L.ssc_compact_flags_b32(A, B, C, 100, None, S, big, None) == ARG
+    assert L.ssc_compact_flags_b32(A, A + 396, C, 100, D, S, big, None) == ALIAS  # flags inside in
+    assert L.ssc_compact_flags_b32(A, B, B + 96, 100, D, S, big, None) == ALIAS   # out over flags
+    assert L.ssc_compact_flags_b32(A, B, C, 100, D, S, 100, None) == SCRATCH
+    assert L.ssc_compact_flags_b32(A, B, C, 100, D, B, big, None) == ALIAS
+    assert L.ssc_compact_flags_b32(A, B, C, INT32_MAX + 1, D, S, big, None) == SIZE
+    assert L.ssc_select_flags(B, C, 100, C + 8, S, big, None) == ALIAS
+    assert L.ssc_select_flags(B + 1, C, 100, D, S, big, None) == ARG
+    assert L.ssc_select_flags(None, C, 100, D, S, big, None) == ARG
+    assert L.ssc_select_flags(B, C, -2, D, S, big, None) == ARG
+    # key-value: every pair of the four arrays and the count apart
+    assert L.ssc_compact_kv_i32(A, A + 200, C, D, 100, 1, 0, 0, S, S + 4096, big, None) == ALIAS
+    assert L.ssc_compact_kv_i32(A, B, C, C + 8, 100, 1, 0, 0, S, S + 4096, big, None) == ALIAS
+    assert L.ssc_compact_kv_i32(A, B, C, D, 100, 1, 0, 0, D + 12, S + 4096, big, None) == ALIAS
+    assert L.ssc_compact_kv_i32(A, B, C, D, 100, 6, 0, 0, S, S + 4096, big, None) == ARG
+    assert L.ssc_compact_kv_i32(A, B, C, D, 100, 3, 32, 0, S, S + 4096, big, None) == ARG
+    assert L.ssc_compact_kv_i32(A, B + 2, C, D, 100, 1, 0, 0, S, S + 4096, big, None) == ARG
+    assert L.ssc_compact_kv_i32(A, B, C, None, 100, 1, 0, 0, S, S + 4096, big, None) == ARG
+    assert L.ssc_compact_kv_i32(A, B, C, D, 100, 1, 0, 0, S, S + 4096, 100, None) == SCRATCH
+    for p in (0, 5, 10):
+        assert L.ssc_compact_kv_f32(A, B, C, D, 100, p, 0.0, 0.0, S, S + 4096, big, None) == ARG
+    # 64-bit elements: bits 0..63, no residue or fp32 predicates, 8-byte alignment
+    assert L.ssc_compact_i64(A, B, 100, 3, 64, C, S, big, None) == ARG
+    assert L.ssc_compact_i64(A, B, 100, 4, -1, C, S, big, None) == ARG
+    assert L.ssc_compact_i64(A, B, 100, 5, 100, C, S, big, None) == ARG
+    assert L.ssc_compact_i64(A, B, 100, 6, 0, C, S, big, None) == ARG
+    assert L.ssc_compact_i64(A + 4, B, 100, 1, 0, C, S, big, None) == ARG
+    assert L.ssc_compact_i64(A, B + 4, 100, 1, 0, C, S, big, None) == ARG
+    assert L.ssc_compact_i64(A, A + 792, 100, 1, 0, C, S, big, None) == ALIAS  # in is 800 bytes
+    assert L.ssc_compact_i64(A, B, 100, 1, 0, B + 796, S, big, None) == ALIAS
+    assert L.ssc_compact_i64(A, B, 100, 1, 0, C, S, 100, None) == SCRATCH
+    assert L.ssc_select_index_i64(A, A + 792, 100, 1, 0, C, S, big, None) == ALIAS
+    assert L.ssc_select_index_i64(A, B, 100, 3, 63, None, S, big, None) == ARG
+    assert L.ssc_select_index_i64(A, B, 100, 2, 0, C, A, big, None) == ALIAS
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(16, dtype=torch.int32)
