@@ -156,6 +156,67 @@ def pipeline_rows(x, m: int, stream, steps: int, copy_us: float) -> dict:
     return rows
 
 
+def format_rows(x, out, dev, steps: int, stream) -> dict:
+    """The kernel's other element formats at the headline's scale (1 GiB or
+    more read per launch, so HBM-bound like the headline), each checked
+    against torch before it is timed: compaction and selection by a flag
+    byte per element (50% nonzero), 2^27 key-value pairs and 2^27 int64
+    values (odd kept)."""
+    import torch
+
+    import scan_stream_compaction_amd as ssc
+    from scan_stream_compaction_amd import workloads as wl
+
+    rows = {}
+
+    def timed(name, fn, alg_bytes, **info):
+        _, per_ms, _ = timed_calls(fn, steps, stream)
+        us = per_ms * 1e3
+        gbs = alg_bytes / (us * 1e-6) / 1e9
+        rows[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                      "pct_hbm_peak": round(gbs / HBM_PEAK_GBPS * 100, 1),
+                      "algorithmic_bytes": alg_bytes, **info}
+
+    n = x.numel()
+    f = torch.from_numpy(wl.flag_bytes(0x5EED0104, n, 50)).to(dev)
+    mask = f != 0
+    k = int(mask.sum())
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    fn = ssc.prepared(ssc.compact_flags, x, f, out=out, count=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == k and torch.equal(out[:k], torch.masked_select(x, mask))
+    timed("compact_flags_2p28", fn, 5 * n + 4 * k, kept=k,
+          note="4-byte values and one flag byte each read, survivors written: 5N + 4K")
+    fn = ssc.prepared(ssc.select_flags, f, out=out, count=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == k and torch.equal(out[:k], torch.nonzero(mask).flatten().to(torch.int32))
+    timed("select_flags_2p28", fn, n + 4 * k, kept=k, note="flag bytes read, positions written: N + 4K")
+    del f, mask
+
+    h = n // 2
+    keys = x[:h]
+    vals = torch.from_numpy(wl.full_int32(0x5EED0105, h)).to(dev)
+    ko, vo = out[:h], out[h:]
+    fn = ssc.prepared(ssc.compact_kv, keys, vals, "odd", keys_out=ko, vals_out=vo, count=cnt)
+    torch.cuda.synchronize()
+    mask = (keys & 1) == 1
+    k = int(mask.sum())
+    assert int(cnt.item()) == k and torch.equal(ko[:k], keys[mask]) and torch.equal(vo[:k], vals[mask])
+    timed("compact_kv_odd_2p27", fn, 8 * h + 8 * k, kept=k,
+          note="2^27 int32 keys (odd kept) with int32 values: 8N + 8K")
+    del vals, mask
+
+    y = torch.from_numpy(wl.full_int64(0x5EED0106, h)).to(dev)
+    out64 = out.view(torch.int64)
+    fn = ssc.prepared(ssc.compact, y, "odd", out=out64, count=cnt)
+    torch.cuda.synchronize()
+    mask = (y & 1) == 1
+    k = int(mask.sum())
+    assert int(cnt.item()) == k and torch.equal(out64[:k], y[mask])
+    timed("compact_i64_odd_2p27", fn, 8 * h + 8 * k, kept=k, note="2^27 full-range int64, odd kept: 8N + 8K")
+    return rows
+
+
 def other_workloads(dev, steps: int, stream) -> dict:
     """The other workloads of the method, each checked against torch before it
     is timed: per-launch time from HIP events and effective GB/s over the
@@ -363,6 +424,7 @@ def main():
         del idx
         extra["pipelines_x_copy"] = pipeline_rows(x, m, stream, args.steps, extra["copy_i32"]["us"])
         extra["other_workloads"] = other_workloads(dev, max(5, args.steps // 5), stream)
+        extra["other_formats"] = format_rows(x, out, dev, max(5, args.steps // 2), stream)
     if extra:
         log("extra: " + json.dumps(extra))
 
@@ -395,7 +457,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "ssc::select_kernel<1, true, 0> (odd, 128-bit, compaction)",
+            "kernel": "ssc::select_kernel<ssc::FmtB32<true>, 1, 0> (odd, 128-bit, compaction)",
             "kernel_us": round(kernel_ms * 1e3, 2),
         },
         "extra": extra,
