@@ -105,10 +105,14 @@ _recording = None  # list of library calls being recorded by prepared(), or None
 
 
 def _call(name: str, fn, *args) -> None:
-    """Make one library call (and record it while prepared() is recording)."""
+    """Make one library call (and record it while prepared() is recording).
+    Tensor arguments are passed as their device pointers; a recording keeps
+    the tensors themselves, so every buffer a recorded call touches (scratch
+    an op allocated for itself included) lives as long as the recording."""
+    raw = tuple(a.data_ptr() if isinstance(a, torch.Tensor) else a for a in args)
     if _recording is not None:
-        _recording.append((name, fn, args))
-    _check(name, fn(*args))
+        _recording.append((name, fn, raw, args))
+    _check(name, fn(*raw))
 
 
 def prepared(op, *args, **kwargs):
@@ -127,8 +131,8 @@ def prepared(op, *args, **kwargs):
         _recording = None
 
     def run():
-        for name, fn, a in calls:
-            _check(name, fn(*a))
+        for name, fn, raw, _ in calls:
+            _check(name, fn(*raw))
         return result
     return run
 
@@ -205,7 +209,7 @@ def _scan(x, out, total, scratch, form):
         raise TypeError(f"{form}_scan takes int32 or float32 tensors of one dtype")
     fn = (names[x.dtype], getattr(lib(), names[x.dtype]))
     _dev(out)
-    _call(fn[0], fn[1], x.data_ptr(), out.data_ptr(), x.numel(), _ptr(total), scratch.data_ptr(),
+    _call(fn[0], fn[1], x, out, x.numel(), total, scratch,
           scratch.numel(), _stream(x))
     return out, total
 
@@ -242,8 +246,8 @@ def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
     if scratch is None:
         scratch = new_scratch(n, x.device)
     _call(fn, getattr(lib(), fn),
-          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), _ptr(rk),
-          scratch.data_ptr(), scratch.numel(), _stream(x))
+          x, out, n, _pred(pred), pa, pb, count, rk,
+          scratch, scratch.numel(), _stream(x))
     return (out, count, rk) if rk is not None else (out, count)
 
 
@@ -266,8 +270,8 @@ def select_index(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
     if scratch is None:
         scratch = new_scratch(n, x.device)
     _call(fn, getattr(lib(), fn),
-          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
-          scratch.data_ptr(), scratch.numel(), _stream(x))
+          x, out, n, _pred(pred), pa, pb, count,
+          scratch, scratch.numel(), _stream(x))
     return out, count
 
 
@@ -285,8 +289,8 @@ def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,
     if scratch is None:
         scratch = new_scratch(n, x.device)
     _call(fn, getattr(lib(), fn),
-          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(),
-          scratch.data_ptr(), scratch.numel(), _stream(x))
+          x, out, n, _pred(pred), pa, pb, count,
+          scratch, scratch.numel(), _stream(x))
     return out, count
 
 
@@ -299,7 +303,7 @@ def count_if(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
     if scratch is None:
         scratch = new_scratch(0, x.device)
     _call("ssc_count_if_i32", lib().ssc_count_if_i32,
-          x.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(), scratch.data_ptr(),
+          x, x.numel(), _pred(pred), pa, pb, count, scratch,
           scratch.numel(), _stream(x))
     return count
 
@@ -314,7 +318,7 @@ def compact_atomic(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     _call("ssc_compact_atomic_i32", lib().ssc_compact_atomic_i32,
-          x.data_ptr(), out.data_ptr(), x.numel(), _pred(pred), pa, pb, count.data_ptr(),
+          x, out, x.numel(), _pred(pred), pa, pb, count,
           variant, _stream(x))
     return out, count
 
@@ -331,7 +335,7 @@ def radix_sort(x: torch.Tensor, *, out: torch.Tensor | None = None,
     if scratch is None:
         scratch = new_scratch(n, x.device, radix=True)
     _call("ssc_radix_sort_u32", lib().ssc_radix_sort_u32,
-          x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, scratch.data_ptr(), scratch.numel(),
+          x, out, tmp, n, scratch, scratch.numel(),
           _stream(x))
     return out
 
@@ -353,7 +357,7 @@ def radix_sort4(x: torch.Tensor, passes: int = 8, *, out: torch.Tensor | None = 
     if scratch is None:
         scratch = torch.zeros(radix_sort4_scratch_bytes(n), dtype=torch.uint8, device=x.device)
     _call("ssc_radix_sort4_u32", lib().ssc_radix_sort4_u32,
-          x.data_ptr(), out.data_ptr(), tmp.data_ptr(), n, passes, scratch.data_ptr(),
+          x, out, tmp, n, passes, scratch,
           scratch.numel(), _stream(x))
     return out
 
@@ -376,7 +380,7 @@ def exclusive_scan_multipass(x: torch.Tensor, out: torch.Tensor | None = None,
     if scratch is None:
         scratch = multipass_scratch(x.numel(), x.device)
     _call("ssc_exclusive_scan_multipass_i32", lib().ssc_exclusive_scan_multipass_i32,
-          x.data_ptr(), out.data_ptr(), x.numel(), total.data_ptr(), scratch.data_ptr(),
+          x, out, x.numel(), total, scratch,
           scratch.numel(), _stream(x))
     return out, total
 
@@ -399,8 +403,8 @@ def compact_multipass(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0,
     if scratch is None:
         scratch = multipass_scratch(n, x.device)
     _call("ssc_compact_multipass_i32", lib().ssc_compact_multipass_i32,
-          x.data_ptr(), out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), ranks.data_ptr(),
-          scratch.data_ptr(), scratch.numel(), _stream(x))
+          x, out, n, _pred(pred), pa, pb, count, ranks,
+          scratch, scratch.numel(), _stream(x))
     return out, count, ranks
 
 
@@ -408,7 +412,7 @@ def copy(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     _dev(x)
     if out is None:
         out = torch.empty_like(x)
-    _call("ssc_copy_i32", lib().ssc_copy_i32, x.data_ptr(), out.data_ptr(), x.numel(), _stream(x))
+    _call("ssc_copy_i32", lib().ssc_copy_i32, x, out, x.numel(), _stream(x))
     return out
 
 
@@ -420,8 +424,8 @@ def _i64_op(fn: str, x: torch.Tensor, pred, bit: int, out: torch.Tensor,
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     if scratch is None:
         scratch = new_scratch(n, x.device)
-    _call(fn, getattr(lib(), fn), x.data_ptr(), out.data_ptr(), n, _pred(pred), bit,
-          count.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(x))
+    _call(fn, getattr(lib(), fn), x, out, n, _pred(pred), bit,
+          count, scratch, scratch.numel(), _stream(x))
     return out, count
 
 
@@ -453,8 +457,8 @@ def compact_flags(x: torch.Tensor, flags: torch.Tensor, *, out: torch.Tensor | N
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     if scratch is None:
         scratch = new_scratch(n, x.device)
-    _call("ssc_compact_flags_b32", lib().ssc_compact_flags_b32, x.data_ptr(), fb.data_ptr(),
-          out.data_ptr(), n, count.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(x))
+    _call("ssc_compact_flags_b32", lib().ssc_compact_flags_b32, x, fb,
+          out, n, count, scratch, scratch.numel(), _stream(x))
     return out, count
 
 
@@ -470,8 +474,8 @@ def select_flags(flags: torch.Tensor, *, out: torch.Tensor | None = None,
         count = torch.empty(1, dtype=torch.int32, device=fb.device)
     if scratch is None:
         scratch = new_scratch(n, fb.device)
-    _call("ssc_select_flags", lib().ssc_select_flags, fb.data_ptr(), out.data_ptr(), n,
-          count.data_ptr(), scratch.data_ptr(), scratch.numel(), _stream(fb))
+    _call("ssc_select_flags", lib().ssc_select_flags, fb, out, n,
+          count, scratch, scratch.numel(), _stream(fb))
     return out, count
 
 
@@ -495,7 +499,7 @@ def compact_kv(keys: torch.Tensor, vals: torch.Tensor, pred="nonzero", pa=0, pb=
         count = torch.empty(1, dtype=torch.int32, device=keys.device)
     if scratch is None:
         scratch = new_scratch(n, keys.device)
-    _call(fn, getattr(lib(), fn), keys.data_ptr(), vals.data_ptr(), keys_out.data_ptr(),
-          vals_out.data_ptr(), n, _pred(pred), pa, pb, count.data_ptr(), scratch.data_ptr(),
+    _call(fn, getattr(lib(), fn), keys, vals, keys_out,
+          vals_out, n, _pred(pred), pa, pb, count, scratch,
           scratch.numel(), _stream(keys))
     return keys_out, vals_out, count

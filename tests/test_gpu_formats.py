@@ -247,3 +247,34 @@ def test_other_formats_empty_and_errors():
     with pytest.raises(ssc.SSCError):  # flags not 4-byte aligned
         big = torch.ones(20, dtype=torch.uint8, device=DEV)
         ssc.compact_flags(torch.zeros(10, dtype=torch.int32, device=DEV), big[1:11])
+
+
+def test_prepared_calls_of_every_format_survive_allocation_churn():
+    """A prepared call keeps the scratch its op allocated for itself: after
+    fresh allocations (which would reuse freed memory) every replay still
+    gives the oracle's result. Timing loops depend on this."""
+    n = 4 * TH + 99
+    keys = wl.full_int32(800, n)
+    vals = wl.full_int32(801, n)
+    f = wl.flag_bytes(802, n, 40)
+    x64 = wl.full_int64(803, n)
+    kd, vd, fd, xd64 = dev(keys), dev(vals), dev(f), dev(x64)
+    wk, wv, mk = oracle.compact_kv(keys, vals, oracle.PRED_ODD)
+    wf, mf = oracle.compact_flags(keys, f)
+    wi, mi = oracle.select_flags(f)
+    w64, m64 = oracle.compact_i64(x64, oracle.PRED_ODD)
+    runs = [
+        (ssc.prepared(ssc.compact_kv, kd, vd, "odd"), lambda r: (r[2], [(r[0], wk), (r[1], wv)], mk)),
+        (ssc.prepared(ssc.compact_flags, kd, fd), lambda r: (r[1], [(r[0], wf)], mf)),
+        (ssc.prepared(ssc.select_flags, fd), lambda r: (r[1], [(r[0], wi)], mi)),
+        (ssc.prepared(ssc.compact, xd64, "odd"), lambda r: (r[1], [(r[0], w64)], m64)),
+    ]
+    churn = [torch.full((ssc.scratch_bytes(n) + 256 * i,), 255, dtype=torch.uint8, device=DEV)
+             for i in range(32)]
+    for _ in range(3):
+        for run, unpack in runs:
+            cnt, outs, m = unpack(run())
+            assert int(host(cnt)[0]) == m
+            for got, want in outs:
+                assert checks.first_mismatch(host(got)[:m], want) == -1
+    del churn

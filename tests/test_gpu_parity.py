@@ -605,6 +605,10 @@ def test_prepared_call_repeats_the_same_library_call():
     out = torch.full_like(xd, SENTINEL)
     cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
     run = ssc.prepared(ssc.compact, xd, "odd", out=out, count=cnt)
+    # the scratch compact() allocated for itself must outlive the call: fresh
+    # allocations of that size, filled with ones, would otherwise land on it
+    churn = [torch.full((ssc.scratch_bytes(x.size) + 64 * i,), 255, dtype=torch.uint8, device=DEV)
+             for i in range(16)]
     for _ in range(3):
         out.fill_(SENTINEL)
         cnt.zero_()
@@ -613,6 +617,7 @@ def test_prepared_call_repeats_the_same_library_call():
         assert int(host(cnt)[0]) == m
         o = host(out)
         assert checks.first_mismatch(o[:m], want) == -1 and np.all(o[m:] == SENTINEL)
+    del churn
 
 
 def test_argument_errors_raise_on_gpu():
