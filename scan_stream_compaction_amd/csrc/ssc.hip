@@ -19,14 +19,18 @@
 // the current tile and, in flight, its chunk of the next: every tile's
 // aggregate is published as soon as its data has landed, the loads of later
 // tiles overlap the look-back waits, and survivors leave as contiguous runs
-// staged in LDS. Ranks inside a wavefront come from ballot + mbcnt. The scan
-// kernel keeps one tile per workgroup: two rounds of 15 chunks, the last data
-// wavefront to finish scanning the 30 chunk totals.
+// staged in LDS. Ranks inside a wavefront come from packed DPP scans of the
+// lanes' per-load flag counts. The kernel is a template over element formats
+// (32-bit values, a caller's flag bytes, key-value pairs, 64-bit values) that
+// share this pipeline. The scan kernel keeps one tile per workgroup: two
+// rounds of 15 chunks, the last data wavefront to finish scanning the 30
+// chunk totals.
 //
 // Scratch needs no clearing between calls: tile numbers and an epoch come
-// from one 64-bit atomic word {epoch:32 | next tile:32}; the workgroup that
-// makes a call's last claim resets the counter and advances the epoch, and
-// descriptors carry the epoch as a tag. The counting passes reset their own
+// from one 64-bit atomic word {epoch:32 | next tile:32}, reset and advanced
+// by the call itself (by its last claim where a call makes a known number of
+// claims, else by the last workgroup to finish claiming), and descriptors
+// carry the epoch as a tag. The counting passes reset their own
 // accumulators (the last workgroup to finish does it).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
