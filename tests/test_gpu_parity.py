@@ -598,6 +598,48 @@ def test_runs_on_a_side_stream():
     assert checks.first_mismatch(out.cpu().numpy()[:m], want) == -1
 
 
+def test_concurrent_calls_on_three_streams():
+    """Three calls of the persistent kernel in flight at once on three streams
+    (each with its own scratch), repeated without host synchronization. One
+    workgroup fills a compute unit's LDS, so the calls' grids share the GPU
+    and none is fully resident from the start; tiles are numbered by claims
+    of running workgroups only, so each call still finishes with the
+    oracle's result, and every call leaves its counter reset for the next."""
+    n1, n2, n3 = (1 << 22) + 17, (1 << 21) + 5, 3 * T + 611
+    x1 = wl.full_int32(501, n1)
+    k2 = wl.uniform_below(502, n2, 5)
+    v2 = wl.full_int32(503, n2)
+    x3 = wl.full_int32(504, n3)
+    w1, m1 = oracle.compact_i32(x1, oracle.PRED_ODD)
+    wk, wv, m2 = oracle.compact_kv(k2, v2, oracle.PRED_NONZERO)
+    w3, k3 = oracle.partition_i32(x3, oracle.PRED_EVEN)
+    d1, dk, dv, d3 = dev(x1), dev(k2), dev(v2), dev(x3)
+    sc = [ssc.new_scratch(n, DEV) for n in (n1, n2, n3)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    outs = None
+    for _ in range(4):
+        with torch.cuda.stream(streams[0]):
+            o1 = ssc.compact(d1, "odd", scratch=sc[0])
+        with torch.cuda.stream(streams[1]):
+            o2 = ssc.compact_kv(dk, dv, "nonzero", scratch=sc[1])
+        with torch.cuda.stream(streams[2]):
+            o3 = ssc.partition(d3, "even", scratch=sc[2])
+        outs = (o1, o2, o3)
+    for st in streams:
+        st.synchronize()
+    (o1, c1), (ok, ov, c2), (o3, c3) = outs
+    assert int(c1.cpu()[0]) == m1 and int(c2.cpu()[0]) == m2 and int(c3.cpu()[0]) == k3
+    assert checks.first_mismatch(o1.cpu().numpy()[:m1], w1) == -1
+    assert checks.first_mismatch(ok.cpu().numpy()[:m2], wk) == -1
+    assert checks.first_mismatch(ov.cpu().numpy()[:m2], wv) == -1
+    assert checks.first_mismatch(o3.cpu().numpy(), w3) == -1
+    # no look-back gave up waiting
+    for s_ in sc:
+        assert int(s_[8:12].view(torch.int32).cpu()[0]) == 0
+
+
 def test_prepared_call_repeats_the_same_library_call():
     x = wl.full_int32(91, 3 * T + 5)
     want, m = oracle.compact_i32(x, oracle.PRED_ODD)
