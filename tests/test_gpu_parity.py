@@ -259,6 +259,31 @@ def test_headline_odd_selection_full_size(headline):
     say(f"  odd selected {m} of {x.size}")
 
 
+def test_maximum_size_compaction_and_selection():
+    """n = 2^31 - 1, the largest n the C ABI takes (8 GiB in and out): byte
+    offsets past 4 GiB, tile numbers near the descriptor capacity, and a
+    count near 2^30; compared element by element with the full oracle."""
+    n = 2**31 - 1
+    say("  generating 2^31 - 1 full-range int32 ...")
+    x = wl.full_int32(0x5EED0107, n)
+    want, m = oracle.compact_i32(x, oracle.PRED_ODD)
+    xd = dev(x)
+    out = torch.empty_like(xd)
+    out[-1] = SENTINEL
+    _, cnt = ssc.compact(xd, "odd", out=out)
+    assert int(host(cnt)[0]) == m
+    got = host(out)
+    assert checks.first_mismatch(got[:m], want) == -1
+    assert got[-1] == SENTINEL or m == n
+    del got, want
+    idx = out  # reuse the 8 GiB buffer for the positions
+    _, cnt = ssc.select_index(xd, "odd", out=idx)
+    assert int(host(cnt)[0]) == m
+    wi, mi = oracle.select_index_i32(x, oracle.PRED_ODD)
+    assert mi == m and checks.first_mismatch(host(idx)[:m], wi) == -1
+    say(f"  kept {m} of {n}")
+
+
 @pytest.mark.parametrize("keep", wl.SWEEP_KEEP)
 def test_headline_selectivity_sweep(headline, keep):
     """Keep x when mod(x, 100) < s, s in {1, 50, 99}, on the same 2^28 array."""
