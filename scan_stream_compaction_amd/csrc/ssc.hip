@@ -919,9 +919,10 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         int ln = lane;                                                                        \
         asm volatile("" : "+v"(ln));                                                          \
         {                                                                                     \
-            /* every element gets a slot of its own, no branches: survivors at    */            \
-            /* their rank, the others after all survivors at a_cur + (index -     */            \
-            /* rank), elements past rem included (they land past the runs)        */            \
+            /* a partition gives every element a slot of its own, no branches:   */            \
+            /* survivors at their rank, the others after all survivors at a_cur + */            \
+            /* (index - rank), elements past rem included (they land past the     */            \
+            /* runs); compaction and selection stage the survivors only           */            \
             uint32_t lead[S::kLoads];                                                         \
             chunk_leads<S::kLoads, S::kPer>(fm_cur, lead);                                    \
             /* (a selection stages each element's index instead of its value)    */            \
@@ -932,11 +933,14 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
                     a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);      \
                 _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                         \
                     const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                    \
-                    const uint32_t slot = f ? r : rej + k - r;                                \
-                    if constexpr (KIND == kSelectIndex)                                       \
-                        s_stage[w][slot] = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
-                    else                                                                      \
-                        F::stage(s_stage[w], slot, CUR, j, k);                                \
+                    if constexpr (KIND == kPartition) {                                       \
+                        F::stage(s_stage[w], f ? r : rej + k - r, CUR, j, k);                 \
+                    } else if (f) {                                                           \
+                        if constexpr (KIND == kSelectIndex)                                   \
+                            s_stage[w][r] = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
+                        else                                                                  \
+                            F::stage(s_stage[w], r, CUR, j, k);                               \
+                    }                                                                         \
                     r += f;                                                                   \
                 }                                                                             \
             }                                                                                 \
