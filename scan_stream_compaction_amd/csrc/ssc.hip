@@ -1678,17 +1678,14 @@ int32_t f32_bits(float f) {
 }
 
 // Arguments of a predicate as the kernels take them (see PredArgs); for
-// MOD_LT the constants of division by the invariant modulus a >= 1.
+// MOD_LT the fp64 constants of the division by the invariant modulus a >= 1.
 PredArgs make_pred_args(int pred, int32_t pa, int32_t pb) {
-    PredArgs p{pa, pb, 0u, 0u, 0u, 0u};
+    PredArgs p{pa, pb, 0.0, 0.0, 0.0, 0.0};
     if (pred == SSC_PRED_MOD_LT) {
-        const uint32_t d = static_cast<uint32_t>(pa);
-        uint32_t l = 0;
-        while ((uint64_t{1} << l) < d) ++l;  // ceil(log2 d)
-        p.magic = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1);
-        p.sh1 = l < 1u ? l : 1u;
-        p.sh2 = l > 1u ? l - 1u : 0u;
-        p.bias = 0x80000000u % d;
+        p.inv = 1.0 / static_cast<double>(pa);
+        p.ad = static_cast<double>(pa);
+        p.bd = static_cast<double>(pb);
+        p.bma = static_cast<double>(pb) - static_cast<double>(pa);
     }
     return p;
 }

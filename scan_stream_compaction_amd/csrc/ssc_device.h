@@ -87,18 +87,17 @@ __device__ __forceinline__ typename Op::T wave_sum(typename Op::T v) {
 // F32 predicates (6..9) read the 32-bit element and a, b as fp32 bits and
 // compare with IEEE semantics (NaN compares false, -0.0 == 0.0).
 //
-// The modulus is invariant over a call, so MOD_LT divides by multiplication
-// (Granlund and Montgomery, "Division by Invariant Integers using
-// Multiplication", PLDI 1994, the unsigned N = 32 case): with
-// l = ceil(log2 a), magic = floor(2^32 (2^l - a) / a) + 1, sh1 = min(l, 1)
-// and sh2 = max(l - 1, 0), floor(u / a) = (t + ((u - t) >> sh1)) >> sh2 for
-// t = mulhi(magic, u) and every 32-bit u. The host computes the constants
-// (make_pred_args). A signed x is taken as u = x + 2^31, so that
-// mod(x, a) = (u mod a - bias) mod a with bias = 2^31 mod a, a value in
-// (-a, a) before the final correction.
+// MOD_LT divides in fp64 with constants the host computes once per call
+// (make_pred_args): inv = 1/a rounded once, then q = floor(fma(x, inv,
+// 2^-20)) and r = fma(-q, a, x) = x - q*a exactly (all integers below 2^33).
+// fma(x, inv, 2^-20) is within 2^-21 of x/a + 2^-20 for |x| <= 2^31, so q is
+// floor(x/a) or one more and r lies in [-a, a); the non-negative residue is
+// below b iff 0 <= r < b, or r < b - a (a negative r stands for r + a). Four
+// full-rate fp64 operations and three compares, where an integer division by
+// multiplication needs two quarter-rate 32-bit multiplies and corrections.
 struct PredArgs {
     int32_t a, b;
-    uint32_t magic, sh1, sh2, bias;
+    double inv, ad, bd, bma;  // MOD_LT: 1/a, a, b, b - a
 };
 
 template <int P>
@@ -125,12 +124,10 @@ __device__ __forceinline__ bool pred_eval(int32_t x, const PredArgs &pr) {
         return __int_as_float(pr.a) <= f && f < __int_as_float(pr.b);
     } else {
         static_assert(P == 5, "predicate numbering");
-        const uint32_t v = u ^ 0x80000000u;  // x + 2^31
-        const uint32_t t = __umulhi(pr.magic, v);
-        const uint32_t q = (t + ((v - t) >> pr.sh1)) >> pr.sh2;  // floor(v / a)
-        int32_t r = static_cast<int32_t>(v - q * static_cast<uint32_t>(pr.a) - pr.bias);
-        if (r < 0) r += pr.a;
-        return r < pr.b;
+        const double xd = static_cast<double>(x);
+        const double q = __builtin_floor(__builtin_fma(xd, pr.inv, 0x1p-20));
+        const double r = __builtin_fma(-q, pr.ad, xd);
+        return (r >= 0.0 && r < pr.bd) || r < pr.bma;
     }
 }
 
