@@ -665,6 +665,57 @@ def test_concurrent_calls_on_three_streams():
         assert int(s_[8:12].view(torch.int32).cpu()[0]) == 0
 
 
+def test_graph_capture_replays_match_the_oracle():
+    """The calls are one launch each (partition: two) with no memset and no
+    allocation, and the claim counter's epoch lives in the scratch, so they
+    can be captured in a HIP graph: each replay, with eager work and host
+    synchronization between replays, gives the oracle's result."""
+    n = 7 * T + 123
+    x = wl.full_int32(505, n)
+    want, m = oracle.compact_i32(x, oracle.PRED_ODD)
+    pwant, k = oracle.partition_i32(x, oracle.PRED_EVEN)
+    swant, stot = oracle.exclusive_scan_i32(x)
+    xd = dev(x)
+    out = torch.empty_like(xd)
+    pout = torch.empty_like(xd)
+    sout = torch.empty_like(xd)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pcnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    tot = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sc = [ssc.new_scratch(n, DEV) for _ in range(3)]
+
+    def calls():
+        ssc.compact(xd, "odd", out=out, count=cnt, scratch=sc[0])
+        ssc.partition(xd, "even", out=pout, count=pcnt, scratch=sc[1])
+        ssc.exclusive_scan(xd, out=sout, total=tot, scratch=sc[2])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for _ in range(4):
+        out.fill_(SENTINEL)
+        pout.fill_(SENTINEL)
+        sout.fill_(SENTINEL)
+        cnt.zero_()
+        pcnt.zero_()
+        tot.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(cnt.cpu()[0]) == m and int(pcnt.cpu()[0]) == k and int(tot.cpu()[0]) == stot
+        o = out.cpu().numpy()
+        assert checks.first_mismatch(o[:m], want) == -1 and np.all(o[m:] == SENTINEL)
+        assert checks.first_mismatch(pout.cpu().numpy(), pwant) == -1
+        assert checks.first_mismatch(sout.cpu().numpy(), swant) == -1
+    del g
+
+
 def test_prepared_call_repeats_the_same_library_call():
     x = wl.full_int32(91, 3 * T + 5)
     want, m = oracle.compact_i32(x, oracle.PRED_ODD)
