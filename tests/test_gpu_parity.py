@@ -351,6 +351,18 @@ def test_radix4_edge_sizes(n):
     assert checks.first_mismatch(got, oracle.radix_sort_u32(y, passes=12)) == -1
 
 
+def test_radix4_reuses_one_scratch_across_sizes_and_passes():
+    """The sort keeps state in its scratch between calls (digit counters that
+    end each call at zero, the tile counter and its epoch): calls of
+    different sizes and pass counts on one zero-filled scratch all match."""
+    big = 100_003
+    scratch = torch.zeros(ssc.radix_sort4_scratch_bytes(big), dtype=torch.uint8, device=DEV)
+    for i, (n, p) in enumerate([(big, 8), (5000, 3), (big, 5), (2 * R4, 8), (1, 1), (big, 8)]):
+        x = wl.full_uint32(0x5EED0505 + i, n)
+        got = host(ssc.radix_sort4(dev(x.view(np.int32)), passes=p, scratch=scratch)).view(np.uint32)
+        assert checks.first_mismatch(got, oracle.radix_sort_u32(x, passes=4 * p)) == -1, (n, p)
+
+
 def test_radix4_unaligned_in_place_and_odd_passes():
     n = 5 * R4 + 77
     x = wl.full_uint32(0x5EED0405, n)
