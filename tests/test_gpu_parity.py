@@ -585,6 +585,32 @@ def test_repeated_runs_are_identical():
     assert int(host(scratch[8:12].view(torch.int32))[0]) == 0
 
 
+def test_look_back_wait_is_bounded_and_reported():
+    """A descriptor that is never published must not keep the kernel
+    running: the host starts a fresh scratch's tile counter at 1, so tile 0
+    is never claimed and tile 1's look-back waits on it. The wait gives up
+    after its fixed number of polls (about a second), the kernel finishes
+    normally and word 2 of the scratch reports it; a zeroed scratch then
+    serves a correct call again."""
+    import time
+    x = wl.uniform_below(77, 4 * T, 3)
+    want, m = oracle.compact_i32(x, oracle.PRED_NONZERO)
+    xd = dev(x)
+    scratch = ssc.new_scratch(x.size, xd.device)
+    scratch[0:8].view(torch.int64)[0] = 1  # {epoch 0 | next tile 1}
+    torch.cuda.synchronize()
+    t0 = time.time()
+    ssc.compact(xd, "nonzero", scratch=scratch)
+    torch.cuda.synchronize()
+    say(f"  forced look-back time-out: call finished after {time.time() - t0:.2f} s")
+    assert int(host(scratch[8:12].view(torch.int32))[0]) == 1
+    scratch.zero_()
+    out, cnt = ssc.compact(xd, "nonzero", scratch=scratch)
+    assert int(host(cnt)[0]) == m
+    assert checks.first_mismatch(host(out)[:m], want) == -1
+    assert int(host(scratch[8:12].view(torch.int32))[0]) == 0
+
+
 def test_one_scratch_across_sizes_and_ops():
     """One scratch buffer serves many calls of different sizes and kinds in a
     row: the epoch tags keep descriptors of earlier calls from being read."""
