@@ -93,6 +93,18 @@ def timed_calls(fn, steps: int, stream):
     return region_ms, region_ms / steps, wall
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(x_np, target_s: float = 12.0):
     """Sequential oracle compaction (predicate odd) on the host, 1 thread.
     Runs the full input repeatedly until about target_s of CPU time has
@@ -126,7 +138,7 @@ def cpu_baseline(x_np, target_s: float = 12.0):
         "kind": "oracle",
         "sample": (f"full 2^28-element input, sequential orc_compact_i32 (odd), "
                    f"median of {len(times)} runs ({med * 1e3:.1f} ms each), "
-                   f"{platform.processor() or platform.machine()}, "
+                   f"{cpu_model()}, "
                    f"host has {os.cpu_count()} logical CPUs, 1 thread used"),
         "elements_per_s": round(n / med, 1),
         "kept": int(m),
