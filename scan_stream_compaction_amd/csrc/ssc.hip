@@ -427,8 +427,11 @@ __device__ __forceinline__ void load_b32x4(const int32_t *in, int64_t chunk, uin
 // shared with the neighbouring runs and take the default policy, so the L2
 // merges them; its whole lines are stored nontemporal. Measured at 2^28:
 // 99% kept 386 -> 366 us, partition 564 -> 541 us, 50% kept unchanged
-// (all lines nontemporal: slower; all default: the 386 / 564).
-template <int C>
+// (all lines nontemporal: slower; all default: the 386 / 564). POL is the
+// whole lines' policy: a run the library itself reads next (the radix
+// driver's chained partitions) takes the default policy, which keeps it in
+// the caches (2^24 keys: 1,265 us against 1,360 us with nontemporal lines).
+template <int C, int POL = kNT>
 __device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, uint32_t at,
                                            uint32_t len, int64_t n, int lane) {
     len = uniform(len);
@@ -447,7 +450,7 @@ __device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, u
     const uint32_t *src = run + head + lane;
 #pragma unroll
     for (int i = 0; i < C / kWave; ++i)
-        __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, kNT);
+        __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, POL);
     __builtin_amdgcn_raw_buffer_store_b32(run[tail_at + lane],
                                           buffer_rsrc(dst + tail_at, (len - tail_at) * 4u), voff,
                                           0, 0);
@@ -606,9 +609,10 @@ struct FmtB32 {
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
         region[slot] = static_cast<uint32_t>(r.v[j][k]);
     }
+    template <int POL = kNT>
     __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
                                  uint32_t len, int64_t n, int lane) {
-        stream_run<Shape::kChunk>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+        stream_run<Shape::kChunk, POL>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
     }
 };
 
@@ -648,9 +652,10 @@ struct FmtFlags {
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
         region[slot] = static_cast<uint32_t>(r.v[j][k]);
     }
+    template <int POL = kNT>
     __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
                                  uint32_t len, int64_t n, int lane) {
-        stream_run<Shape::kChunk>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+        stream_run<Shape::kChunk, POL>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
     }
 };
 
@@ -678,11 +683,12 @@ struct FmtPairs {
         region[slot] = static_cast<uint32_t>(r.k[j][k]);
         region[Shape::kChunk + slot] = static_cast<uint32_t>(r.v[j][k]);
     }
+    template <int POL = kNT>
     __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
                                  uint32_t len, int64_t n, int lane) {
-        stream_run<Shape::kChunk>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
-        stream_run<Shape::kChunk>(region + Shape::kChunk, static_cast<uint32_t *>(a.out_aux), at,
-                                  len, n, lane);
+        stream_run<Shape::kChunk, POL>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+        stream_run<Shape::kChunk, POL>(region + Shape::kChunk, static_cast<uint32_t *>(a.out_aux),
+                                       at, len, n, lane);
     }
 };
 
@@ -746,6 +752,7 @@ struct FmtB64 {
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
         reinterpret_cast<uint64_t *>(region)[slot] = r.v[j][k];
     }
+    template <int POL = kNT>  // 64-bit runs keep the default policy throughout
     __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
                                  uint32_t len, int64_t n, int lane) {
         stream_run64<Shape::kChunk>(reinterpret_cast<const uint64_t *>(region),
@@ -796,7 +803,10 @@ struct FmtB64 {
 // workgroups are resident at once.
 // KIND: compaction (survivors' values), compaction that also writes the
 // ranks, stable partition, or selection (survivors' indices).
-enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3 };
+// kPartitionCached is a partition whose output the library reads with its
+// next launch (the radix driver's chained splits): its runs are stored with
+// the default cache policy throughout.
+enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3, kPartitionCached = 4 };
 constexpr int kSelPollSleep = 32;  // look-back poll interval, s_sleep units (measured)
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
@@ -810,6 +820,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     using S = typename F::Shape;
     static_assert(KIND == kCompact || KIND == kSelectIndex || __is_same(F, FmtB32<F::kVec>),
                   "partition and ranks take 32-bit elements");
+    constexpr bool kPart = KIND == kPartition || KIND == kPartitionCached;
+    constexpr int kRunPol = KIND == kPartitionCached ? 0 : kNT;  // whole lines of the runs
     // one staging region per data wavefront, plus two of padding for run reads
     // (a partition's second run starts inside its region)
     __shared__ __attribute__((aligned(16))) uint32_t s_stage[kDataWaves + 2][kStageWords];
@@ -869,7 +881,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             const uint32_t agg = uniform(s_pre[tri][kDataWaves]);
             if (lane == 0) {
                 if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, prefix + agg);
-                if (KIND != kPartition && tile == num_tiles - 1)
+                if (!kPart && tile == num_tiles - 1)
                     *count = static_cast<int32_t>(prefix + agg);
                 // after the barrier: the count's atomic round trip stays off
                 // the path to this tile's base
@@ -885,7 +897,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         }
     }
 
-    const uint32_t kept = KIND == kPartition ? static_cast<uint32_t>(*kept_total) : 0u;
+    const uint32_t kept = kPart ? static_cast<uint32_t>(*kept_total) : 0u;
     typename F::Regs va, vb;
     uint32_t fm_cur = 0, fm_nxt = 0;  // flags of the current / next chunk
     uint32_t a_cur = 0, a_nxt = 0;    // their totals
@@ -948,7 +960,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
                     a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);      \
                 _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                         \
                     const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                    \
-                    if constexpr (KIND == kPartition) {                                       \
+                    if constexpr (kPart) {                                                    \
                         F::stage(s_stage[w], f ? r : rej + k - r, CUR, j, k);                 \
                     } else if (f) {                                                           \
                         if constexpr (KIND == kSelectIndex)                                   \
@@ -972,11 +984,11 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         if constexpr (KIND == kSelectIndex)                                                   \
             stream_run<S::kChunk>(s_stage[w], static_cast<uint32_t *>(a.out), seg, a_cur, n, ln); \
         else                                                                                  \
-            F::write(s_stage[w], a, seg, a_cur, n, ln);                                       \
-        if constexpr (KIND == kPartition) {                                                   \
+            F::template write<kRunPol>(s_stage[w], a, seg, a_cur, n, ln);                     \
+        if constexpr (kPart) {                                                                \
             /* rejected before this chunk = elements before it - kept before it */            \
             const uint32_t rej = static_cast<uint32_t>(chunk_now) - seg;                      \
-            F::write(s_stage[w] + a_cur, a, kept + rej, rem_cur - a_cur, n, ln);              \
+            F::template write<kRunPol>(s_stage[w] + a_cur, a, kept + rej, rem_cur - a_cur, n, ln); \
         }                                                                                     \
         if constexpr (KIND == kCompactRanks)                                                  \
             write_ranks<S::kLoads, F::kVec>(ranks, chunk_now, rem_cur, seg, fm_cur, ln);      \
@@ -2361,16 +2373,15 @@ int ssc_radix_sort_u32(const uint32_t *in, uint32_t *out, uint32_t *tmp, int64_t
     for (int b = 0; b < 32; ++b) {
         uint32_t *dst = (b % 2 == 0) ? tmp : out;  // pass 31 lands in out
         const int32_t *kept = reinterpret_cast<const int32_t *>(sv.kept32 + b);
+        // the next split reads this output: keep it in the caches
+        const SelArgs sa{src, nullptr, dst, nullptr};
+        const PredArgs pr = make_pred_args(SSC_PRED_BIT_CLEAR, b, 0);
         if (vec)
-            SSC_TRY((LaunchSelect<4, true>::run(kPartition, reinterpret_cast<const int32_t *>(src),
-                                                reinterpret_cast<int32_t *>(dst), n,
-                                                make_pred_args(SSC_PRED_BIT_CLEAR, b, 0), scratch,
-                                                cap, nullptr, nullptr, kept, s)));
+            SSC_TRY((launch_select<FmtB32<true>, 4, kPartitionCached>(sa, n, pr, scratch, cap, nullptr,
+                                                                      nullptr, kept, s)));
         else
-            SSC_TRY((LaunchSelect<4, false>::run(kPartition, reinterpret_cast<const int32_t *>(src),
-                                                 reinterpret_cast<int32_t *>(dst), n,
-                                                 make_pred_args(SSC_PRED_BIT_CLEAR, b, 0),
-                                                 scratch, cap, nullptr, nullptr, kept, s)));
+            SSC_TRY((launch_select<FmtB32<false>, 4, kPartitionCached>(sa, n, pr, scratch, cap,
+                                                                       nullptr, nullptr, kept, s)));
         src = dst;
     }
     return SSC_OK;
