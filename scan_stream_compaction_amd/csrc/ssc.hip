@@ -1199,9 +1199,15 @@ __global__ __launch_bounds__(kBlock) void count_kernel(const int32_t *__restrict
         const uint32_t done =
             __hip_atomic_fetch_add(sv.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
+            // all loads first: one coherent round trip, not one per accumulator
+            uint32_t part[kSpread];
+#pragma unroll
+            for (int i = 0; i < kSpread; ++i)
+                part[i] = __hip_atomic_load(sv.acc + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             uint32_t k = 0;
+#pragma unroll
             for (int i = 0; i < kSpread; ++i) {
-                k += __hip_atomic_load(sv.acc + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                k += part[i];
                 __hip_atomic_store(sv.acc + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             *result = static_cast<int32_t>(k);
@@ -1221,30 +1227,44 @@ __global__ __launch_bounds__(kBlock) void bit_clear_count_kernel(const uint32_t 
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
-    uint32_t acc[32];
+    // Per lane, keys with bit b set. Packed counting: word q of `nib` holds
+    // 4-bit counters for bits q, q+4, ..., q+28, so one shift, mask and add
+    // per word counts all 32 bits of a key; eight keys (at most 8 per
+    // counter) are then unpacked into `set`. Invalid slots count as 0.
+    uint32_t set[32];
 #pragma unroll
-    for (int b = 0; b < 32; ++b) acc[b] = 0;
+    for (int b = 0; b < 32; ++b) set[b] = 0;
+    uint32_t valid = 0;  // keys of this wavefront's chunks (uniform)
     for (uint32_t sub = blockIdx.x; sub < num_subs; sub += gridDim.x) {
         const int64_t chunk = static_cast<int64_t>(sub) * kSub + static_cast<int64_t>(w) * kChunk;
         const uint32_t rem = chunk_rem(n, chunk);
+        valid += rem;
         uint32_t v[kLoads][4];
         load_chunk<VEC>(in, chunk, lane, rem, v);
 #pragma unroll
-        for (int j = 0; j < kLoads; ++j) {
+        for (int half = 0; half < kLoads / 2; ++half) {
+            uint32_t nib[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bool valid = in_chunk(rem, j, lane, k);
-                const uint32_t x = v[j][k];
+            for (int j = 2 * half; j < 2 * half + 2; ++j) {
 #pragma unroll
-                for (int b = 0; b < 32; ++b)
-                    acc[b] += static_cast<uint32_t>(
-                        __builtin_popcountll(ballot(valid && ((x >> b) & 1u) == 0u)));
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t x = in_chunk(rem, j, lane, k) ? v[j][k] : 0u;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) nib[q] += (x >> q) & 0x11111111u;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) set[q + 4 * i] += (nib[q] >> (4 * i)) & 0xFu;
             }
         }
     }
-    if (lane == 0) {
 #pragma unroll
-        for (int b = 0; b < 32; ++b) s_cnt[w][b] = acc[b];
+    for (int b = 0; b < 32; ++b) {
+        const uint32_t all = wave_inclusive_scan<SumU32>(set[b]);
+        const uint32_t t = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(all), kWave - 1));
+        if (lane == 0) s_cnt[w][b] = valid - t;  // keys with bit b clear
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1258,10 +1278,14 @@ __global__ __launch_bounds__(kBlock) void bit_clear_count_kernel(const uint32_t 
         const uint32_t done =
             __hip_atomic_fetch_add(sv.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (done == gridDim.x - 1) {
+            // all loads first: one coherent round trip, not one per bit
+            uint32_t t[32];
+#pragma unroll
+            for (int b = 0; b < 32; ++b)
+                t[b] = __hip_atomic_load(sv.acc32 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
             for (int b = 0; b < 32; ++b) {
-                const uint32_t t =
-                    __hip_atomic_load(sv.acc32 + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(sv.kept32 + b, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(sv.kept32 + b, t[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(sv.acc32 + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __hip_atomic_store(sv.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1409,8 +1433,10 @@ __global__ __launch_bounds__(kBlock) void digit_scatter_kernel(const uint32_t *_
         const uint32_t y = s_keys[i];
         const uint32_t o = s_obase[(y >> shift) & 15u] + i;
         // a correct count table never trips this; a broken one gives wrong
-        // results instead of stray writes
-        if (static_cast<int64_t>(o) < n) __builtin_nontemporal_store(y, out + o);
+        // results instead of stray writes. Default cache policy: the next
+        // pass reads this output (measured 435 us a sort against 439 us with
+        // nontemporal stores, 2^24 keys)
+        if (static_cast<int64_t>(o) < n) out[o] = y;
     }
 }
 
