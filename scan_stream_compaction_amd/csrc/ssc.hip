@@ -421,8 +421,9 @@ __device__ __forceinline__ void load_b32x4(const int32_t *in, int64_t chunk, uin
 // Writes run[0 .. len) (LDS words) to out[at .. at + len) with a fixed
 // C / 64 + 2 32-bit stores per lane whatever len is: slots past each part
 // fall outside its resource and are dropped, so words up to run[C + 63] are
-// read (the staging array is padded for that). The run is also cut at n: a correct look-back never
-// needs it, a broken one then gives wrong results instead of stray writes.
+// read (the staging array is padded for that). The run is also cut at n: a
+// correct look-back never needs it, a broken one then gives wrong results
+// instead of stray writes.
 // Cache policy by 128-byte line: the run's partial first and last lines are
 // shared with the neighbouring runs and take the default policy, so the L2
 // merges them; its whole lines are stored nontemporal. Measured at 2^28:
