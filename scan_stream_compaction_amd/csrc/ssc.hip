@@ -808,7 +808,9 @@ struct FmtB64 {
 // next launch (the radix driver's chained splits): its runs are stored with
 // the default cache policy throughout.
 enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3, kPartitionCached = 4 };
-constexpr int kSelPollSleep = 32;  // look-back poll interval, s_sleep units (measured)
+// look-back poll interval, s_sleep units: 16 and 32 measured equal at 50% kept,
+// 16 about 1% faster at 1% kept (215.5 against 218.2 us at 2^28)
+constexpr int kSelPollSleep = 16;
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
 // F is the element format (what a chunk holds and how survivors are staged

@@ -166,7 +166,7 @@ __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
 // one workgroup per tile (hundreds of tiles waiting at once), frequent
 // coherent polling costs more throughput than it saves latency, and about
 // 3.4 us (s_sleep 127) is best; the persistent compaction kernel, whose
-// control wavefronts wait on tiles published earlier, is fastest at s_sleep 32.
+// control wavefronts wait on tiles published earlier, polls at s_sleep 16.
 //
 // Walking: then each step reads the descriptors of the 64 tiles just below
 // the window end at once (one load, 512 contiguous bytes). The window is
