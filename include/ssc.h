@@ -256,7 +256,8 @@ int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t
 /* Unordered compaction by atomic counter, kept only for comparison:
  * out[0 .. count) holds the same multiset as ssc_compact_i32's output, in
  * an order the hardware scheduler decides. variant 0: one atomicAdd per
- * 64-lane wavefront and 1024-element chunk; variant 1: one atomicAdd per
+ * 512-thread workgroup and 8192-element tile (its survivors keep tile
+ * order inside the reserved range); variant 1: one atomicAdd per
  * survivor (the form of "Day 33 compaction.cu", compactAtomic). *count is
  * cleared and used as the counter. No overlap between in, out and count. */
 int ssc_compact_atomic_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
