@@ -585,6 +585,43 @@ def test_repeated_runs_are_identical():
     assert int(host(scratch[8:12].view(torch.int32))[0]) == 0
 
 
+@pytest.mark.parametrize("shift_words", [4, 12])
+def test_outputs_that_start_inside_a_cache_line(shift_words):
+    """Runs are stored by 128-byte line: the partial first and last lines
+    with the default policy, whole lines nontemporal. An output array that is
+    16-byte aligned (the 128-bit path) but starts 16 or 48 bytes into a line
+    puts every run boundary at another offset. Compaction, partition (every
+    slot written) and selection must still match the oracle exactly and
+    leave everything outside their output untouched."""
+    n = 3 * T + 2 * C2 + 17
+    x = wl.uniform_below(0x5EED0909 + shift_words, n, 3)
+    xd = dev(x)
+    base = torch.full((n + 64,), SENTINEL, dtype=torch.int32, device=DEV)
+    out = base[shift_words:shift_words + n]
+    assert out.data_ptr() % 16 == 0 and out.data_ptr() % 128 != 0
+
+    def check(want, m, what):
+        h = host(base)
+        assert checks.first_mismatch(h[shift_words:shift_words + m], want) == -1, what
+        assert (h[:shift_words] == SENTINEL).all(), what
+        assert (h[shift_words + m:] == SENTINEL).all(), what
+
+    want, m = oracle.compact_i32(x, oracle.PRED_NONZERO)
+    _, cnt = ssc.compact(xd, "nonzero", out=out)
+    assert int(host(cnt)[0]) == m
+    check(want, m, "compact")
+    base.fill_(SENTINEL)
+    pw, k = oracle.partition_i32(x, oracle.PRED_EVEN)
+    _, kc = ssc.partition(xd, "even", out=out)
+    assert int(host(kc)[0]) == k
+    check(pw, n, "partition")
+    base.fill_(SENTINEL)
+    iw, mi = oracle.select_index_i32(x, oracle.PRED_NONZERO)
+    _, ci = ssc.select_index(xd, "nonzero", out=out)
+    assert int(host(ci)[0]) == mi
+    check(iw, mi, "select")
+
+
 def test_look_back_wait_is_bounded_and_reported():
     """A descriptor that is never published must not keep the kernel
     running: the host starts a fresh scratch's tile counter at 1, so tile 0
