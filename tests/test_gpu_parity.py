@@ -516,6 +516,7 @@ def test_keep_all_is_copy_and_keep_none_writes_nothing():
     assert checks.first_mismatch(host(out), x) == -1
     check_compact(np.zeros(7 * T + 77, np.int32), "nonzero")   # count 0, out untouched
     check_partition(x, "mod_lt", 100, 0)                        # nothing kept: out == in
+    check_partition(x, "nonzero")   # everything kept: each rejected run starts at its region's end
 
 
 @pytest.mark.parametrize("n", [S - 3, 3 * T + 611, 100_003])
