@@ -1,0 +1,101 @@
+"""Seeded random parity sweep (GPU): many sizes, output offsets and
+predicates, each case checked element by element against the oracle.
+
+The fixed edge cases elsewhere pin the tile and chunk boundaries; this sweep
+varies everything at once, the way a caller's arrays would: sizes from one
+element to four tiles, outputs that are 128-byte aligned, 16-byte aligned
+but inside a 128-byte line (runs are stored by line), or only 4-byte
+aligned (the 32-bit path), and every int32 predicate with random arguments.
+Compaction (with and without ranks), partition, selection and the exclusive
+scan run on the same input; words around every output must stay untouched."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_stream_compaction_amd as ssc
+from scan_stream_compaction_amd import workloads as wl
+from tests import checks
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+T = 30720                      # elements per tile of the single pass
+SENTINEL = -123456789
+CASES = 48
+OFFSETS = (0, 1, 4, 12, 33)    # output offset in 32-bit words
+
+
+def _case(i: int):
+    """Size, output offset, predicate and input of case i (all seeded)."""
+    rng = np.random.default_rng(0x5EED0A00 + i)
+    n = int(rng.integers(1, 3000)) if i % 4 == 0 else int(rng.integers(1, 4 * T + 1))
+    off = OFFSETS[i % len(OFFSETS)]
+    kind = i % 6
+    if kind in (3, 4):
+        pred, pa, pb = ("bit_set", "bit_clear")[kind - 3], int(rng.integers(0, 32)), 0
+    elif kind == 5:
+        pa = int(rng.integers(1, 1001))
+        pred, pb = "mod_lt", int(rng.integers(-1, pa + 2))
+    else:
+        pred, pa, pb = ("nonzero", "odd", "even")[kind], 0, 0
+    if i % 3 == 0:
+        x = wl.uniform_below(0x5EED0B00 + i, n, int(rng.integers(2, 11)))
+    else:
+        x = wl.full_int32(0x5EED0C00 + i, n)
+    return n, off, pred, pa, pb, x
+
+
+def _framed(n: int, off: int):
+    """An output view of n words at `off` words into a sentinel-filled buffer."""
+    base = torch.full((n + off + 64,), SENTINEL, dtype=torch.int32, device=DEV)
+    return base, base[off:off + n]
+
+
+def _check_frame(base: torch.Tensor, off: int, written: int, what: str):
+    h = base.cpu().numpy()
+    assert (h[:off] == SENTINEL).all(), f"{what}: words before the output written"
+    assert (h[off + written:] == SENTINEL).all(), f"{what}: words past the output written"
+
+
+@pytest.mark.parametrize("i", range(CASES))
+def test_random_case_matches_the_oracle(i):
+    n, off, pred, pa, pb, x = _case(i)
+    p = ssc.PRED[pred]
+    tag = f"case {i}: n={n} off={off} {pred}({pa}, {pb})"
+    xd = torch.from_numpy(x).to(DEV)
+
+    want, m, want_ranks = oracle.compact_i32(x, p, pa, pb, want_ranks=True)
+    base, out = _framed(n, off)
+    if i % 2 == 0:
+        ranks = torch.empty(n, dtype=torch.int32, device=DEV)
+        _, cnt, rk = ssc.compact(xd, pred, pa, pb, out=out, ranks=ranks)
+        assert checks.first_mismatch(rk.cpu().numpy(), want_ranks) == -1, tag + " ranks"
+    else:
+        _, cnt = ssc.compact(xd, pred, pa, pb, out=out)
+    assert int(cnt.cpu()[0]) == m, tag
+    assert checks.first_mismatch(base.cpu().numpy()[off:off + m], want) == -1, tag + " compact"
+    _check_frame(base, off, m, tag + " compact")
+
+    pw, k = oracle.partition_i32(x, p, pa, pb)
+    base, out = _framed(n, off)
+    _, kc = ssc.partition(xd, pred, pa, pb, out=out)
+    assert int(kc.cpu()[0]) == k, tag
+    assert checks.first_mismatch(base.cpu().numpy()[off:off + n], pw) == -1, tag + " partition"
+    _check_frame(base, off, n, tag + " partition")
+
+    iw, mi = oracle.select_index_i32(x, p, pa, pb)
+    base, out = _framed(n, off)
+    _, ci = ssc.select_index(xd, pred, pa, pb, out=out)
+    assert int(ci.cpu()[0]) == mi, tag
+    assert checks.first_mismatch(base.cpu().numpy()[off:off + mi], iw) == -1, tag + " select"
+    _check_frame(base, off, mi, tag + " select")
+
+    sw, total = oracle.exclusive_scan_i32(x)
+    base, out = _framed(n, off)
+    _, tot = ssc.exclusive_scan(xd, out=out)
+    assert int(tot.cpu()[0]) == total, tag
+    assert checks.first_mismatch(base.cpu().numpy()[off:off + n], sw) == -1, tag + " scan"
+    _check_frame(base, off, n, tag + " scan")
