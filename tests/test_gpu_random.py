@@ -99,3 +99,66 @@ def test_random_case_matches_the_oracle(i):
     assert int(tot.cpu()[0]) == total, tag
     assert checks.first_mismatch(base.cpu().numpy()[off:off + n], sw) == -1, tag + " scan"
     _check_frame(base, off, n, tag + " scan")
+
+
+FORMAT_CASES = 30
+OFFSETS64 = (0, 1, 2, 5)       # output offset in 64-bit elements (2: 16 bytes into a line)
+SENTINEL64 = -1234567890123
+
+
+@pytest.mark.parametrize("i", range(FORMAT_CASES))
+def test_random_format_case_matches_the_oracle(i):
+    """64-bit elements, flag bytes (values and positions) and key-value pairs
+    with random sizes, output offsets and predicates."""
+    rng = np.random.default_rng(0x5EED0D00 + i)
+    n = int(rng.integers(1, 2000)) if i % 3 == 0 else int(rng.integers(1, 2 * T + 1))
+    tag = f"case {i}: n={n}"
+
+    # 64-bit elements: predicates on all 64 bits
+    kind = i % 5
+    pred = ("nonzero", "odd", "even", "bit_set", "bit_clear")[kind]
+    bit = int(rng.integers(0, 64)) if kind >= 3 else 0
+    off = OFFSETS64[i % len(OFFSETS64)]
+    x64 = wl.full_int64(0x5EED0E00 + i, n)
+    want, m = oracle.compact_i64(x64, ssc.PRED[pred], bit)
+    base = torch.full((n + off + 32,), SENTINEL64, dtype=torch.int64, device=DEV)
+    _, cnt = ssc.compact(torch.from_numpy(x64).to(DEV), pred, bit, out=base[off:off + n])
+    assert int(cnt.cpu()[0]) == m, tag + f" i64 {pred}({bit}) off={off}"
+    h = base.cpu().numpy()
+    assert checks.first_mismatch(h[off:off + m], want) == -1, tag + " i64"
+    assert (h[:off] == SENTINEL64).all() and (h[off + m:] == SENTINEL64).all(), tag + " i64 frame"
+
+    # flag bytes: values moved, and positions
+    off32 = OFFSETS[i % len(OFFSETS)]
+    f = wl.flag_bytes(0x5EED0F00 + i, n, int(rng.integers(0, 101)))
+    x = wl.full_int32(0x5EED1000 + i, n)
+    fd = torch.from_numpy(f).to(DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    wf, mf = oracle.compact_flags(x, f)
+    base32, out32 = _framed(n, off32)
+    _, cf = ssc.compact_flags(xd, fd, out=out32)
+    assert int(cf.cpu()[0]) == mf, tag + f" flags off={off32}"
+    assert checks.first_mismatch(base32.cpu().numpy()[off32:off32 + mf], wf) == -1, tag + " flags"
+    _check_frame(base32, off32, mf, tag + " flags")
+    wi, mi = oracle.select_flags(f)
+    base32, out32 = _framed(n, off32)
+    _, ci = ssc.select_flags(fd, out=out32)
+    assert int(ci.cpu()[0]) == mi, tag + " select_flags"
+    assert checks.first_mismatch(base32.cpu().numpy()[off32:off32 + mi], wi) == -1, tag + " select_flags"
+    _check_frame(base32, off32, mi, tag + " select_flags")
+
+    # key-value pairs: the predicate on the keys, values carried
+    pk = ("nonzero", "odd", "even", "mod_lt")[i % 4]
+    pa, pb = (int(rng.integers(1, 200)), int(rng.integers(0, 200))) if pk == "mod_lt" else (0, 0)
+    keys = wl.uniform_below(0x5EED1100 + i, n, 7) if i % 2 else x
+    vals = wl.full_int32(0x5EED1200 + i, n)
+    wk, wv, mk = oracle.compact_kv(keys, vals, ssc.PRED[pk], pa, pb)
+    bk, ok_ = _framed(n, off32)
+    bv, ov = _framed(n, off32)
+    _, _, ck = ssc.compact_kv(torch.from_numpy(keys).to(DEV), torch.from_numpy(vals).to(DEV), pk,
+                              pa, pb, keys_out=ok_, vals_out=ov)
+    assert int(ck.cpu()[0]) == mk, tag + f" kv {pk}({pa}, {pb})"
+    assert checks.first_mismatch(bk.cpu().numpy()[off32:off32 + mk], wk) == -1, tag + " kv keys"
+    assert checks.first_mismatch(bv.cpu().numpy()[off32:off32 + mk], wv) == -1, tag + " kv values"
+    _check_frame(bk, off32, mk, tag + " kv keys")
+    _check_frame(bv, off32, mk, tag + " kv values")
