@@ -612,6 +612,7 @@ template <bool VEC>
 struct FmtB32 {
     using Shape = ChunkShape<8, 4>;
     static constexpr bool kVec = VEC;
+    static constexpr bool kValues = true;  // element values are loaded
     struct Regs {
         int32_t v[8][4];
     };
@@ -641,6 +642,7 @@ template <bool VEC, bool VALUES>
 struct FmtFlags {
     using Shape = ChunkShape<8, 4>;
     static constexpr bool kVec = VEC;
+    static constexpr bool kValues = VALUES;
     struct Regs {
         int32_t v[8][4];
         uint32_t f[8];
@@ -683,6 +685,7 @@ template <bool VEC>
 struct FmtPairs {
     using Shape = ChunkShape<4, 4>;
     static constexpr bool kVec = VEC;
+    static constexpr bool kValues = true;
     struct Regs {
         int32_t k[4][4];
         int32_t v[4][4];
@@ -732,6 +735,7 @@ template <bool VEC>
 struct FmtB64 {
     using Shape = ChunkShape<8, 2>;
     static constexpr bool kVec = VEC;
+    static constexpr bool kValues = true;
     struct Regs {
         uint64_t v[8][2];
     };
@@ -789,7 +793,7 @@ struct FmtB64 {
 //   1. stages the current chunk's survivors at their rank in its own LDS
 //      region (for a partition the rejected ones after them);
 //   2. issues the loads of the tile after next into the registers that just
-//      freed up;
+//      freed up (with a third register set, before step 1: see three_sets);
 //   3. flags the next tile's chunk (waiting only for those loads), writes
 //      its total to LDS and arrives; the last of the 15 to arrive scans the
 //      totals and publishes the next tile's {aggregate} at once;
@@ -823,10 +827,30 @@ struct FmtB64 {
 // next launch (the radix driver's chained splits): its runs are stored with
 // the default cache policy throughout.
 enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3, kPartitionCached = 4 };
-// look-back poll interval, s_sleep units: 16 and 32 measured equal at 50% kept,
-// 16 about 1% faster at 1% kept (215.5 against 218.2 us at 2^28)
-constexpr int kSelPollSleep = 16;
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+
+// Register sets per data wavefront. With two, the loads of the tile after next
+// reuse the current chunk's registers, so they leave only once that chunk is
+// staged; with three they leave before the staging. Which one a kernel takes
+// is measured (2^28 elements, microseconds per launch, two sets -> three):
+//   three: odd 50% kept 285.4 -> 274.4, odd 1% 210.9 -> 206.8, odd
+//     selection 283.6 -> 275.4, int64 279.1 -> 275.8, key-value pairs
+//     283.7 -> 270.7, flag-byte compaction 327.4 -> 317.0;
+//   two: MOD_LT(100, s) s = 1 / 10 / 99 (216 -> 233 / 231 -> 240 / 367 ->
+//     372; 50%: 289 -> 281), ranks 463 -> 476, partitions 537 -> 540, the
+//     radix driver's chained splits (2^24 keys, 1,176 -> 1,210 a sort), and
+//     selection by flag bytes 181 -> 192.
+template <class F, int P, int KIND>
+constexpr bool three_sets() {
+    return (KIND == kCompact || KIND == kSelectIndex) && P != 5 && F::kValues;
+}
+// The look-back with three sets goes straight to its window and polls at
+// s_sleep 32; with two it first waits on its predecessor and polls at s_sleep
+// 16 (each measured best for its pipeline).
+template <bool THREE>
+constexpr int sel_poll_sleep() {
+    return THREE ? 32 : 16;
+}
 
 // F is the element format (what a chunk holds and how survivors are staged
 // and written); partition and ranks are defined for 32-bit elements.
@@ -848,6 +872,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
     __shared__ uint32_t s_first[3], s_epoch, s_arrive;
 
+    constexpr bool kThree = three_sets<F, P, KIND>();
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
@@ -890,7 +915,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             }
             uint32_t prefix = 0;
             if (tile != 0)
-                prefix = look_back<SumU32, kSelPollSleep>(sv.desc, tile, tag, sv.timed_out);
+                prefix = look_back<SumU32, sel_poll_sleep<kThree>(), !kThree>(sv.desc, tile, tag,
+                                                                              sv.timed_out);
             if (lane == 0) {
                 s_base[par] = prefix;
                 s_next[par] = nxt3;
@@ -916,7 +942,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
 
     const uint32_t kept = kPart ? static_cast<uint32_t>(*kept_total) : 0u;
-    typename F::Regs va, vb;
+    typename F::Regs va, vb, vc;  // vc: the third set (kThree)
     uint32_t fm_cur = 0, fm_nxt = 0;  // flags of the current / next chunk
     uint32_t a_cur = 0, a_nxt = 0;    // their totals
     uint32_t rem_cur = 0, rem_nxt = 0;
@@ -957,12 +983,14 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         }                                                                                     \
     }
 
-    // One tile (steps 1-5 above) with CUR holding the current chunk and NX
-    // the next one in flight; the loop below alternates the two register sets.
-#define SSC_TILE(CUR, NX)                                                                     \
+    // One tile (steps 1-5 above) with CUR holding the current chunk, NX the
+    // next one in flight and, with three sets, FREE the registers of the chunk
+    // staged one tile ago; the loop below rotates the register sets.
+#define SSC_TILE(CUR, NX, FREE)                                                               \
     {                                                                                         \
         int ln = lane;                                                                        \
         asm volatile("" : "+v"(ln));                                                          \
+        if constexpr (kThree) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, FREE);             \
         {                                                                                     \
             /* a partition gives every element a slot of its own, no branches:   */            \
             /* survivors at their rank, the others after all survivors at a_cur + */            \
@@ -990,7 +1018,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
                 }                                                                             \
             }                                                                                 \
         }                                                                                     \
-        F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, CUR);                                    \
+        if constexpr (!kThree) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, CUR);             \
         const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                     \
         rem_nxt = rem_of(nxt);                                                                \
         SSC_FLAG_AND_ARRIVE(NX, nxt, rem_nxt, fm_nxt, a_nxt, tri_n, ln)                       \
@@ -1031,11 +1059,22 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // B0': without it a fast wavefront could arrive for the next tile
     // before a slow one has arrived for this one
     __syncthreads();
-    while (true) {
-        SSC_TILE(va, vb)
-        if (tile >= num_tiles) break;
-        SSC_TILE(vb, va)
-        if (tile >= num_tiles) break;
+    if constexpr (kThree) {
+        while (true) {
+            SSC_TILE(va, vb, vc)
+            if (tile >= num_tiles) break;
+            SSC_TILE(vb, vc, va)
+            if (tile >= num_tiles) break;
+            SSC_TILE(vc, va, vb)
+            if (tile >= num_tiles) break;
+        }
+    } else {
+        while (true) {
+            SSC_TILE(va, vb, va)
+            if (tile >= num_tiles) break;
+            SSC_TILE(vb, va, vb)
+            if (tile >= num_tiles) break;
+        }
     }
 #undef SSC_TILE
 #undef SSC_FLAG_AND_ARRIVE

@@ -168,6 +168,10 @@ __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
 // 3.4 us (s_sleep 127) is best; the persistent compaction kernel, whose
 // control wavefronts wait on tiles published earlier, polls at s_sleep 16.
 //
+// With PRED_FIRST false the wavefront skips that first wait and polls the
+// window itself: for a caller whose predecessor has almost always published
+// already, the lone poll is one coherent round trip spent for nothing.
+//
 // Walking: then each step reads the descriptors of the 64 tiles just below
 // the window end at once (one load, 512 contiguous bytes). The window is
 // usable once the nearest tile with an {inclusive} value is nearer than every
@@ -210,7 +214,7 @@ __device__ __forceinline__ uint32_t status_of(uint64_t word, uint32_t tag) {
 // slower on MI355X: the extra coherent traffic costs more than the steps saved.
 constexpr int kLookBackWindows = 1;
 
-template <class Op, int SLEEP>
+template <class Op, int SLEEP, bool PRED_FIRST = true>
 __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
                                     uint32_t *timed_out) {
     using T = typename Op::T;
@@ -218,7 +222,7 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
     T prefix = Op::zero();
     uint32_t spins = 0;
     // wait on the immediate predecessor alone
-    while (true) {
+    while (PRED_FIRST) {
         uint64_t w1 = 0;
         if (lane == 0) w1 = peek_tile(desc, static_cast<int32_t>(tile) - 1, tag);
         if (status_of(w1, tag) != 0u && lane == 0) spins |= 0x80000000u;
