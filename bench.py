@@ -105,75 +105,208 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
-def cpu_baseline(x_np, target_s: float = 12.0):
-    """Sequential oracle compaction (predicate odd) on the host, 1 thread.
-    Runs the full input repeatedly until about target_s of CPU time has
-    been spent (at least once), and reports GB/s over the same algorithmic
-    bytes as the GPU figure."""
-    import ctypes
+def _median_of_3(fn):
+    """Median wall time of three runs after one warm-up run."""
+    fn()
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return sorted(times)[1]
 
+
+def cpu_baseline(x_np):
+    """The sequential CPU oracle (one thread) on every workload, each on the
+    same seeded input the GPU rows use: median of three runs after one
+    warm-up, GB/s over the same algorithmic bytes as the GPU figures. The
+    headline entry (2^28 odd compaction) is the one in the metric's unit; the
+    others are listed under per_config."""
     import numpy as np
 
     import oracle
-    L = oracle.lib()
+    from scan_stream_compaction_amd import workloads as wl
+
+    rows = []
+
+    def row(name, fn, n, alg_bytes, **info):
+        t = _median_of_3(fn)
+        rows.append({"workload": name, "ms": round(t * 1e3, 2), "GB/s": round(alg_bytes / t / 1e9, 3),
+                     "elements_per_s": round(n / t, 1), "algorithmic_bytes": alg_bytes, **info})
+        log(f"cpu oracle {name}: {t * 1e3:.1f} ms")
+
     n = x_np.size
-    out = np.empty(n, np.int32)
-    ip = x_np.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    op = out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    times = []
-    m = 0
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        m = L.orc_compact_i32(ip, op, n, oracle.PRED_ODD, 0, 0, None)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start >= target_s or len(times) >= 10:
-            break
-    med = sorted(times)[len(times) // 2]
-    alg = 4 * n + 4 * m
+    m = oracle.count(x_np, oracle.PRED_ODD)
+    row("ordered compaction, 2^28 full-range int32, odd", lambda: oracle.compact_i32(x_np, oracle.PRED_ODD),
+        n, 4 * n + 4 * m, kept=int(m))
+    head = rows[-1]
+    x1 = wl.small_compact_input()
+    k1 = oracle.count(x1, oracle.PRED_NONZERO)
+    row("compaction with ranks, 65,533 int32 in [0,4), nonzero",
+        lambda: oracle.compact_i32(x1, oracle.PRED_NONZERO, want_ranks=True), x1.size, 8 * x1.size + 4 * k1)
+    x2 = wl.zero_removal_input()
+    k2 = oracle.count(x2, oracle.PRED_NONZERO)
+    row("zero removal, 8,387,997 int32 in [0,10)", lambda: oracle.compact_i32(x2, oracle.PRED_NONZERO),
+        x2.size, 4 * x2.size + 4 * k2)
+    row("even/odd stable partition, 8,387,997 int32", lambda: oracle.partition_i32(x2, oracle.PRED_EVEN),
+        x2.size, 8 * x2.size)
+    x3 = wl.mod8_plus1(wl.N_SCAN)
+    row("exclusive scan, 10^7 int32 (i % 8) + 1", lambda: oracle.exclusive_scan_i32(x3), x3.size, 8 * x3.size)
+    x3f = wl.scan_f32_input()
+    row("exclusive scan, 10^7 fp32 in [0,1) (fp64 accumulation)", lambda: oracle.exclusive_scan_f32(x3f),
+        x3f.size, 8 * x3f.size)
+    x5 = wl.radix_input()
+    row("radix sort, 2^24 uint32, 32 chained one-bit partitions", lambda: oracle.radix_sort_u32(x5),
+        x5.size, 32 * 8 * x5.size)
+    row("std::sort check of the same keys (numpy sort)", lambda: np.sort(x5), x5.size, 8 * x5.size)
     return {
-        "value": round(alg / med / 1e9, 3),
+        "value": head["GB/s"],
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"full 2^28-element input, sequential orc_compact_i32 (odd), "
-                   f"median of {len(times)} runs ({med * 1e3:.1f} ms each), "
-                   f"{cpu_model()}, "
-                   f"host has {os.cpu_count()} logical CPUs, 1 thread used"),
-        "elements_per_s": round(n / med, 1),
-        "kept": int(m),
+        "sample": (f"full inputs of all five workloads, sequential C oracle, median of 3 runs after "
+                   f"1 warm-up each; headline: 2^28 orc_compact_i32 (odd) {head['ms']} ms; "
+                   f"{cpu_model()}, host has {os.cpu_count()} logical CPUs, 1 thread used"),
+        "elements_per_s": head["elements_per_s"],
+        "kept": head["kept"],
+        "per_config": rows,
     }
 
 
+def recheck(name, scratch, check=None):
+    """After a timed region: the scratch's look-back time-out flag must be
+    clear and (when given) the output must still be right; otherwise the row
+    is not reported."""
+    import scan_stream_compaction_amd as ssc
+    if scratch is not None and ssc.timed_out(scratch):
+        raise RuntimeError(f"{name}: a look-back wait timed out during the timed calls")
+    if check is not None and not check():
+        raise RuntimeError(f"{name}: output wrong after the timed calls")
+
+
 def pipeline_rows(x, m: int, stream, steps: int, copy_us: float) -> dict:
-    """The pages' "where the time goes" rows on this hardware: the
-    multi-launch compaction (mark, tree scan of the flags, scatter) and its
-    parts against the single pass, each as a multiple of the copy kernel's
-    time. Each result is checked first."""
+    """The pages' "where the time goes" rows on this hardware ("Day 33
+    compaction.cu", its timing table): copy, mark alone, the multi-launch scan
+    of the flags, scatter alone, the multi-launch compaction, the single pass,
+    the stable partition and the atomic comparison, each as a multiple of the
+    copy kernel's time. Each result is checked first."""
     import torch
 
     import scan_stream_compaction_amd as ssc
     n = x.numel()
     out = torch.empty_like(x)
     ranks = torch.empty_like(x)
+    flags = torch.empty_like(x)
     cnt = torch.zeros(1, dtype=torch.int32, device=x.device)
+    mask = (x & 1).bool()
+    want = torch.masked_select(x, mask)
     sc = ssc.multipass_scratch(n, x.device)
     mp = ssc.prepared(ssc.compact_multipass, x, "odd", out=out, count=cnt, ranks=ranks, scratch=sc)
     torch.cuda.synchronize()
-    assert int(cnt.item()) == m and torch.equal(out[:m], torch.masked_select(x, (x & 1).bool()))
-    scan = ssc.prepared(ssc.exclusive_scan_multipass, ranks, out=ranks, scratch=sc)
+    assert int(cnt.item()) == m and torch.equal(out[:m], want)
     rows = {}
 
-    def row(name, fn, launches):
-        _, ms, _ = timed_calls(fn, steps, stream)
+    def row(name, fn, launches, check=None, scratch=None, calls=steps):
+        _, ms, _ = timed_calls(fn, calls, stream)
+        recheck(name, scratch, check)
         rows[name] = {"launches": launches, "us": round(ms * 1e3, 2),
                       "x_copy": round(ms * 1e3 / copy_us, 3)}
 
-    row("compaction, multi-launch (mark, scan, scatter)", mp, 7)
-    row("scan of 2^28 flags, multi-launch", scan, 5)
-    single = ssc.prepared(ssc.compact, x, "odd", out=out, count=cnt)
-    row("compaction, single pass (this library)", single, 1)
     rows["copy in to out"] = {"launches": 1, "us": copy_us, "x_copy": 1.0}
+    mk = ssc.prepared(ssc.mark, x, "odd", out=flags)
+    torch.cuda.synchronize()
+    assert torch.equal(flags, mask.to(torch.int32))
+    row("mark (flags written)", mk, 1, lambda: torch.equal(flags, mask.to(torch.int32)))
+    scan = ssc.prepared(ssc.exclusive_scan_multipass, flags, out=ranks, scratch=sc)
+    row("scan of the 2^28 flags, multi-launch", scan, 5)
+    sc_out = torch.empty_like(x)
+    scat = ssc.prepared(ssc.scatter, x, ranks, "odd", out=sc_out, count=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == m and torch.equal(sc_out[:m], want)
+    row("scatter alone (ranks given)", scat, 1, lambda: int(cnt.item()) == m and torch.equal(sc_out[:m], want))
+    row("compaction, multi-launch (mark, scan, scatter)", mp, 7,
+        lambda: int(cnt.item()) == m and torch.equal(out[:m], want))
+    ss = ssc.new_scratch(n, x.device)
+    single = ssc.prepared(ssc.compact, x, "odd", out=out, count=cnt, scratch=ss)
+    row("compaction, single pass (this library)", single, 1,
+        lambda: int(cnt.item()) == m and torch.equal(out[:m], want), ss)
+    part = ssc.prepared(ssc.partition, x, "odd", out=out, count=cnt, scratch=ss)
+    torch.cuda.synchronize()
+    pwant = torch.cat([want, torch.masked_select(x, ~mask)])
+    assert int(cnt.item()) == m and torch.equal(out, pwant)
+    row("stable partition (count pass + single pass)", part, 2,
+        lambda: int(cnt.item()) == m and torch.equal(out, pwant), ss)
+    del pwant
+    for variant, name in ((1, "atomic compaction, one atomicAdd per survivor (compactAtomic form)"),
+                          (0, "atomic compaction, one atomicAdd per 8192-element workgroup")):
+        fa = ssc.prepared(ssc.compact_atomic, x, "odd", variant=variant, out=out, count=cnt)
+        torch.cuda.synchronize()
+        assert int(cnt.item()) == m and torch.equal(torch.sort(out[:m]).values, torch.sort(want).values)
+        # the per-survivor form takes tens of milliseconds a call: a few calls
+        row(name, fa, 1, lambda: int(cnt.item()) == m, calls=steps if variant == 0 else 3)
+    return rows
+
+
+def hbm_rows(x, dev, steps: int, stream) -> dict:
+    """The other 2^28 operations of the path, HBM-bound like the headline:
+    stable partition (a counting read, then the single pass) and the
+    exclusive scans of int32 and fp32 values, each checked before and after
+    its timed calls."""
+    import torch
+
+    import scan_stream_compaction_amd as ssc
+    from scan_stream_compaction_amd import workloads as wl
+
+    rows = {}
+    n = x.numel()
+    out = torch.empty_like(x)
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    sc = ssc.new_scratch(n, dev)
+
+    def timed(name, fn, alg_bytes, check, **info):
+        _, per_ms, _ = timed_calls(fn, steps, stream)
+        recheck(name, sc, check)
+        us = per_ms * 1e3
+        gbs = alg_bytes / (us * 1e-6) / 1e9
+        rows[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                      "pct_hbm_peak": round(gbs / HBM_PEAK_GBPS * 100, 1),
+                      "algorithmic_bytes": alg_bytes, **info}
+
+    ev = (x & 1) == 0
+    k = int(ev.sum())
+    pwant = torch.cat([x[ev], x[~ev]])
+    del ev
+    fn = ssc.prepared(ssc.partition, x, "even", out=out, count=cnt, scratch=sc)
+    torch.cuda.synchronize()
+    ok = lambda: int(cnt.item()) == k and torch.equal(out, pwant)
+    assert ok()
+    timed("partition_even_2p28", fn, 8 * n, ok, kept=k,
+          note="algorithmic 8N; the counting pass before the single pass reads another 4N (12N moved)")
+    del pwant
+    c = torch.cumsum(x.to(torch.int64), 0)
+    swant = ((c - x.to(torch.int64)) & 0xFFFFFFFF).to(torch.int64)
+    del c
+    tot = torch.zeros(1, dtype=torch.int32, device=dev)
+    fn = ssc.prepared(ssc.exclusive_scan, x, out=out, total=tot, scratch=sc)
+    torch.cuda.synchronize()
+    ok = lambda: torch.equal(out.to(torch.int64) & 0xFFFFFFFF, swant)
+    assert ok()
+    timed("exclusive_scan_i32_2p28", fn, 8 * n, ok, note="full-range int32, wrapping sums; 8N")
+    del swant
+    xf = torch.from_numpy(wl.unit_float32(0x5EED0107, n)).to(dev)
+    outf = torch.empty_like(xf)
+    totf = torch.zeros(1, dtype=torch.float32, device=dev)
+    ref = torch.cumsum(xf.to(torch.float64), 0) - xf.to(torch.float64)
+
+    def fok():
+        rel = ((outf[1:].to(torch.float64) - ref[1:]).abs() / ref[1:].abs()).max()
+        return float(outf[0]) == 0.0 and float(rel) <= 1e-5
+    fn = ssc.prepared(ssc.exclusive_scan, xf, out=outf, total=totf, scratch=sc)
+    torch.cuda.synchronize()
+    assert fok()
+    rel = float(((outf[1:].to(torch.float64) - ref[1:]).abs() / ref[1:].abs()).max())
+    timed("exclusive_scan_f32_2p28", fn, 8 * n, fok, max_rel_err=rel,
+          note="uniform [0, 1), fp64 carries between tiles; 8N")
     return rows
 
 
@@ -190,8 +323,9 @@ def format_rows(x, out, dev, steps: int, stream) -> dict:
 
     rows = {}
 
-    def timed(name, fn, alg_bytes, **info):
+    def timed(name, fn, alg_bytes, check=None, **info):
         _, per_ms, _ = timed_calls(fn, steps, stream)
+        recheck(name, sc, check)
         us = per_ms * 1e3
         gbs = alg_bytes / (us * 1e-6) / 1e9
         rows[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
@@ -199,42 +333,43 @@ def format_rows(x, out, dev, steps: int, stream) -> dict:
                       "algorithmic_bytes": alg_bytes, **info}
 
     n = x.numel()
+    sc = ssc.new_scratch(n, dev)
     f = torch.from_numpy(wl.flag_bytes(0x5EED0104, n, 50)).to(dev)
     mask = f != 0
     k = int(mask.sum())
     cnt = torch.zeros(1, dtype=torch.int32, device=dev)
-    fn = ssc.prepared(ssc.compact_flags, x, f, out=out, count=cnt)
+    fn = ssc.prepared(ssc.compact_flags, x, f, out=out, count=cnt, scratch=sc)
     torch.cuda.synchronize()
     assert int(cnt.item()) == k and torch.equal(out[:k], torch.masked_select(x, mask))
-    timed("compact_flags_2p28", fn, 5 * n + 4 * k, kept=k,
+    timed("compact_flags_2p28", fn, 5 * n + 4 * k, lambda: int(cnt.item()) == k, kept=k,
           note="4-byte values and one flag byte each read, survivors written: 5N + 4K")
-    fn = ssc.prepared(ssc.select_flags, f, out=out, count=cnt)
+    fn = ssc.prepared(ssc.select_flags, f, out=out, count=cnt, scratch=sc)
     torch.cuda.synchronize()
     assert int(cnt.item()) == k and torch.equal(out[:k], torch.nonzero(mask).flatten().to(torch.int32))
-    timed("select_flags_2p28", fn, n + 4 * k, kept=k, note="flag bytes read, positions written: N + 4K")
+    timed("select_flags_2p28", fn, n + 4 * k, lambda: int(cnt.item()) == k, kept=k, note="flag bytes read, positions written: N + 4K")
     del f, mask
 
     h = n // 2
     keys = x[:h]
     vals = torch.from_numpy(wl.full_int32(0x5EED0105, h)).to(dev)
     ko, vo = out[:h], out[h:]
-    fn = ssc.prepared(ssc.compact_kv, keys, vals, "odd", keys_out=ko, vals_out=vo, count=cnt)
+    fn = ssc.prepared(ssc.compact_kv, keys, vals, "odd", keys_out=ko, vals_out=vo, count=cnt, scratch=sc)
     torch.cuda.synchronize()
     mask = (keys & 1) == 1
     k = int(mask.sum())
     assert int(cnt.item()) == k and torch.equal(ko[:k], keys[mask]) and torch.equal(vo[:k], vals[mask])
-    timed("compact_kv_odd_2p27", fn, 8 * h + 8 * k, kept=k,
+    timed("compact_kv_odd_2p27", fn, 8 * h + 8 * k, lambda: int(cnt.item()) == k, kept=k,
           note="2^27 int32 keys (odd kept) with int32 values: 8N + 8K")
     del vals, mask
 
     y = torch.from_numpy(wl.full_int64(0x5EED0106, h)).to(dev)
     out64 = out.view(torch.int64)
-    fn = ssc.prepared(ssc.compact, y, "odd", out=out64, count=cnt)
+    fn = ssc.prepared(ssc.compact, y, "odd", out=out64, count=cnt, scratch=sc)
     torch.cuda.synchronize()
     mask = (y & 1) == 1
     k = int(mask.sum())
     assert int(cnt.item()) == k and torch.equal(out64[:k], y[mask])
-    timed("compact_i64_odd_2p27", fn, 8 * h + 8 * k, kept=k, note="2^27 full-range int64, odd kept: 8N + 8K")
+    timed("compact_i64_odd_2p27", fn, 8 * h + 8 * k, lambda: int(cnt.item()) == k, kept=k, note="2^27 full-range int64, odd kept: 8N + 8K")
     return rows
 
 
@@ -254,6 +389,9 @@ def other_workloads(dev, steps: int, stream) -> dict:
     def timed(name, op, args, kwargs, alg_bytes, **info):
         fn = ssc.prepared(op, *args, **kwargs)
         _, per_ms, _ = timed_calls(fn, steps, stream)
+        # look-back scratches only (the multi-launch pipelines' scratch holds tile sums)
+        lookback = op not in (ssc.exclusive_scan_multipass, ssc.compact_multipass)
+        recheck(name, kwargs.get("scratch") if lookback else None)
         us = per_ms * 1e3
         rows[name] = {"us": round(us, 2), "effective_GB/s": round(alg_bytes / (us * 1e-6) / 1e9, 1),
                       "algorithmic_bytes": alg_bytes, **info}
@@ -388,27 +526,24 @@ def main():
         log(f"PARITY FAILED: count {m} vs {want_m}; no number reported")
         sys.exit(1)
     log(f"parity ok: kept {m} of {n} ({m / n:.5f})")
+    alg_bytes = 4 * n + 4 * m  # input read + survivors written
 
-    for _ in range(args.warmup):
-        step()
-    region_ms, ms_per_step, wall = timed_calls(step, args.steps, stream)
-    kernel_ms = ms_per_step  # one launch per step: the average launch duration over the region
-    alg_bytes = 4 * n + 4 * m
-    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-    log(f"compact odd: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s "
-        f"({value / HBM_PEAK_GBPS * 100:.1f}% of {HBM_PEAK_GBPS:.0f}), "
-        f"per-launch {kernel_ms * 1e3:.1f} us, wall {wall * 1e6 / args.steps:.1f} us/step")
-
+    # The headline is timed after the other rows have run: on this part the
+    # memory clocks settle some milliseconds into sustained streaming, and
+    # launches 11-40 after an idle period run about 4% slower than the
+    # sustained rate (per-launch kernel traces: launches 1-10 after 0.5 s idle
+    # 268 us, 11-30 277-279 us, 51-100 266 us; after 40 copy launches a flat
+    # 266 us). The first timed launches after the parity check are kept
+    # below as cold_us for the record.
+    _, cold_ms, _ = timed_calls(step, args.steps, stream)
     extra = {}
     if args.extra in ("all", "copy"):
         cp = torch.empty_like(x)
         _, cp_ms, _ = timed_calls(ssc.prepared(ssc.copy, x, cp), args.steps, stream)
-        assert torch.equal(cp, x)
+        recheck("copy", None, lambda: torch.equal(cp, x))
         cp_gbps = 8 * n / (cp_ms * 1e-3) / 1e9
         extra["copy_i32"] = {"us": round(cp_ms * 1e3, 2), "GB/s": round(cp_gbps, 1),
                              "bytes": 8 * n}
-        extra["compact_odd_pct_of_copy"] = round(achieved / cp_gbps * 100, 1)
         del cp
     if args.extra == "all":
         for s in wl.SWEEP_KEEP:
@@ -420,8 +555,10 @@ def main():
             mask = (torch.remainder(x, wl.SWEEP_MOD) < s)
             assert ms_ == int(mask.sum().item())
             assert torch.equal(out[:ms_], torch.masked_select(x, mask))
-            del mask
             _, k_ms, _ = timed_calls(fn, args.steps, stream)
+            recheck(f"compact_mod100_lt{s}", scratch,
+                    lambda: int(cnt.item()) == ms_ and torch.equal(out[:ms_], torch.masked_select(x, mask)))
+            del mask
             b = 4 * n + 4 * ms_
             extra[f"compact_mod100_lt{s}"] = {
                 "kept": ms_, "us": round(k_ms * 1e3, 2), "GB/s": round(b / (k_ms * 1e-3) / 1e9, 1),
@@ -429,7 +566,7 @@ def main():
             cnt2 = torch.zeros(1, dtype=torch.int32, device=dev)
             fa = ssc.prepared(ssc.compact_atomic, x, "mod_lt", wl.SWEEP_MOD, s, out=out, count=cnt2)
             _, k_ms, _ = timed_calls(fa, args.steps, stream)
-            assert int(cnt2.item()) == ms_
+            recheck(f"atomic_mod100_lt{s}", None, lambda: int(cnt2.item()) == ms_)
             extra[f"atomic_mod100_lt{s}"] = {
                 "us": round(k_ms * 1e3, 2), "GB/s": round(b / (k_ms * 1e-3) / 1e9, 1)}
     if args.extra == "all":
@@ -439,13 +576,30 @@ def main():
         torch.cuda.synchronize()
         assert int(cnt3.item()) == m and torch.equal(idx[:m], torch.nonzero(x & 1).flatten().to(torch.int32))
         _, k_ms, _ = timed_calls(fi, args.steps, stream)
+        recheck("select_index_odd_2p28", scratch, lambda: int(cnt3.item()) == m)
         extra["select_index_odd_2p28"] = {
             "us": round(k_ms * 1e3, 2), "GB/s": round(alg_bytes / (k_ms * 1e-3) / 1e9, 1),
             "note": "positions of the odd elements; same bytes as the compaction"}
         del idx
         extra["pipelines_x_copy"] = pipeline_rows(x, m, stream, args.steps, extra["copy_i32"]["us"])
+        extra["hbm_2p28"] = hbm_rows(x, dev, max(5, args.steps // 2), stream)
         extra["other_workloads"] = other_workloads(dev, max(5, args.steps // 5), stream)
         extra["other_formats"] = format_rows(x, out, dev, max(5, args.steps // 2), stream)
+    for _ in range(args.warmup):
+        step()
+    region_ms, ms_per_step, wall = timed_calls(step, args.steps, stream)
+    mask = (x & 1).bool()
+    recheck("headline", scratch, lambda: int(count.item()) == m and torch.equal(out[:m], torch.masked_select(x, mask)))
+    del mask
+    kernel_ms = ms_per_step  # one launch per step: the average launch duration over the region
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    log(f"compact odd: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s "
+        f"({value / HBM_PEAK_GBPS * 100:.1f}% of {HBM_PEAK_GBPS:.0f}), "
+        f"per-launch {kernel_ms * 1e3:.1f} us, wall {wall * 1e6 / args.steps:.1f} us/step")
+
+    if "copy_i32" in extra:
+        extra["compact_odd_pct_of_copy"] = round(achieved / extra["copy_i32"]["GB/s"] * 100, 1)
     if extra:
         log("extra: " + json.dumps(extra))
 
@@ -470,6 +624,7 @@ def main():
             "tile_elems": ssc.tile_elems(), "algorithmic_bytes": alg_bytes,
             "pct_hbm_peak": round(value / HBM_PEAK_GBPS * 100, 2),
             "elements_per_s": round(n / (ms_per_step * 1e-3), 1),
+            "cold_us": round(cold_ms * 1e3, 2),
         },
         "roofline": {
             "bound": "hbm",

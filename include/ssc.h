@@ -26,9 +26,13 @@
  *     call is a single kernel launch (two for a partition). Pass the same
  *     scratch_bytes every time a buffer is used. One scratch buffer must not
  *     serve two calls that may run at the same time (the calls race).
- *     Diagnostic: after a call completes, 32-bit word 2 of the scratch is 1
- *     if a look-back wait gave up after its bounded spin (results invalid;
- *     only possible on misuse such as an uninitialised scratch).
+ *     Diagnostic: a look-back wait that gives up after its bounded spin
+ *     (only possible on misuse, such as a scratch that was never zeroed or
+ *     one shared by two calls in flight) sets a time-out flag in the
+ *     scratch; ssc_scratch_timed_out reads it. Once set, the results of the
+ *     calls made with that scratch are invalid and the flag stays set: the
+ *     scratch must be re-initialised (ssc_scratch_init) before it is used
+ *     again.
  *   - Element pointers must be 4-byte aligned. 16-byte aligned arrays take
  *     the 128-bit load/store path; other arrays take a 32-bit path with the
  *     same results.
@@ -110,8 +114,17 @@ size_t ssc_radix_sort_scratch_bytes(int64_t n);
  * a 16 x ceil(n / 8192) table of per-tile digit counts, then the table. */
 size_t ssc_radix_sort4_scratch_bytes(int64_t n);
 
-/* Zero-fills a scratch buffer on `stream` (needed once, before first use). */
+/* Zero-fills a scratch buffer on `stream` (needed once, before first use,
+ * and again after a time-out, see below). */
 int ssc_scratch_init(void *scratch, size_t scratch_bytes, void *stream);
+
+/* Stream-ordered check of a scratch buffer: writes 1 to *flag (a device
+ * int32) if a look-back wait of a call made with this scratch gave up after
+ * its bounded spin since the scratch was last initialised, else 0. A set
+ * flag means those calls' results are invalid and the scratch needs
+ * ssc_scratch_init before further use; it never comes from a correct call.
+ * One tiny launch; flag must not lie inside the scratch. */
+int ssc_scratch_timed_out(const void *scratch, size_t scratch_bytes, int32_t *flag, void *stream);
 
 /* Exclusive scan of int32 values: out[0] = 0, out[i] = in[0] + ... + in[i-1],
  * with two's-complement wrap (sums taken modulo 2^32). `total` (nullable)
@@ -253,7 +266,8 @@ int ssc_select_index_i64(const int64_t *in, int32_t *idx, int64_t n, int pred, i
 int ssc_count_if_i32(const int32_t *in, int64_t n, int pred, int32_t pa, int32_t pb,
                      int32_t *count, void *scratch, size_t scratch_bytes, void *stream);
 
-/* Unordered compaction by atomic counter, kept only for comparison:
+/* Unordered compaction by atomic counter, kept only for comparison (it
+ * needs no scratch: its counter is *count itself):
  * out[0 .. count) holds the same multiset as ssc_compact_i32's output, in
  * an order the hardware scheduler decides. variant 0: one atomicAdd per
  * 512-thread workgroup and 8192-element tile (its survivors keep tile
@@ -310,9 +324,24 @@ int ssc_compact_multipass_i32(const int32_t *in, int32_t *out, int64_t n, int pr
                               int32_t pb, int32_t *count, int32_t *ranks, void *scratch,
                               size_t scratch_bytes, void *stream);
 
-/* out[i] = in[i] with 128-bit loads and stores: the bandwidth reference the
- * single pass is compared with ("Day 33 compaction.cu", copyInts; "Day 32
- * scan_2.cu", copyFloats). No overlap allowed. */
+/* Comparison only, the separate steps of that multi-launch compaction, so
+ * that each can be timed alone ("Day 33 compaction.cu", markNonZero /
+ * markEven and scatterCompact, and its table of where the time goes):
+ * ssc_mark_i32 writes flags[i] = P(in[i]) (0 or 1) for every i;
+ * ssc_scatter_i32 writes out[ranks[i]] = in[i] for every i with P(in[i])
+ * (the predicate evaluated again, not read back) given the exclusive scan
+ * of the flags in `ranks`, and *count = ranks[n-1] + P(in[n-1]). A rank
+ * outside [0, n) is skipped. No overlap of the arrays is allowed. */
+int ssc_mark_i32(const int32_t *in, int32_t *flags, int64_t n, int pred, int32_t pa, int32_t pb,
+                 void *stream);
+int ssc_scatter_i32(const int32_t *in, const int32_t *ranks, int32_t *out, int64_t n, int pred,
+                    int32_t pa, int32_t pb, int32_t *count, void *stream);
+
+/* out[i] = in[i] with 128-bit nontemporal loads and stores (32-bit ones when
+ * either array is not 16-byte aligned), one 256-thread workgroup per 4096
+ * elements: the bandwidth reference the single pass is compared with ("Day
+ * 33 compaction.cu", copyInts; "Day 32 scan_2.cu", copyFloats). No overlap
+ * allowed. */
 int ssc_copy_i32(const int32_t *in, int32_t *out, int64_t n, void *stream);
 
 /* Human-readable name of a status code (static storage). */

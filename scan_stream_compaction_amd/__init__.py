@@ -55,6 +55,9 @@ SIGNATURES = {
     "ssc_exclusive_scan_multipass_i32": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_compact_multipass_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "ssc_copy_i32": (_INT, [_P, _P, _I64, _P]),
+    "ssc_scratch_timed_out": (_INT, [_P, _SZ, _P, _P]),
+    "ssc_mark_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P]),
+    "ssc_scatter_i32": (_INT, [_P, _P, _P, _I64, _INT, _I32, _I32, _P, _P]),
     "ssc_compact_flags_b32": (_INT, [_P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_select_flags": (_INT, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "ssc_compact_kv_i32": (_INT, [_P, _P, _P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
@@ -151,10 +154,42 @@ def _pred(p) -> int:
 
 
 def _dev(t: torch.Tensor) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("arguments must be torch tensors")
     if not t.is_cuda:
         raise ValueError("tensors must be on the GPU (no CPU path)")
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
+
+
+def _need(t, name: str, like: torch.Tensor, dtypes, numel: int) -> torch.Tensor:
+    """Checks a caller-supplied tensor before its device pointer reaches the
+    library (which can check only alignment and overlap): a contiguous GPU
+    tensor on the same device as `like`, of one of `dtypes` (None: any), with
+    at least `numel` elements. Raises TypeError or ValueError otherwise."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (no CPU path)")
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the input on {like.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must be of dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; this call needs {numel}")
+    return t
+
+
+def _scratch(scratch, like: torch.Tensor, nbytes: int) -> torch.Tensor:
+    return _need(scratch, "scratch", like, (torch.uint8,), nbytes)
+
+
+def _count(count, like: torch.Tensor) -> torch.Tensor:
+    if count is None:
+        return torch.empty(1, dtype=torch.int32, device=like.device)
+    return _need(count, "count", like, (torch.int32,), 1)
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -198,18 +233,16 @@ def inclusive_scan(x: torch.Tensor, out: torch.Tensor | None = None,
 
 def _scan(x, out, total, scratch, form):
     _dev(x)
-    if out is None:
-        out = torch.empty_like(x)
-    if total is None:
-        total = torch.empty(1, dtype=x.dtype, device=x.device)
-    if scratch is None:
-        scratch = new_scratch(x.numel(), x.device)
     names = {torch.int32: f"ssc_{form}_scan_i32", torch.float32: f"ssc_{form}_scan_f32"}
-    if x.dtype not in names or out.dtype != x.dtype or total.dtype != x.dtype:
-        raise TypeError(f"{form}_scan takes int32 or float32 tensors of one dtype")
+    if x.dtype not in names:
+        raise TypeError(f"{form}_scan takes int32 or float32")
+    n = x.numel()
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (x.dtype,), n)
+    total = (torch.empty(1, dtype=x.dtype, device=x.device) if total is None
+             else _need(total, "total", x, (x.dtype,), 1))
+    scratch = new_scratch(n, x.device) if scratch is None else _scratch(scratch, x, scratch_bytes(n))
     fn = (names[x.dtype], getattr(lib(), names[x.dtype]))
-    _dev(out)
-    _call(fn[0], fn[1], x, out, x.numel(), total, scratch,
+    _call(fn[0], fn[1], x, out, n, total, scratch,
           scratch.numel(), _stream(x))
     return out, total
 
@@ -231,20 +264,20 @@ def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
     if x.dtype == torch.int64:
         if ranks is not False:
             raise ValueError("ranks are for 32-bit elements")
-        return _i64_op("ssc_compact_i64", x, pred, pa, torch.empty_like(x) if out is None else out,
+        return _i64_op("ssc_compact_i64", x, pred, pa,
+                       torch.empty_like(x) if out is None else _need(out, "out", x, (torch.int64,), n),
                        count, scratch)
     fn = _typed(x, "compact")
-    if out is None:
-        out = torch.empty_like(x)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (x.dtype,), n)
+    count = _count(count, x)
     rk = None
     if ranks is True:
         rk = torch.empty(n, dtype=torch.int32, device=x.device)
     elif isinstance(ranks, torch.Tensor):
-        rk = ranks
-    if scratch is None:
-        scratch = new_scratch(n, x.device)
+        rk = _need(ranks, "ranks", x, (torch.int32,), n)
+    elif ranks is not False and ranks is not None:
+        raise TypeError("ranks is True, False or an int32 tensor")
+    scratch = new_scratch(n, x.device) if scratch is None else _scratch(scratch, x, scratch_bytes(n))
     _call(fn, getattr(lib(), fn),
           x, out, n, _pred(pred), pa, pb, count, rk,
           scratch, scratch.numel(), _stream(x))
@@ -260,15 +293,14 @@ def select_index(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
     _dev(x)
     n = x.numel()
     if x.dtype == torch.int64:
-        idx = torch.empty(n, dtype=torch.int32, device=x.device) if out is None else out
+        idx = (torch.empty(n, dtype=torch.int32, device=x.device) if out is None
+               else _need(out, "out", x, (torch.int32,), n))
         return _i64_op("ssc_select_index_i64", x, pred, pa, idx, count, scratch)
     fn = _typed(x, "select_index")
-    if out is None:
-        out = torch.empty(n, dtype=torch.int32, device=x.device)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
-    if scratch is None:
-        scratch = new_scratch(n, x.device)
+    out = (torch.empty(n, dtype=torch.int32, device=x.device) if out is None
+           else _need(out, "out", x, (torch.int32,), n))
+    count = _count(count, x)
+    scratch = new_scratch(n, x.device) if scratch is None else _scratch(scratch, x, scratch_bytes(n))
     _call(fn, getattr(lib(), fn),
           x, out, n, _pred(pred), pa, pb, count,
           scratch, scratch.numel(), _stream(x))
@@ -282,12 +314,9 @@ def partition(x: torch.Tensor, pred="even", pa: int = 0, pb: int = 0, *,
     _dev(x)
     fn = _typed(x, "partition")
     n = x.numel()
-    if out is None:
-        out = torch.empty_like(x)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
-    if scratch is None:
-        scratch = new_scratch(n, x.device)
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (x.dtype,), n)
+    count = _count(count, x)
+    scratch = new_scratch(n, x.device) if scratch is None else _scratch(scratch, x, scratch_bytes(n))
     _call(fn, getattr(lib(), fn),
           x, out, n, _pred(pred), pa, pb, count,
           scratch, scratch.numel(), _stream(x))
@@ -298,10 +327,10 @@ def count_if(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
              count: torch.Tensor | None = None,
              scratch: torch.Tensor | None = None) -> torch.Tensor:
     _dev(x)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
-    if scratch is None:
-        scratch = new_scratch(0, x.device)
+    if x.dtype != torch.int32:
+        raise TypeError("count_if takes int32")
+    count = _count(count, x)
+    scratch = new_scratch(0, x.device) if scratch is None else _scratch(scratch, x, scratch_bytes(0))
     _call("ssc_count_if_i32", lib().ssc_count_if_i32,
           x, x.numel(), _pred(pred), pa, pb, count, scratch,
           scratch.numel(), _stream(x))
@@ -313,10 +342,10 @@ def compact_atomic(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
                    count: torch.Tensor | None = None):
     """(out, count): unordered compaction by atomic counter (comparison only)."""
     _dev(x)
-    if out is None:
-        out = torch.empty_like(x)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if x.dtype != torch.int32:
+        raise TypeError("compact_atomic takes int32")
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (torch.int32,), x.numel())
+    count = _count(count, x)
     _call("ssc_compact_atomic_i32", lib().ssc_compact_atomic_i32,
           x, out, x.numel(), _pred(pred), pa, pb, count,
           variant, _stream(x))
@@ -327,13 +356,15 @@ def radix_sort(x: torch.Tensor, *, out: torch.Tensor | None = None,
                tmp: torch.Tensor | None = None, scratch: torch.Tensor | None = None):
     """Ascending sort of 32-bit keys taken as unsigned (int32 storage)."""
     _dev(x)
+    if x.element_size() != 4:
+        raise TypeError("radix_sort takes 4-byte keys")
     n = x.numel()
-    if out is None:
-        out = torch.empty_like(x)
-    if tmp is None:
-        tmp = torch.empty_like(x)
-    if scratch is None:
-        scratch = new_scratch(n, x.device, radix=True)
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, None, n)
+    tmp = torch.empty_like(x) if tmp is None else _need(tmp, "tmp", x, None, n)
+    if out.element_size() != 4 or tmp.element_size() != 4:
+        raise TypeError("out and tmp hold 4-byte keys")
+    scratch = (new_scratch(n, x.device, radix=True) if scratch is None
+               else _scratch(scratch, x, radix_sort_scratch_bytes(n)))
     _call("ssc_radix_sort_u32", lib().ssc_radix_sort_u32,
           x, out, tmp, n, scratch, scratch.numel(),
           _stream(x))
@@ -349,13 +380,15 @@ def radix_sort4(x: torch.Tensor, passes: int = 8, *, out: torch.Tensor | None = 
     """Stable LSD sort of 32-bit keys taken as unsigned (int32 storage) by
     their low 4*passes bits, 4-bit digits; passes=8 sorts ascending."""
     _dev(x)
+    if x.element_size() != 4:
+        raise TypeError("radix_sort4 takes 4-byte keys")
     n = x.numel()
-    if out is None:
-        out = torch.empty_like(x)
-    if tmp is None:
-        tmp = torch.empty_like(x)
-    if scratch is None:
-        scratch = torch.zeros(radix_sort4_scratch_bytes(n), dtype=torch.uint8, device=x.device)
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, None, n)
+    tmp = torch.empty_like(x) if tmp is None else _need(tmp, "tmp", x, None, n)
+    if out.element_size() != 4 or tmp.element_size() != 4:
+        raise TypeError("out and tmp hold 4-byte keys")
+    scratch = (torch.zeros(radix_sort4_scratch_bytes(n), dtype=torch.uint8, device=x.device)
+               if scratch is None else _scratch(scratch, x, radix_sort4_scratch_bytes(n)))
     _call("ssc_radix_sort4_u32", lib().ssc_radix_sort4_u32,
           x, out, tmp, n, passes, scratch,
           scratch.numel(), _stream(x))
@@ -373,12 +406,11 @@ def exclusive_scan_multipass(x: torch.Tensor, out: torch.Tensor | None = None,
     _dev(x)
     if x.dtype != torch.int32:
         raise TypeError("exclusive_scan_multipass takes int32")
-    if out is None:
-        out = torch.empty_like(x)
-    if total is None:
-        total = torch.empty(1, dtype=torch.int32, device=x.device)
-    if scratch is None:
-        scratch = multipass_scratch(x.numel(), x.device)
+    n = x.numel()
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (torch.int32,), n)
+    total = _count(total, x)
+    scratch = (multipass_scratch(n, x.device) if scratch is None
+               else _scratch(scratch, x, int(lib().ssc_multipass_scratch_bytes(n))))
     _call("ssc_exclusive_scan_multipass_i32", lib().ssc_exclusive_scan_multipass_i32,
           x, out, x.numel(), total, scratch,
           scratch.numel(), _stream(x))
@@ -394,14 +426,11 @@ def compact_multipass(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0,
     if x.dtype != torch.int32:
         raise TypeError("compact_multipass takes int32")
     n = x.numel()
-    if out is None:
-        out = torch.empty_like(x)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
-    if ranks is None:
-        ranks = torch.empty_like(x)
-    if scratch is None:
-        scratch = multipass_scratch(n, x.device)
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (torch.int32,), n)
+    count = _count(count, x)
+    ranks = torch.empty_like(x) if ranks is None else _need(ranks, "ranks", x, (torch.int32,), n)
+    scratch = (multipass_scratch(n, x.device) if scratch is None
+               else _scratch(scratch, x, int(lib().ssc_multipass_scratch_bytes(n))))
     _call("ssc_compact_multipass_i32", lib().ssc_compact_multipass_i32,
           x, out, n, _pred(pred), pa, pb, count, ranks,
           scratch, scratch.numel(), _stream(x))
@@ -409,21 +438,63 @@ def compact_multipass(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0,
 
 
 def copy(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = x for 4-byte elements (the bandwidth reference)."""
     _dev(x)
-    if out is None:
-        out = torch.empty_like(x)
+    if x.element_size() != 4:
+        raise TypeError("copy takes 4-byte elements")
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (x.dtype,), x.numel())
     _call("ssc_copy_i32", lib().ssc_copy_i32, x, out, x.numel(), _stream(x))
     return out
+
+
+def mark(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+         out: torch.Tensor | None = None) -> torch.Tensor:
+    """flags[i] = P(x[i]) as int32 0/1: the first launch of the multi-launch
+    compaction (comparison only)."""
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("mark takes int32")
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (torch.int32,), x.numel())
+    _call("ssc_mark_i32", lib().ssc_mark_i32, x, out, x.numel(), _pred(pred), pa, pb, _stream(x))
+    return out
+
+
+def scatter(x: torch.Tensor, ranks: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+            out: torch.Tensor | None = None, count: torch.Tensor | None = None):
+    """(out, count): out[ranks[i]] = x[i] where P(x[i]), given the exclusive
+    scan of the flags: the last launch of the multi-launch compaction
+    (comparison only)."""
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("scatter takes int32")
+    n = x.numel()
+    _need(ranks, "ranks", x, (torch.int32,), n)
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, (torch.int32,), n)
+    count = _count(count, x)
+    _call("ssc_scatter_i32", lib().ssc_scatter_i32, x, ranks, out, n, _pred(pred), pa, pb, count,
+          _stream(x))
+    return out, count
+
+
+def timed_out(scratch: torch.Tensor) -> bool:
+    """True if a look-back wait of a call made with this scratch gave up after
+    its bounded spin since the scratch was last zeroed (those calls' results
+    are invalid; zero the scratch before reusing it). Synchronises with the
+    scratch's device."""
+    _dev(scratch)
+    if scratch.dtype != torch.uint8:
+        raise TypeError("scratch is a uint8 tensor")
+    flag = torch.empty(1, dtype=torch.int32, device=scratch.device)
+    _call("ssc_scratch_timed_out", lib().ssc_scratch_timed_out, scratch, scratch.numel(), flag,
+          _stream(scratch))
+    return bool(int(flag.item()))
 
 
 def _i64_op(fn: str, x: torch.Tensor, pred, bit: int, out: torch.Tensor,
             count: torch.Tensor | None, scratch: torch.Tensor | None):
     n = x.numel()
-    _dev(out)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
-    if scratch is None:
-        scratch = new_scratch(n, x.device)
+    count = _count(count, x)
+    scratch = new_scratch(n, x.device) if scratch is None else _scratch(scratch, x, scratch_bytes(n))
     _call(fn, getattr(lib(), fn), x, out, n, _pred(pred), bit,
           count, scratch, scratch.numel(), _stream(x))
     return out, count
@@ -451,12 +522,12 @@ def compact_flags(x: torch.Tensor, flags: torch.Tensor, *, out: torch.Tensor | N
     n = x.numel()
     if fb.numel() != n:
         raise ValueError("one flag byte per element")
-    if out is None:
-        out = torch.empty_like(x)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=x.device)
-    if scratch is None:
-        scratch = new_scratch(n, x.device)
+    _need(fb, "flags", x, None, n)
+    out = torch.empty_like(x) if out is None else _need(out, "out", x, None, n)
+    if out.element_size() != 4:
+        raise TypeError("out holds 4-byte elements")
+    count = _count(count, x)
+    scratch = new_scratch(n, x.device) if scratch is None else _scratch(scratch, x, scratch_bytes(n))
     _call("ssc_compact_flags_b32", lib().ssc_compact_flags_b32, x, fb,
           out, n, count, scratch, scratch.numel(), _stream(x))
     return out, count
@@ -468,12 +539,10 @@ def select_flags(flags: torch.Tensor, *, out: torch.Tensor | None = None,
     one-pass form of torch.nonzero on a bool mask)."""
     fb = _flag_bytes(flags)
     n = fb.numel()
-    if out is None:
-        out = torch.empty(n, dtype=torch.int32, device=fb.device)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=fb.device)
-    if scratch is None:
-        scratch = new_scratch(n, fb.device)
+    out = (torch.empty(n, dtype=torch.int32, device=fb.device) if out is None
+           else _need(out, "out", fb, (torch.int32,), n))
+    count = _count(count, fb)
+    scratch = new_scratch(n, fb.device) if scratch is None else _scratch(scratch, fb, scratch_bytes(n))
     _call("ssc_select_flags", lib().ssc_select_flags, fb, out, n,
           count, scratch, scratch.numel(), _stream(fb))
     return out, count
@@ -491,14 +560,14 @@ def compact_kv(keys: torch.Tensor, vals: torch.Tensor, pred="nonzero", pa=0, pb=
         raise ValueError("one 4-byte value per key")
     fn = _typed(keys, "compact_kv")
     n = keys.numel()
-    if keys_out is None:
-        keys_out = torch.empty_like(keys)
-    if vals_out is None:
-        vals_out = torch.empty_like(vals)
-    if count is None:
-        count = torch.empty(1, dtype=torch.int32, device=keys.device)
-    if scratch is None:
-        scratch = new_scratch(n, keys.device)
+    _need(vals, "vals", keys, None, n)
+    keys_out = (torch.empty_like(keys) if keys_out is None
+                else _need(keys_out, "keys_out", keys, (keys.dtype,), n))
+    vals_out = torch.empty_like(vals) if vals_out is None else _need(vals_out, "vals_out", keys, None, n)
+    if vals_out.element_size() != 4:
+        raise TypeError("vals_out holds 4-byte values")
+    count = _count(count, keys)
+    scratch = new_scratch(n, keys.device) if scratch is None else _scratch(scratch, keys, scratch_bytes(n))
     _call(fn, getattr(lib(), fn), keys, vals, keys_out,
           vals_out, n, _pred(pred), pa, pb, count, scratch,
           scratch.numel(), _stream(keys))

@@ -1560,17 +1560,50 @@ __global__ __launch_bounds__(kBlock) void compact_atomic_kernel(const int32_t *_
 }
 
 // ============================================================ copy kernel ---
+// The measured ceiling beside the compaction ("Day 33 compaction.cu",
+// copyInts): one 256-thread workgroup per 4096 elements, four 128-bit
+// nontemporal buffer loads then four stores per lane (32-bit ones for arrays
+// that are not 16-byte aligned), the resource cut at n. Small workgroups of
+// one shot each keep the most reads in flight on this part: at 2^28 int32
+// this shape measured 336-339 us against 379 us for 512-thread workgroups
+// with pointer accesses, and persistent grids 358 us.
+constexpr int kCopyBlock = 256;
+constexpr int kCopyLoads = 4;
+constexpr int kCopyTile = kCopyBlock * kCopyLoads * 4;  // elements per workgroup
+
 template <bool VEC>
-__global__ __launch_bounds__(kBlock) void copy_kernel(const int32_t *__restrict__ in,
-                                                      int32_t *__restrict__ out, int64_t n) {
-    const int lane = lane_id();
-    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
-    const int64_t chunk =
-        static_cast<int64_t>(blockIdx.x) * kSub + static_cast<int64_t>(w) * kChunk;
-    const uint32_t rem = chunk_rem(n, chunk);
-    int32_t v[kLoads][4];
-    load_chunk<VEC>(in, chunk, lane, rem, v);
-    store_chunk<VEC>(out, chunk, lane, rem, v);
+__global__ __launch_bounds__(kCopyBlock) void copy_kernel(const int32_t *__restrict__ in,
+                                                          int32_t *__restrict__ out, int64_t n) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyTile;
+    const int64_t left = n - base;
+    const uint32_t bytes =
+        left >= kCopyTile ? static_cast<uint32_t>(kCopyTile) * 4u : static_cast<uint32_t>(left) * 4u;
+    const __amdgpu_buffer_rsrc_t ri = buffer_rsrc(in + base, bytes);
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(out + base, bytes);
+    const int off = static_cast<int>(threadIdx.x) * 16;
+    if constexpr (VEC) {
+        u32x4 v[kCopyLoads];
+#pragma unroll
+        for (int j = 0; j < kCopyLoads; ++j)
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(ri, j * (kCopyBlock * 16) + off, 0, kNT);
+#pragma unroll
+        for (int j = 0; j < kCopyLoads; ++j)
+            __builtin_amdgcn_raw_buffer_store_b128(v[j], ro, j * (kCopyBlock * 16) + off, 0, kNT);
+    } else {
+        uint32_t v[kCopyLoads][4];
+#pragma unroll
+        for (int j = 0; j < kCopyLoads; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[j][k] = __builtin_amdgcn_raw_buffer_load_b32(ri, j * (kCopyBlock * 16) + off + 4 * k, 0,
+                                                               kNT);
+#pragma unroll
+        for (int j = 0; j < kCopyLoads; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                __builtin_amdgcn_raw_buffer_store_b32(v[j][k], ro, j * (kCopyBlock * 16) + off + 4 * k, 0,
+                                                      kNT);
+    }
 }
 
 // ============================== multi-launch pipelines (comparison only) ---
@@ -1684,6 +1717,13 @@ __global__ __launch_bounds__(kBlock) void scatter_kernel(const int32_t *__restri
         if (f && r >= 0 && static_cast<int64_t>(r) < n) out[r] = x;
         if (i == n - 1) *count = r + (f ? 1 : 0);
     }
+}
+
+// *flag = the scratch's look-back time-out word (one thread; a coherent load,
+// so a flag set by any compute unit is seen).
+__global__ void timed_out_kernel(const uint32_t *__restrict__ word, int32_t *__restrict__ flag) {
+    if (threadIdx.x == 0)
+        *flag = static_cast<int32_t>(__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Clears `words` 32-bit words (a kernel rather than a memset node).
@@ -2587,12 +2627,56 @@ int ssc_copy_i32(const int32_t *in, int32_t *out, int64_t n, void *stream) {
     if (overlap(in, bytes, out, bytes)) return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return SSC_OK;
+    const dim3 grid(static_cast<unsigned>((n + kCopyTile - 1) / kCopyTile));
     if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL((copy_kernel<true>), dim3(subs_for(n)), dim3(kBlock), 0, s, in, out, n);
+        hipLaunchKernelGGL((copy_kernel<true>), grid, dim3(kCopyBlock), 0, s, in, out, n);
     else
-        hipLaunchKernelGGL((copy_kernel<false>), dim3(subs_for(n)), dim3(kBlock), 0, s, in, out,
-                           n);
+        hipLaunchKernelGGL((copy_kernel<false>), grid, dim3(kCopyBlock), 0, s, in, out, n);
     return launched();
+}
+
+int ssc_scratch_timed_out(const void *scratch, size_t scratch_bytes, int32_t *flag, void *stream) {
+    if (scratch == nullptr || !aligned(scratch, 8) || scratch_bytes < kHeaderBytes)
+        return SSC_ERR_SCRATCH;
+    if (flag == nullptr || !aligned(flag, 4)) return SSC_ERR_ARG;
+    if (overlap(scratch, scratch_bytes, flag, 4)) return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    const ScratchView sv = view(const_cast<void *>(scratch));
+    hipLaunchKernelGGL(timed_out_kernel, dim3(1), dim3(kWave), 0, static_cast<hipStream_t>(stream),
+                       sv.timed_out, flag);
+    return launched();
+}
+
+int ssc_mark_i32(const int32_t *in, int32_t *flags, int64_t n, int pred, int32_t pa, int32_t pb,
+                 void *stream) {
+    SSC_TRY(check_n(n));
+    if (n > 0 && (in == nullptr || flags == nullptr)) return SSC_ERR_ARG;
+    SSC_TRY(check_pred(pred, pa, pb));
+    if (!aligned(in, 4) || !aligned(flags, 4)) return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    if (overlap(in, bytes, flags, bytes)) return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    if (n == 0) return SSC_OK;
+    return dispatch_pred<LaunchMark>(pred, aligned(in, 16) && aligned(flags, 16), in, flags, n,
+                                     make_pred_args(pred, pa, pb), static_cast<hipStream_t>(stream));
+}
+
+int ssc_scatter_i32(const int32_t *in, const int32_t *ranks, int32_t *out, int64_t n, int pred,
+                    int32_t pa, int32_t pb, int32_t *count, void *stream) {
+    SSC_TRY(check_n(n));
+    if (count == nullptr || (n > 0 && (in == nullptr || ranks == nullptr || out == nullptr)))
+        return SSC_ERR_ARG;
+    SSC_TRY(check_pred(pred, pa, pb));
+    if (!aligned(in, 4) || !aligned(ranks, 4) || !aligned(out, 4) || !aligned(count, 4))
+        return SSC_ERR_ARG;
+    const size_t bytes = static_cast<size_t>(n) * 4;
+    const Span arrays[] = {{in, bytes}, {ranks, bytes}, {out, bytes}, {count, 4}};
+    if (spans_overlap(arrays)) return SSC_ERR_ALIAS;
+    SSC_TRY(check_device());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n == 0) return clear_words(count, 1, s);
+    return dispatch_pred<LaunchScatter>(pred, true, in, ranks, out, n, make_pred_args(pred, pa, pb),
+                                        count, s);
 }
 
 const char *ssc_status_str(int status) {

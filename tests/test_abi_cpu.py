@@ -208,6 +208,22 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     # copy
     assert L.ssc_copy_i32(A, A + 4, 100, None) == ALIAS
     assert L.ssc_copy_i32(A, B, -1, None) == ARG
+    # the multi-launch compaction's separate steps
+    assert L.ssc_mark_i32(A, A + 8, 100, 1, 0, 0, None) == ALIAS
+    assert L.ssc_mark_i32(A, B, 100, 4, 32, 0, None) == ARG
+    assert L.ssc_mark_i32(None, B, 100, 1, 0, 0, None) == ARG
+    assert L.ssc_mark_i32(A, B, INT32_MAX + 1, 1, 0, 0, None) == SIZE
+    assert L.ssc_scatter_i32(A, B, C, 100, 1, 0, 0, None, None) == ARG
+    assert L.ssc_scatter_i32(A, B, B + 8, 100, 1, 0, 0, C, None) == ALIAS
+    assert L.ssc_scatter_i32(A, B, C, 100, 1, 0, 0, A + 12, None) == ALIAS
+    assert L.ssc_scatter_i32(A, B, C, 100, 5, 0, 0, C + 4096, None) == ARG
+    # the time-out check reads a scratch header into a device int outside it
+    assert L.ssc_scratch_timed_out(None, big, C, None) == SCRATCH
+    assert L.ssc_scratch_timed_out(S + 4, big, C, None) == SCRATCH
+    assert L.ssc_scratch_timed_out(S, 100, C, None) == SCRATCH
+    assert L.ssc_scratch_timed_out(S, big, None, None) == ARG
+    assert L.ssc_scratch_timed_out(S, big, C + 2, None) == ARG
+    assert L.ssc_scratch_timed_out(S, big, S + 8, None) == ALIAS
 
 
 def test_flag_pair_and_64bit_argument_errors():
@@ -260,3 +276,17 @@ def test_binding_refuses_cpu_tensors():
         ssc.compact(x, "odd")
     with pytest.raises(ValueError):
         ssc.exclusive_scan(x)
+    with pytest.raises(ValueError):
+        ssc.timed_out(torch.zeros(1024, dtype=torch.uint8))
+
+
+def test_binding_argument_checker():
+    """The checker every caller-supplied tensor goes through: it refuses what
+    is not a tensor and what is not on the GPU before looking further (on the
+    GPU the dtype, device and size checks follow; tested there)."""
+    import torch
+    x = torch.zeros(16, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        ssc._need([0] * 16, "out", x, (torch.int32,), 16)
+    with pytest.raises(ValueError, match="GPU"):
+        ssc._need(torch.zeros(16, dtype=torch.int32), "out", x, (torch.int32,), 16)

@@ -820,5 +820,67 @@ def test_argument_errors_raise_on_gpu():
         ssc.compact(x, "bit_set", 40)
     with pytest.raises(ssc.SSCError):
         ssc.partition(x, "even", out=x)
-    with pytest.raises(ssc.SSCError):
+    with pytest.raises(ValueError):
         ssc.compact(x, "odd", scratch=torch.empty(8, dtype=torch.uint8, device=DEV))
+
+
+@pytest.mark.gpu
+def test_binding_checks_caller_tensors_before_launch():
+    """Every tensor a caller passes is checked in the binding (GPU, device,
+    contiguity, dtype, size) before its pointer reaches the library, so an
+    undersized output or a host-side scratch raises instead of being written
+    past its end or handed to device atomics; the sentinel output stays."""
+    n = 5000
+    x = torch.arange(n, dtype=torch.int32, device=DEV)
+    sentinel = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    short = torch.full((n - 1,), -7, dtype=torch.int32, device=DEV)
+    sc = ssc.new_scratch(n, DEV)
+    cases = [
+        (ValueError, lambda: ssc.compact(x, "odd", out=short)),
+        (ValueError, lambda: ssc.compact(x, "odd", out=sentinel, ranks=short)),
+        (ValueError, lambda: ssc.compact(x, "odd", out=sentinel,
+                                         scratch=torch.zeros(sc.numel(), dtype=torch.uint8))),
+        (TypeError, lambda: ssc.compact(x, "odd", out=sentinel, scratch=sc.view(torch.int32))),
+        (TypeError, lambda: ssc.compact(x, "odd", out=sentinel.float())),
+        (ValueError, lambda: ssc.compact(x, "odd", out=sentinel,
+                                         count=torch.zeros(0, dtype=torch.int32, device=DEV))),
+        (ValueError, lambda: ssc.compact(x, "odd", out=sentinel,
+                                         count=torch.zeros(1, dtype=torch.int32))),
+        (ValueError, lambda: ssc.partition(x, "even", out=short)),
+        (ValueError, lambda: ssc.select_index(x, "odd", out=short)),
+        (ValueError, lambda: ssc.exclusive_scan(x, out=short)),
+        (TypeError, lambda: ssc.exclusive_scan(x, total=torch.zeros(1, dtype=torch.int64, device=DEV))),
+        (ValueError, lambda: ssc.exclusive_scan(x, out=torch.zeros(2 * n, dtype=torch.int32, device=DEV)[::2])),
+        (ValueError, lambda: ssc.radix_sort(x, out=sentinel, tmp=short)),
+        (ValueError, lambda: ssc.compact_atomic(x, "odd", out=short)),
+        (ValueError, lambda: ssc.compact_flags(x, (x & 1).bool(), out=short)),
+        (ValueError, lambda: ssc.select_flags((x & 1).bool(), out=short)),
+        (ValueError, lambda: ssc.compact_kv(x, x, "odd", keys_out=sentinel, vals_out=short)),
+        (ValueError, lambda: ssc.copy(x, out=short)),
+        (ValueError, lambda: ssc.scatter(x, short, "odd", out=sentinel)),
+    ]
+    for err, call in cases:
+        with pytest.raises(err):
+            call()
+    torch.cuda.synchronize()
+    assert bool((sentinel == -7).all()) and bool((short == -7).all())
+
+
+@pytest.mark.gpu
+def test_mark_and_scatter_steps_match_the_oracle():
+    """The multi-launch compaction's separate steps: mark writes the 0/1
+    flags, and scatter with their exclusive scan gives the ordered survivors
+    and the count."""
+    x_np = wl.full_int32(0x5EED0A11, 3 * 30720 + 77)
+    x = torch.from_numpy(x_np).to(DEV)
+    flags = ssc.mark(x, "mod_lt", 10, 3)
+    want_flags = oracle.flags(x_np, oracle.PRED_MOD_LT, 10, 3)
+    assert np.array_equal(flags.cpu().numpy(), want_flags.astype(np.int32))
+    ranks, _ = ssc.exclusive_scan(flags)
+    out = torch.full_like(x, -7)
+    out, cnt = ssc.scatter(x, ranks, "mod_lt", 10, 3, out=out)
+    want, m = oracle.compact_i32(x_np, oracle.PRED_MOD_LT, 10, 3)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == m
+    assert np.array_equal(out[:m].cpu().numpy(), want)
+    assert bool((out[m:] == -7).all())
