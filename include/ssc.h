@@ -171,6 +171,21 @@ int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_
                     int32_t pb, int32_t *count, int32_t *ranks, void *scratch,
                     size_t scratch_bytes, void *stream);
 
+/* ssc_compact_i32 without a scratch argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results, errors and
+ * kernels as ssc_compact_i32; nothing is allocated or freed: the scratch is a
+ * library-owned device array of 1,119,232 bytes on each GPU (enough for every
+ * n up to INT32_MAX; a larger scratch need would give SSC_ERR_SIZE), held
+ * until the process ends. Its address is looked up and the array zero-filled
+ * by one clearing kernel on `stream` at the first call on a device; later
+ * calls reuse it as left by the previous call, which keeps it ready. All
+ * calls on one GPU share that one array, so calls that may run at the same
+ * time on one GPU (other streams, other host threads) race and give wrong
+ * results: serialise them. */
+int ssc_compact_i32_noalloc(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
+                            int32_t pb, int32_t *count, int32_t *ranks, void *stream);
+
 /* ssc_compact_i32 for fp32 arrays with an fp32 predicate (6..9) and its
  * thresholds a, b; values move bit for bit (-0.0 and NaN payloads kept). */
 int ssc_compact_f32(const float *in, float *out, int64_t n, int pred, float a, float b,

@@ -45,6 +45,7 @@ SIGNATURES = {
     "ssc_select_index_f32": (_INT, [_P, _P, _I64, _INT, _F32, _F32, _P, _P, _SZ, _P]),
     "ssc_partition_f32": (_INT, [_P, _P, _I64, _INT, _F32, _F32, _P, _P, _SZ, _P]),
     "ssc_compact_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "ssc_compact_i32_noalloc": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _P]),
     "ssc_partition_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
     "ssc_count_if_i32": (_INT, [_P, _I64, _INT, _I32, _I32, _P, _P, _SZ, _P]),
     "ssc_compact_atomic_i32": (_INT, [_P, _P, _I64, _INT, _I32, _I32, _P, _INT, _P]),
@@ -282,6 +283,24 @@ def compact(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
           x, out, n, _pred(pred), pa, pb, count, rk,
           scratch, scratch.numel(), _stream(x))
     return (out, count, rk) if rk is not None else (out, count)
+
+
+def compact_noalloc(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,
+                    out: torch.Tensor, count: torch.Tensor, ranks: torch.Tensor | None = None):
+    """(out, count[, ranks]) as compact() for int32, through the entry point
+    that allocates nothing (its scratch is a library-owned array per GPU):
+    the caller passes every output. Calls that may overlap on one GPU race."""
+    _dev(x)
+    if x.dtype != torch.int32:
+        raise TypeError("compact_noalloc takes int32")
+    n = x.numel()
+    _need(out, "out", x, (torch.int32,), n)
+    _need(count, "count", x, (torch.int32,), 1)
+    if ranks is not None:
+        _need(ranks, "ranks", x, (torch.int32,), n)
+    _call("ssc_compact_i32_noalloc", lib().ssc_compact_i32_noalloc,
+          x, out, n, _pred(pred), pa, pb, count, ranks, _stream(x))
+    return (out, count, ranks) if ranks is not None else (out, count)
 
 
 def select_index(x: torch.Tensor, pred="nonzero", pa: int = 0, pb: int = 0, *,

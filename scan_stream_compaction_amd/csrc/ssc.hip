@@ -36,6 +36,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "ssc.h"
@@ -1735,6 +1736,16 @@ __global__ __launch_bounds__(kBlock) void clear_kernel(uint32_t *__restrict__ p,
 
 }  // namespace ssc
 
+// Scratch of ssc_compact_i32_noalloc: a look-back scratch (header and two
+// descriptor words per tile) for every n the C ABI accepts, 1,119,232 bytes,
+// held on each GPU the library runs on until the process ends. In host code
+// this name stands for the symbol only: its device address comes from
+// hipGetSymbolAddress (noalloc_scratch below), once per device.
+constexpr size_t kNoAllocScratchBytes =
+    (ssc::kHeaderBytes + static_cast<size_t>(ssc::tiles_for(INT32_MAX)) * 2 * sizeof(uint64_t) + 255) &
+    ~static_cast<size_t>(255);
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 // ======================================================================
 // Host side: argument checks and dispatch.
 // ======================================================================
@@ -2107,11 +2118,11 @@ size_t radix4_scratch_need(int64_t n) {
     return radix4_scan_part(n) + static_cast<size_t>(kRadixDigits * radix_tiles_for(n)) * 4;
 }
 
+// The checks of a compaction's arrays and predicate (everything but the
+// scratch), made before anything is enqueued.
 template <bool F32>
-int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
-                 int32_t *count, int32_t *ranks, void *scratch, size_t scratch_bytes,
-                 void *stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
+int compact_arrays_ok(const int32_t *in, const int32_t *out, int64_t n, int pred, int32_t pa,
+                      int32_t pb, const int32_t *count, const int32_t *ranks) {
     SSC_TRY(check_n(n));
     if (count == nullptr || (n > 0 && (in == nullptr || out == nullptr))) return SSC_ERR_ARG;
     SSC_TRY(F32 ? check_pred_f32(pred) : check_pred(pred, pa, pb));
@@ -2123,6 +2134,16 @@ int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t p
         (ranks && (overlap(ranks, bytes, in, bytes) || overlap(ranks, bytes, out, bytes) ||
                    overlap(ranks, bytes, count, 4))))
         return SSC_ERR_ALIAS;
+    return SSC_OK;
+}
+
+template <bool F32>
+int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa, int32_t pb,
+                 int32_t *count, int32_t *ranks, void *scratch, size_t scratch_bytes,
+                 void *stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SSC_TRY(compact_arrays_ok<F32>(in, out, n, pred, pa, pb, count, ranks));
+    const size_t bytes = static_cast<size_t>(n) * 4;
     SSC_TRY(check_scratch(scratch, scratch_bytes, scratch_need(n)));
     if (overlap(scratch, scratch_bytes, in, bytes) || overlap(scratch, scratch_bytes, out, bytes) ||
         overlap(scratch, scratch_bytes, count, 4) ||
@@ -2305,6 +2326,31 @@ int i64_impl(int kind, const int64_t *in, void *out, int64_t n, int pred, int32_
                                            capacity_of(scratch_bytes), count, s);
 }
 
+// The device address of `scratch` on the current device, fetched once per
+// device with that device current and kept; the first fetch also zero-fills
+// the array on `s` (a clearing kernel ordered before the call that needs it:
+// the look-back keeps the scratch ready from then on).
+std::mutex g_noalloc_mutex;
+void *g_noalloc_ptr[64];
+
+int noalloc_scratch(void **ptr, hipStream_t s) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= 64) return SSC_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+    if (g_noalloc_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (p == nullptr) return SSC_ERR_HIP;
+        SSC_TRY(clear_words(p, static_cast<int64_t>(kNoAllocScratchBytes / 4), s));
+        g_noalloc_ptr[dev] = p;
+    }
+    *ptr = g_noalloc_ptr[dev];
+    return SSC_OK;
+}
+
 }  // namespace
 
 // ======================================================================
@@ -2357,6 +2403,19 @@ int ssc_compact_i32(const int32_t *in, int32_t *out, int64_t n, int pred, int32_
                     int32_t *count, int32_t *ranks, void *scratch, size_t scratch_bytes,
                     void *stream) {
     return compact_impl<false>(in, out, n, pred, pa, pb, count, ranks, scratch, scratch_bytes,
+                               stream);
+}
+
+int ssc_compact_i32_noalloc(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t pa,
+                            int32_t pb, int32_t *count, int32_t *ranks, void *stream) {
+    SSC_TRY(compact_arrays_ok<false>(in, out, n, pred, pa, pb, count, ranks));
+    if (scratch_need(n) > kNoAllocScratchBytes) return SSC_ERR_SIZE;
+    SSC_TRY(check_device());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n == 0) return clear_words(count, 1, s);
+    void *p = nullptr;
+    SSC_TRY(noalloc_scratch(&p, s));
+    return compact_impl<false>(in, out, n, pred, pa, pb, count, ranks, p, kNoAllocScratchBytes,
                                stream);
 }
 

@@ -217,6 +217,15 @@ def test_scan_partition_atomic_sort_copy_argument_errors():
     assert L.ssc_scatter_i32(A, B, B + 8, 100, 1, 0, 0, C, None) == ALIAS
     assert L.ssc_scatter_i32(A, B, C, 100, 1, 0, 0, A + 12, None) == ALIAS
     assert L.ssc_scatter_i32(A, B, C, 100, 5, 0, 0, C + 4096, None) == ARG
+    # the allocation-free compaction: the same argument checks, before any HIP call
+    assert L.ssc_compact_i32_noalloc(A, B, 100, 1, 0, 0, None, None, None) == ARG
+    assert L.ssc_compact_i32_noalloc(A, A + 8, 100, 1, 0, 0, C, None, None) == ALIAS
+    assert L.ssc_compact_i32_noalloc(A, B, 100, 1, 0, 0, C, A + 40, None) == ALIAS
+    assert L.ssc_compact_i32_noalloc(A, B, 100, 4, 32, 0, C, None, None) == ARG
+    assert L.ssc_compact_i32_noalloc(A, B, 100, 6, 0, 0, C, None, None) == ARG
+    assert L.ssc_compact_i32_noalloc(A, B, -1, 1, 0, 0, C, None, None) == ARG
+    assert L.ssc_compact_i32_noalloc(A, B, INT32_MAX + 1, 1, 0, 0, C, None, None) == SIZE
+    assert L.ssc_compact_i32_noalloc(A, B + 2, 100, 1, 0, 0, C, None, None) == ARG
     # the time-out check reads a scratch header into a device int outside it
     assert L.ssc_scratch_timed_out(None, big, C, None) == SCRATCH
     assert L.ssc_scratch_timed_out(S + 4, big, C, None) == SCRATCH
