@@ -11,6 +11,7 @@ count (the top of the scan), compact, partition.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -18,6 +19,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssc.so")
+PERTURB_LIB_PATH = os.path.join(_PKG, "libssc_perturb.so")  # race-test build
 
 PRED = {"nonzero": 0, "odd": 1, "even": 2, "bit_set": 3, "bit_clear": 4, "mod_lt": 5,
         "f32_nonzero": 6, "f32_gt": 7, "f32_lt": 8, "f32_in": 9}
@@ -79,21 +81,39 @@ class SSCError(RuntimeError):
 _lib = None
 
 
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the C ABI at `path` with every declared signature set."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with "
+            "`python -m scan_stream_compaction_amd.build` (there is no fallback)")
+    L = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Load libssc.so (built in-tree by ``python -m scan_stream_compaction_amd.build``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with "
-                "`python -m scan_stream_compaction_amd.build` (there is no fallback)")
-        L = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(L, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every call of this module through another build of the same
+    sources (the race tests use libssc_perturb.so) while the block runs."""
+    global _lib
+    saved = lib()
+    _lib = load_library(path)
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def _check(call: str, rc: int) -> None:

@@ -1,6 +1,11 @@
 """Build libssc.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m scan_stream_compaction_amd.build [--asm DIR]
+Also builds libssc_perturb.so, the same sources with -DSSC_PERTURB: every
+tile claim, descriptor publication, arrival and look-back poll pauses for a
+hashed number of clocks, so the race tests see tiles finish in other orders.
+The library proper never contains that code.
+
+Usage: python -m scan_stream_compaction_amd.build [--asm DIR] [--only lib|perturb]
 """
 from __future__ import annotations
 
@@ -14,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "ssc.hip")
 LIB = os.path.join(PKG, "libssc.so")
+PERTURB_LIB = os.path.join(PKG, "libssc_perturb.so")
 ARCH = "gfx950"
 
 
@@ -34,24 +40,38 @@ def flags() -> list[str]:
     ]
 
 
-def build(asm_dir: str | None = None) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *flags(), "-shared", SRC, "-o", tmp]
+def _command(out: str, perturb: bool, asm_dir: str | None) -> tuple[list[str], str]:
+    cmd = [hipcc(), *flags(), *(["-DSSC_PERTURB=1"] if perturb else []), "-shared", SRC, "-o", out]
+    cwd = ROOT
     if asm_dir:
+        # intermediate files (device ISA included) go next to the output
         os.makedirs(asm_dir, exist_ok=True)
-        cmd += ["-save-temps=obj"]
+        cmd += ["-save-temps=cwd"]
         cwd = asm_dir
-        cmd[-1] = os.path.abspath(tmp)
-    else:
-        cwd = ROOT
-    subprocess.run(cmd, check=True, cwd=cwd)
-    os.replace(tmp, LIB)
-    return LIB
+    return cmd, cwd
+
+
+def build(asm_dir: str | None = None, only: str | None = None) -> list[str]:
+    """Compile the library (and, unless only == "lib", the perturbed test
+    build) in parallel; each output is replaced only once it is complete."""
+    jobs = []
+    for name, out, perturb in (("lib", LIB, False), ("perturb", PERTURB_LIB, True)):
+        if only and only != name:
+            continue
+        cmd, cwd = _command(out + ".tmp", perturb, asm_dir if name == "lib" else None)
+        jobs.append((out, subprocess.Popen(cmd, cwd=cwd)))
+    failed = [out for out, p in jobs if p.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed for {', '.join(failed)}")
+    for out, _ in jobs:
+        os.replace(out + ".tmp", out)
+    return [out for out, _ in jobs]
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
-    ap.add_argument("--asm", default=None, help="keep intermediate files (ISA) in this directory")
+    ap.add_argument("--asm", default=None, help="keep intermediate files (ISA) of libssc.so in this directory")
+    ap.add_argument("--only", choices=("lib", "perturb"), default=None)
     a = ap.parse_args()
-    print(build(a.asm))
+    print("\n".join(build(a.asm, a.only)))
     sys.exit(0)

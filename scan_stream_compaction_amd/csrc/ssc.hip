@@ -298,6 +298,7 @@ __device__ __forceinline__ void end_epoch(const ScratchView &sv, uint32_t epoch,
 
 __device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t words_used,
                                                uint32_t claims, uint32_t capacity) {
+    perturb(blockIdx.x, 8);
     const uint64_t c =
         __hip_atomic_fetch_add(sv.claim, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (static_cast<uint32_t>(c) == claims - 1)
@@ -318,18 +319,43 @@ __device__ __forceinline__ uint64_t claim_tile(const ScratchView &sv, uint32_t w
 // completes the count ends the epoch. Every claim of the call has been
 // performed by then, so all carry one epoch.
 __device__ __forceinline__ uint64_t claim_tiles(const ScratchView &sv, uint64_t k) {
+    perturb(blockIdx.x * 4u + static_cast<uint32_t>(k), 9);
     return __hip_atomic_fetch_add(sv.claim, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void finish_claims(const ScratchView &sv, uint32_t epoch,
                                               uint32_t workgroups, uint32_t words_used,
                                               uint32_t capacity) {
+    perturb(blockIdx.x, 10);
     const uint32_t before =
         __hip_atomic_fetch_add(sv.claimed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (before == workgroups - 1u) {
         __hip_atomic_store(sv.claimed, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         end_epoch(sv, epoch, words_used, capacity);
     }
+}
+
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;  // no tile: past the end
+
+// The second and third tiles of a persistent workgroup (control lane 0,
+// while the data wavefronts load the first). With at least three tiles per
+// workgroup both come from one atomic (one round trip); with fewer they are
+// claimed one at a time, so that no workgroup takes two of the last tiles
+// while others get none (10^7 int32 scan: 22.4 -> 20.6 us). Returns true when
+// the claims reached the end.
+__device__ __forceinline__ bool claim_second_third(const ScratchView &sv, uint32_t num_tiles,
+                                                   uint32_t *first) {
+    uint32_t c1, c2;
+    if (num_tiles >= 3u * gridDim.x) {
+        c1 = static_cast<uint32_t>(claim_tiles(sv, 2));
+        c2 = c1 + 1u;
+    } else {
+        c1 = static_cast<uint32_t>(claim_tiles(sv, 1));
+        c2 = c1 < num_tiles ? static_cast<uint32_t>(claim_tiles(sv, 1)) : kNoTile;
+    }
+    first[1] = c1;
+    first[2] = c2;
+    return c2 >= num_tiles;
 }
 
 // Arrival of a data wavefront (whole wavefront) after writing its chunk
@@ -343,6 +369,7 @@ template <class Op, bool WIDE>
 __device__ __forceinline__ void arrive_and_publish(uint32_t *s_arrive, const uint32_t *s_tot,
                                                    uint32_t *s_pre, uint64_t *desc, uint32_t tile,
                                                    uint32_t tag, int lane) {
+    perturb(tile * 16u + threadIdx.x / kWave, 11);
     uint32_t before = 0;
     if (lane == 0)
         before = __hip_atomic_fetch_add(s_arrive, 1u, __ATOMIC_ACQ_REL,
@@ -828,7 +855,6 @@ struct FmtB64 {
 // next launch (the radix driver's chained splits): its runs are stored with
 // the default cache policy throughout.
 enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3, kPartitionCached = 4 };
-constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 
 // Register sets per data wavefront. With two, the loads of the tile after next
 // reuse the current chunk's registers, so they leave only once that chunk is
@@ -892,14 +918,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         return;
     }
     bool last_claim = false;  // control lane 0: the claims just made reached the end
-    if (w == kCtrlWave && lane == 0) {
-        // the second and third tiles, one atomic round trip while the data
-        // wavefronts load the first tile
-        const uint32_t c1 = static_cast<uint32_t>(claim_tiles(sv, 2));
-        s_first[1] = c1;
-        s_first[2] = c1 + 1u;
-        last_claim = c1 + 1u >= num_tiles;
-    }
+    if (w == kCtrlWave && lane == 0) last_claim = claim_second_third(sv, num_tiles, s_first);
     uint32_t par = 0;  // tile parity within the workgroup: s_base, s_next
     uint32_t tri = 0;  // tile number within the workgroup mod 3: s_pre
 
@@ -963,6 +982,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         FM = F::template flags<P>(V, LN, R, pr);                                              \
         A = chunk_total(FM);                                                                  \
         if (LN == 0) s_tot[w] = A;                                                            \
+        perturb((T) * 16u + w, 11);                                                           \
         uint32_t before_ = 0;                                                                 \
         if (LN == 0)                                                                          \
             before_ = __hip_atomic_fetch_add(&s_arrive, 1u, __ATOMIC_ACQ_REL,                 \
@@ -1084,7 +1104,9 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 // =========================================================== scan kernel ---
 constexpr int kScanPollSleep = 127;  // look-back poll interval, s_sleep units (measured)
 // Exclusive (or, INCL, inclusive) scan of 32-bit values: one tile per
-// workgroup with a control wavefront for the look-back; the tile aggregate is
+// workgroup, two workgroups resident per compute unit, with a control
+// wavefront for the look-back (used for one to two tiles per compute unit;
+// scan_persistent_kernel otherwise); the tile aggregate is
 // the sum of the values. Per load j a lane sums its 4 values, a DPP wavefront
 // scan gives the lane offsets, and results leave with the same 128-bit layout
 // they were read with. in == out is allowed.
@@ -1216,6 +1238,289 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
         const int64_t chunk = tile_start + q * kLbSub + w * kChunk;
         store_chunk<VEC>(out, chunk, lane, chunk_rem(n, chunk), v[q]);
     }
+}
+
+// ================================================== persistent scan kernel ---
+// The scan in the compaction kernel's pipeline: one 1024-thread workgroup per
+// compute unit loops over tiles of 30720 values claimed three ahead, each data
+// wavefront holding three chunks of 2048 values (eight 128-bit loads per
+// lane) in registers. Per tile it
+//   1. issues the loads of the tile after next into the chunk written last;
+//   2. sums the next tile's chunk once it has landed and arrives with the
+//      total; the last of the 15 to arrive scans the chunk totals and
+//      publishes the next tile's {aggregate} at once;
+//   3. waits at the tile's barrier for its base from the control wavefront;
+//   4. scans the current chunk load by load (per load a DPP wavefront scan of
+//      the lanes' 4-value sums) and stores base + chunk prefix + the value's
+//      prefix at once, in the layout it was read with.
+// No LDS staging is needed: the output of a chunk is its input's positions.
+// Scanning at the store instead of on arrival keeps one chunk's prefixes
+// live instead of two, which is what lets three chunks fit in 128 VGPRs.
+// WIDE (fp32): carries between tiles are fp64 (wide descriptors, fp64
+// look-back) and each output is rounded to fp32 once from the fp64 sum of
+// base, chunk prefix and in-chunk prefix. Forward progress as for
+// select_kernel. Measured at 2^28 int32 (exclusive): 369.7 us against 377.1
+// for one workgroup per tile; fp32 376 against 405; 2^24: 29.8 against 36.1;
+// without the look-back wait (results wrong, timing only) 368 -> 378 us
+// before the per-load resources, i.e. the look-back costs about 10 us.
+constexpr int kScanPSleep = 32;  // look-back poll interval, s_sleep units
+
+template <class Op, bool VEC, bool INCL, bool WIDE>
+__global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void scan_persistent_kernel(
+    const typename Op::T *in, typename Op::T *out, int64_t n, void *scratch, uint32_t num_tiles,
+    uint32_t capacity, typename Op::T *total) {
+    using T = typename Op::T;
+    using S = ChunkShape<8, 4>;
+    static_assert(S::kTileElems == kTile, "one descriptor per kTile values");
+    static_assert(!WIDE || sizeof(T) == 4, "wide carries are for fp32 values");
+    __shared__ uint32_t s_tot[kDataWaves];
+    __shared__ uint32_t s_pre[3][kDataWaves + 1];  // chunk prefixes + aggregate, by tile mod 3
+    __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
+    __shared__ double s_base64[2];
+    __shared__ uint32_t s_first[3], s_epoch, s_arrive;
+
+    const ScratchView sv = view(scratch);
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
+    // descriptor words this call uses: the stale-slot sweep spares them
+    const uint32_t words_used = WIDE ? 2u * num_tiles : num_tiles;
+    if (threadIdx.x == 0) {
+        const uint64_t c = claim_tiles(sv, 1);
+        s_first[0] = static_cast<uint32_t>(c);
+        s_epoch = static_cast<uint32_t>(c >> 32);
+        s_arrive = 0;
+    }
+    __syncthreads();  // B0: the first tile
+    uint32_t tile = uniform(s_first[0]);
+    const uint32_t epoch = uniform(s_epoch);
+    const uint32_t tag = epoch & kTagMask;
+    if (tile >= num_tiles) {
+        if (w == kCtrlWave && lane == 0) finish_claims(sv, epoch, gridDim.x, words_used, capacity);
+        return;
+    }
+    bool last_claim = false;
+    if (w == kCtrlWave && lane == 0) last_claim = claim_second_third(sv, num_tiles, s_first);
+    uint32_t par = 0;
+    uint32_t tri = 0;
+
+    if (w == kCtrlWave) {
+        __syncthreads();  // B0b: the second and third tiles
+        uint32_t nxt = uniform(s_first[1]);
+        uint32_t nxt2 = uniform(s_first[2]);
+        __syncthreads();  // B0': the first tile's arrivals are in
+        while (true) {
+            uint32_t nxt3 = kNoTile;
+            if (lane == 0 && nxt2 < num_tiles) {
+                nxt3 = static_cast<uint32_t>(claim_tiles(sv, 1));
+                last_claim = nxt3 >= num_tiles;
+            }
+            T prefix = Op::zero();
+            double prefix64 = 0.0;
+            if (tile != 0) {
+                if constexpr (WIDE)
+                    prefix64 = look_back_wide<kScanPSleep>(sv.desc, tile, tag, sv.timed_out);
+                else
+                    prefix = look_back<Op, kScanPSleep, false>(sv.desc, tile, tag, sv.timed_out);
+            }
+            if (lane == 0) {
+                if constexpr (WIDE)
+                    s_base64[par] = prefix64;
+                else
+                    s_base[par] = Op::bits(prefix);
+                s_next[par] = nxt3;
+            }
+            __syncthreads();  // B1
+            const T agg = Op::from_bits(uniform(s_pre[tri][kDataWaves]));
+            if (lane == 0) {
+                // {inclusive} at least one barrier after this tile's
+                // {aggregate}: from one compute unit, in issue order
+                if constexpr (WIDE) {
+                    const double incl = prefix64 + static_cast<double>(agg);
+                    if (tile != 0) publish_wide(sv.desc, tile, tag, kStatusInclusive, incl);
+                    if (total != nullptr && tile == num_tiles - 1) *total = static_cast<T>(incl);
+                } else {
+                    const T incl = Op::add(prefix, agg);
+                    if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, Op::bits(incl));
+                    if (total != nullptr && tile == num_tiles - 1) *total = incl;
+                }
+                if (last_claim) finish_claims(sv, epoch, gridDim.x, words_used, capacity);
+                last_claim = false;
+            }
+            if (nxt >= num_tiles) return;
+            tile = nxt;
+            nxt = nxt2;
+            nxt2 = uniform(nxt3);
+            par ^= 1u;
+            tri = tri == 2u ? 0u : tri + 1u;
+        }
+    }
+
+    uint32_t va[S::kLoads][4], vb[S::kLoads][4], vc[S::kLoads][4];
+    const auto chunk_of = [&](uint32_t t) {
+        return static_cast<int64_t>(t) * kTile + static_cast<int64_t>(w) * S::kChunk;
+    };
+    const auto rem_of = [&](uint32_t t) {
+        return t < num_tiles ? chunk_rem<S::kChunk>(n, chunk_of(t)) : 0u;
+    };
+    // Load j of a chunk goes through its own buffer resource, based j KiB
+    // into the chunk with the bytes left from there: every lane then needs one
+    // offset register, and the range check still covers the whole access
+    // (the instruction's scalar offset is outside that check, so it cannot
+    // carry j).
+    const auto part_rsrc = [&](const void *chunk, uint32_t bytes, int j) {
+        const uint32_t skip = static_cast<uint32_t>(j) * (kWave * 16);
+        return buffer_rsrc(static_cast<const char *>(chunk) + skip, bytes > skip ? bytes - skip : 0u);
+    };
+    const auto load = [&](uint32_t t, int ln, uint32_t(&v)[S::kLoads][4]) {
+        const T *c = in + chunk_of(t);
+        const uint32_t bytes = rem_of(t) * 4u;
+#pragma unroll
+        for (int j = 0; j < S::kLoads; ++j) {
+            const __amdgpu_buffer_rsrc_t r = part_rsrc(c, bytes, j);
+            if constexpr (VEC) {
+                const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, ln * 16, 0, kNT);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[j][k] = q[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    v[j][k] = __builtin_amdgcn_raw_buffer_load_b32(r, ln * 16 + 4 * k, 0, kNT);
+            }
+        }
+    };
+    // The chunk's total (values past the end read as 0).
+    const auto chunk_sum = [&](const uint32_t(&v)[S::kLoads][4]) {
+        T s = Op::zero();
+#pragma unroll
+        for (int j = 0; j < S::kLoads; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s = Op::add(s, Op::from_bits(v[j][k]));
+        const T incl = wave_inclusive_scan<Op>(s);
+        return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(Op::bits(incl)), kWave - 1));
+    };
+    // Arrival with the chunk total: the last data wavefront to arrive scans
+    // the 15 totals into s_pre[TRI] (fixed order, so fp32 sums agree for every
+    // reader) and publishes tile T's {aggregate} ({inclusive} for tile 0).
+    const auto arrive = [&](uint32_t tot, uint32_t t, uint32_t tri_, int ln) {
+        if (ln == 0) s_tot[w] = tot;
+        perturb(t * 16u + w, 11);
+        uint32_t before = 0;
+        if (ln == 0)
+            before = __hip_atomic_fetch_add(&s_arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (uniform(before) == kDataWaves - 1) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const T mine = ln < kDataWaves ? Op::from_bits(s_tot[ln]) : Op::zero();
+            const T incl = wave_inclusive_scan<Op>(mine);
+            const uint32_t up = static_cast<uint32_t>(__shfl_up(static_cast<int>(Op::bits(incl)), 1));
+            if (ln < kDataWaves) s_pre[tri_][ln] = ln == 0 ? Op::bits(Op::zero()) : up;
+            const T agg = Op::from_bits(static_cast<uint32_t>(
+                __builtin_amdgcn_readlane(static_cast<int>(Op::bits(incl)), kDataWaves - 1)));
+            if (ln == 0) {
+                s_arrive = 0;
+                s_pre[tri_][kDataWaves] = Op::bits(agg);
+                if (t < num_tiles) {
+                    const uint32_t st = t == 0 ? kStatusInclusive : kStatusAggregate;
+                    if constexpr (WIDE)
+                        publish_wide(sv.desc, t, tag, st, static_cast<double>(agg));
+                    else
+                        publish(sv.desc + t, tag, st, Op::bits(agg));
+                }
+            }
+        }
+    };
+    // Scans the chunk load by load (exclusive, or with INCL inclusive) and
+    // stores base + chunk prefix + in-chunk prefix in the load layout.
+    const auto write = [&](const uint32_t(&v)[S::kLoads][4], uint32_t t, uint32_t par_, uint32_t tri_,
+                           int ln) {
+        const T *c = out + chunk_of(t);
+        const uint32_t bytes = rem_of(t) * 4u;
+        const T cb = Op::from_bits(uniform(s_pre[tri_][w]));
+        double b64 = 0.0;
+        T base = Op::zero();
+        if constexpr (WIDE)
+            b64 = s_base64[par_] + static_cast<double>(cb);
+        else
+            base = Op::add(Op::from_bits(uniform(s_base[par_])), cb);
+        T running = Op::zero();
+#pragma unroll
+        for (int j = 0; j < S::kLoads; ++j) {
+            T p[4];
+            T s = Op::zero();
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const T x = Op::from_bits(v[j][k]);
+                if constexpr (INCL) {
+                    s = Op::add(s, x);
+                    p[k] = s;
+                } else {
+                    p[k] = s;
+                    s = Op::add(s, x);
+                }
+            }
+            const T incl = wave_inclusive_scan<Op>(s);
+            const uint32_t up = static_cast<uint32_t>(__shfl_up(static_cast<int>(Op::bits(incl)), 1));
+            const T lead = Op::add(running, ln == 0 ? Op::zero() : Op::from_bits(up));
+            running = Op::add(running, Op::from_bits(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                                           static_cast<int>(Op::bits(incl)), kWave - 1))));
+            uint32_t q[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const T pre = Op::add(lead, p[k]);
+                if constexpr (WIDE)
+                    q[k] = Op::bits(static_cast<T>(b64 + static_cast<double>(pre)));
+                else
+                    q[k] = Op::bits(Op::add(base, pre));
+            }
+            const __amdgpu_buffer_rsrc_t r = part_rsrc(c, bytes, j);
+            if constexpr (VEC) {
+                u32x4 o;
+                o[0] = q[0];
+                o[1] = q[1];
+                o[2] = q[2];
+                o[3] = q[3];
+                __builtin_amdgcn_raw_buffer_store_b128(o, r, ln * 16, 0, kNT);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) __builtin_amdgcn_raw_buffer_store_b32(q[k], r, ln * 16 + 4 * k, 0, kNT);
+            }
+        }
+    };
+
+    // One tile: CUR holds the current tile's scanned chunk, NX the next one in
+    // flight, FREE the chunk written one tile ago.
+#define SSC_SCAN_TILE(CUR, NX, FREE)                                                         \
+    {                                                                                        \
+        int ln = lane;                                                                       \
+        asm volatile("" : "+v"(ln));                                                         \
+        load(nxt2, ln, FREE);                                                                \
+        const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                    \
+        arrive(chunk_sum(NX), nxt, tri_n, ln);                                          \
+        __syncthreads(); /* B1: this tile's base is known */                                 \
+        const uint32_t nxt3 = uniform(s_next[par]);                                          \
+        write(CUR, tile, par, tri, ln);                                                      \
+        tile = nxt;                                                                          \
+        nxt = nxt2;                                                                          \
+        nxt2 = nxt3;                                                                         \
+        par ^= 1u;                                                                           \
+        tri = tri_n;                                                                         \
+    }
+
+    load(tile, lane, va);
+    __syncthreads();  // B0b: the second and third tiles
+    uint32_t nxt = uniform(s_first[1]);
+    uint32_t nxt2 = uniform(s_first[2]);
+    load(nxt, lane, vb);
+    arrive(chunk_sum(va), tile, tri, lane);
+    __syncthreads();  // B0': every wavefront has arrived for the first tile
+    while (true) {
+        SSC_SCAN_TILE(va, vb, vc)
+        if (tile >= num_tiles) break;
+        SSC_SCAN_TILE(vb, vc, va)
+        if (tile >= num_tiles) break;
+        SSC_SCAN_TILE(vc, va, vb)
+        if (tile >= num_tiles) break;
+    }
+#undef SSC_SCAN_TILE
 }
 
 // ======================================================= counting kernels ---
@@ -2097,12 +2402,28 @@ int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename
     const uint32_t tiles = static_cast<uint32_t>(tiles_for(n));
     const uint32_t cap = capacity_of(scratch_bytes);
     constexpr bool kWide = sizeof(T) == 4 && !std::is_integral<T>::value;  // fp32: fp64 carries
-    if (aligned(in, 16) && aligned(out, 16))
-        hipLaunchKernelGGL((scan_kernel<Op, true, INCL, kWide>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
-                           scratch, tiles, cap, total);
+    uint32_t slots = 0;
+    SSC_TRY(compute_units(&slots));
+    const bool vec = aligned(in, 16) && aligned(out, 16);
+    if (tiles > slots && tiles <= 2 * slots) {
+        // One to two tiles per compute unit: one workgroup per tile, two
+        // resident per compute unit, beats a persistent workgroup taking
+        // its two tiles in turn (10^7 int32: 19.6 against 22.5 us).
+        if (vec)
+            hipLaunchKernelGGL((scan_kernel<Op, true, INCL, kWide>), dim3(tiles), dim3(kLbBlock), 0, s, in, out,
+                               n, scratch, tiles, cap, total);
+        else
+            hipLaunchKernelGGL((scan_kernel<Op, false, INCL, kWide>), dim3(tiles), dim3(kLbBlock), 0, s, in,
+                               out, n, scratch, tiles, cap, total);
+        return launched();
+    }
+    const dim3 grid(tiles < slots ? tiles : slots);  // persistent: one workgroup per compute unit
+    if (vec)
+        hipLaunchKernelGGL((scan_persistent_kernel<Op, true, INCL, kWide>), grid, dim3(kLbBlock), 0, s, in,
+                           out, n, scratch, tiles, cap, total);
     else
-        hipLaunchKernelGGL((scan_kernel<Op, false, INCL, kWide>), dim3(tiles), dim3(kLbBlock), 0, s, in, out, n,
-                           scratch, tiles, cap, total);
+        hipLaunchKernelGGL((scan_persistent_kernel<Op, false, INCL, kWide>), grid, dim3(kLbBlock), 0, s, in,
+                           out, n, scratch, tiles, cap, total);
     return launched();
 }
 

@@ -148,8 +148,11 @@ __device__ __forceinline__ uint64_t descriptor(uint32_t tag, uint32_t status, ui
     return (static_cast<uint64_t>((tag << 2) | status) << 32) | value;
 }
 
+__device__ __forceinline__ void perturb(uint32_t key, uint32_t site);
+
 __device__ __forceinline__ void publish(uint64_t *desc, uint32_t tag, uint32_t status,
                                         uint32_t value) {
+    perturb(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(desc) >> 3), 2 + status);
     __hip_atomic_store(desc, descriptor(tag, status, value), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -194,8 +197,34 @@ __device__ __forceinline__ uint64_t peek(uint64_t *desc) {
 // can never leave the kernel spinning.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
+// Timing perturbation for race testing, compiled in only with -DSSC_PERTURB
+// (a separate test build; the library proper compiles it out). perturb(key,
+// site) pauses the wavefront for 0 to 7 x 1024 clocks, chosen by a hash of a
+// uniform key (a tile, a descriptor address, a workgroup) and the call site:
+// before every tile claim, descriptor publication and data-wavefront
+// arrival, and after every look-back poll. Tiles then publish, arrive and
+// claim in orders the normal build rarely shows, with every wait still
+// bounded.
+#ifdef SSC_PERTURB
+__device__ __forceinline__ void perturb(uint32_t key, uint32_t site) {
+    uint32_t h = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(key)));
+    h = h * 0x9E3779B1u ^ site * 0x85EBCA77u;
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    for (uint32_t i = 0; i < (h & 7u); ++i) __builtin_amdgcn_s_sleep(16);
+}
+#else
+__device__ __forceinline__ void perturb(uint32_t, uint32_t) {}
+#endif
+
+// One pause between look-back polls; key (the tile and the poll count) only
+// feeds the perturbation.
 template <int SLEEP>
-__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(SLEEP); }
+__device__ __forceinline__ void poll_pause(uint32_t key) {
+    __builtin_amdgcn_s_sleep(SLEEP);
+    perturb(key, 1);
+}
 
 // Descriptor of tile idx (>= 0) read as base + 32-bit byte offset, so the
 // address needs one VGPR; tiles below 0 read as inclusive with value 0.
@@ -232,7 +261,7 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
                 __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return prefix;
         }
-        poll_pause<SLEEP>();
+        poll_pause<SLEEP>(tile * 64u + spins);
     }
     spins &= 0x7FFFFFFFu;
     int32_t end = static_cast<int32_t>(tile);
@@ -270,7 +299,7 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
                     __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return prefix;
             }
-            poll_pause<SLEEP>();
+            poll_pause<SLEEP>(tile * 64u + spins);
         }
         // add the values from the nearest inclusive tile up (everything read
         // when there is none)
@@ -291,20 +320,32 @@ __device__ typename Op::T look_back(uint64_t *desc, uint32_t tile, uint32_t tag,
 // ------------------------------------------------- wide (fp64) descriptors ---
 // For fp32 scans with fp64 carries a tile's descriptor is two 64-bit words,
 // each laid out as a narrow descriptor ((tag << 2) | status in the high
-// half) holding one half of the double's bits in its low half: word 0 the
-// high 32 bits, word 1 the low 32 bits. The two halves are separate atomic
-// stores, so a reader takes a descriptor as published only when both
-// halves carry this call's tag and the same status; a pair torn between a
-// tile's {aggregate} and {inclusive} stores reads as unpublished and is
-// polled again.
+// half). Word 0 decides the status:
+//   {aggregate}: word 0 alone, its low half the fp32 bits of the tile's sum
+//     (a tile aggregate is an fp32 sum, so 32 bits hold it exactly);
+//   {inclusive}: word 0 the high 32 bits of the fp64 prefix, word 1 (also
+//     marked inclusive) the low 32 bits; word 1 is stored first.
+// A reader whose word 0 says inclusive but whose word 1 does not yet carry
+// this call's tag and the inclusive status reads the tile as unpublished and
+// polls again; word 1 is written by the inclusive store alone, so that wait
+// ends. The aggregate (a data wavefront) and the inclusive stores (the
+// control wavefront, a barrier later) are not ordered by a fence: should the
+// aggregate's word 0 land last, the tile reads as {aggregate} with its
+// correct value from then on and readers walk past it. No interleaving of
+// the stores leaves a tile unreadable.
 __device__ __forceinline__ void publish_wide(uint64_t *desc, uint32_t tile, uint32_t tag,
                                              uint32_t status, double value) {
+    uint64_t *p = desc + 2 * static_cast<uint64_t>(tile);
+    perturb(tile, 5 + status);
+    if (status == kStatusAggregate) {
+        __hip_atomic_store(p, descriptor(tag, status, __float_as_uint(static_cast<float>(value))),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const uint64_t b = static_cast<uint64_t>(__double_as_longlong(value));
-    __hip_atomic_store(desc + 2 * static_cast<uint64_t>(tile),
-                       descriptor(tag, status, static_cast<uint32_t>(b >> 32)), __ATOMIC_RELAXED,
+    __hip_atomic_store(p + 1, descriptor(tag, status, static_cast<uint32_t>(b)), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(desc + 2 * static_cast<uint64_t>(tile) + 1,
-                       descriptor(tag, status, static_cast<uint32_t>(b)), __ATOMIC_RELAXED,
+    __hip_atomic_store(p, descriptor(tag, status, static_cast<uint32_t>(b >> 32)), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -320,9 +361,13 @@ __device__ __forceinline__ uint32_t peek_wide(uint64_t *desc, int32_t idx, uint3
         value = 0.0;
         return kStatusInclusive;
     }
-    const uint32_t sh = status_of(hi, tag), sl = status_of(lo, tag);
+    const uint32_t sh = status_of(hi, tag);
+    if (sh == kStatusAggregate) {
+        value = static_cast<double>(__uint_as_float(static_cast<uint32_t>(hi)));
+        return sh;
+    }
     value = __longlong_as_double(static_cast<long long>((hi << 32) | (lo & 0xFFFFFFFFull)));
-    return sh == sl ? sh : 0u;
+    return sh == kStatusInclusive && status_of(lo, tag) == kStatusInclusive ? sh : 0u;
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
@@ -352,7 +397,7 @@ __device__ double look_back_wide(uint64_t *desc, uint32_t tile, uint32_t tag,
                 __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return prefix;
         }
-        poll_pause<SLEEP>();
+        poll_pause<SLEEP>(tile * 64u + spins);
     }
     int32_t end = static_cast<int32_t>(tile);
     while (true) {
@@ -373,7 +418,7 @@ __device__ double look_back_wide(uint64_t *desc, uint32_t tile, uint32_t tag,
                     __hip_atomic_store(timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 return prefix;
             }
-            poll_pause<SLEEP>();
+            poll_pause<SLEEP>(tile * 64u + spins);
         }
         prefix += wave_sum_f64(lane >= top ? val : 0.0);
         if (top >= 0) return prefix;

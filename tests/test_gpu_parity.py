@@ -563,27 +563,62 @@ def test_scan_i32_wraps_and_in_place():
     assert int(host(tot)[0]) == total
 
 
+# Tile counts that take each scan launch: at most one tile per compute unit
+# (persistent, one tile each), one to two (one workgroup per tile), two to
+# three (persistent, later tiles claimed one at a time) and three or more
+# (persistent, second and third tiles claimed together). MI355X has 256
+# compute units.
+SCAN_TILE_COUNTS = [33, 326, 700, 1500]
+
+
+@pytest.mark.parametrize("tiles", SCAN_TILE_COUNTS)
+def test_scan_paths_by_tile_count(tiles):
+    """Exclusive and inclusive int32 (bit-exact, also in place and from
+    unaligned arrays) and fp32 exclusive (1e-5) at each launch shape, with a
+    ragged last tile."""
+    n = (tiles - 1) * T + 611
+    x = wl.full_int32(0x5CA9 + tiles, n)
+    xd = dev(x)
+    want, total = oracle.exclusive_scan_i32(x)
+    out, tot = ssc.exclusive_scan(xd)
+    assert checks.first_mismatch(host(out), want) == -1 and int(host(tot)[0]) == total
+    check_inclusive_i32(x, xd=xd)
+    y = xd.clone()
+    ssc.exclusive_scan(y, out=y)
+    assert checks.first_mismatch(host(y), want) == -1
+    base = torch.empty(n + 1, dtype=torch.int32, device=DEV)
+    base[1:] = xd
+    uo = torch.empty(n + 1, dtype=torch.int32, device=DEV)[1:]
+    assert base[1:].data_ptr() % 16 == 4
+    _, tot = ssc.exclusive_scan(base[1:], out=uo)
+    assert checks.first_mismatch(host(uo), want) == -1 and int(host(tot)[0]) == total
+    del out, y, base, uo
+    check_scan_f32(wl.unit_float32(0x5CAF + tiles, n))
+
+
 def test_repeated_runs_are_identical():
-    """The look-back must give the same answer whatever order tiles finish in."""
-    x = wl.uniform_below(4242, 2_000_003, 3)
+    """The look-back must give the same answer whatever order tiles finish in:
+    100 compactions and 100 scans of 1,500 tiles (several per workgroup, every
+    claim path) on one scratch, each compared with the oracle."""
+    n = 1499 * T + 17
+    x = wl.uniform_below(4242, n, 3)
     want, m = oracle.compact_i32(x, oracle.PRED_NONZERO)
     xd = dev(x)
     scratch = ssc.new_scratch(x.size, xd.device)
     out = torch.empty_like(xd)
     cnt = torch.empty(1, dtype=torch.int32, device=DEV)
     wd = dev(want)
-    for it in range(30):
+    for it in range(100):
         ssc.compact(xd, "nonzero", out=out, count=cnt, scratch=scratch)
         assert int(host(cnt)[0]) == m, it
         assert torch.equal(out[:m], wd), it
     sw, _ = oracle.exclusive_scan_i32(x)
     swd = dev(sw)
     sout = torch.empty_like(xd)
-    for it in range(10):
+    for it in range(100):
         ssc.exclusive_scan(xd, out=sout, scratch=scratch)
         assert torch.equal(sout, swd), it
-    # word 2 of the scratch: set only if a look-back wait gave up
-    assert int(host(scratch[8:12].view(torch.int32))[0]) == 0
+    assert not ssc.timed_out(scratch)
 
 
 @pytest.mark.parametrize("shift_words", [4, 12])

@@ -1,0 +1,103 @@
+"""Parity under perturbed timing: the same calls through libssc_perturb.so.
+
+That build (the library's sources compiled with -DSSC_PERTURB) pauses every
+tile claim, descriptor publication, data-wavefront arrival and look-back poll
+for 0 to 7 x 1024 clocks chosen by a hash of the tile, workgroup or poll
+count, so workgroups claim, publish and finish in orders the library proper
+rarely shows. Every result must still match the oracle exactly (fp32 scans
+within 1e-5), repeated calls must agree, and no look-back wait may give up.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scan_stream_compaction_amd as ssc
+from scan_stream_compaction_amd import workloads as wl
+from tests import checks
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not os.path.exists(ssc.PERTURB_LIB_PATH),
+                       reason="libssc_perturb.so not built (python -m scan_stream_compaction_amd.build)"),
+]
+
+T = 30720
+SENTINEL = -123456789
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def perturbed():
+    with ssc.using_library(ssc.PERTURB_LIB_PATH) as L:
+        yield L
+
+
+@pytest.mark.parametrize("tiles", [33, 700, 1500])
+def test_compaction_family_under_perturbation(perturbed, tiles):
+    n = (tiles - 1) * T + 611
+    x = wl.full_int32(0x7AC3 + tiles, n)
+    xd = dev(x)
+    scratch = ssc.new_scratch(n, xd.device)
+    for pred, pa, pb in (("odd", 0, 0), ("mod_lt", 100, 1), ("mod_lt", 100, 99)):
+        p = ssc.PRED[pred]
+        want, m, want_ranks = oracle.compact_i32(x, p, pa, pb, want_ranks=True)
+        wd, wr = dev(want), dev(want_ranks)
+        out = torch.empty_like(xd)
+        for rep in range(3):
+            out.fill_(SENTINEL)
+            _, cnt, rk = ssc.compact(xd, p, pa, pb, out=out, ranks=True, scratch=scratch)
+            assert int(host(cnt)[0]) == m, (pred, pb, rep)
+            assert torch.equal(out[:m], wd), (pred, pb, rep)
+            assert bool((out[m:] == SENTINEL).all()), (pred, pb, rep)
+            assert torch.equal(rk, wr), (pred, pb, rep)
+    pw, k = oracle.partition_i32(x, oracle.PRED_EVEN)
+    pout, pk = ssc.partition(xd, "even", scratch=scratch)
+    assert int(host(pk)[0]) == k and checks.first_mismatch(host(pout), pw) == -1
+    iw, mi = oracle.select_index_i32(x, oracle.PRED_ODD)
+    idx, icnt = ssc.select_index(xd, "odd", scratch=scratch)
+    assert int(host(icnt)[0]) == mi and checks.first_mismatch(host(idx)[:mi], iw) == -1
+    assert not ssc.timed_out(scratch)
+
+
+@pytest.mark.parametrize("tiles", [33, 326, 700, 1500])
+def test_scans_under_perturbation(perturbed, tiles):
+    n = (tiles - 1) * T + 611
+    x = wl.full_int32(0x5CA7 + tiles, n)
+    xd = dev(x)
+    scratch = ssc.new_scratch(n, xd.device)
+    want, total = oracle.exclusive_scan_i32(x)
+    wd = dev(want)
+    out = torch.empty_like(xd)
+    for rep in range(3):
+        _, tot = ssc.exclusive_scan(xd, out=out, scratch=scratch)
+        assert torch.equal(out, wd) and int(host(tot)[0]) == total, rep
+    inc = oracle.inclusive_scan_i32(x)
+    ssc.inclusive_scan(xd, out=out, scratch=scratch)
+    assert checks.first_mismatch(host(out), inc) == -1
+    del out, wd
+    f = wl.unit_float32(0x5CA8 + tiles, n)
+    ref, ref_total = oracle.exclusive_scan_f32(f)
+    fo, ftot = ssc.exclusive_scan(dev(f), scratch=scratch)
+    max_rel, _, ok = checks.f32_scan_rel_errors(host(fo), ref)
+    assert ok, max_rel
+    assert abs(float(host(ftot)[0]) - ref_total) <= checks.F32_SCAN_REL_TOL * ref_total
+    assert not ssc.timed_out(scratch)
+
+
+def test_radix_sort_under_perturbation(perturbed):
+    keys = wl.full_uint32(0x5EED7, 1 << 20)
+    got = ssc.radix_sort4(dev(keys.view(np.int32)))
+    assert checks.first_mismatch(host(got).view(np.uint32), oracle.radix_sort_u32(keys)) == -1
