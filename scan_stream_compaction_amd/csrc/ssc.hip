@@ -1101,6 +1101,240 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 #undef SSC_FLAG_AND_ARRIVE
 }
 
+// ================================================== flag-byte selection ---
+// Selection by flag bytes (idx[k] = position of the k-th nonzero flag) with
+// tiles four times the compaction kernel's. A flag is one byte, so a
+// 30720-flag tile is too little data to hide the look-back and the barrier
+// each tile costs. Here each data lane loads eight 128-bit words of flags
+// (8192 per data wavefront, 122,880 per tile) and turns them into four
+// 32-bit masks as soon as they land. The bytes are then dead, so two raw
+// register sets keep two tiles of loads in flight. After the tile's barrier a
+// wavefront writes its survivors' positions in four rounds of two loads
+// (2048 flags each), every round staged in its 8 KiB LDS region and streamed
+// out as one run. The claims, arrivals, look-back and control wavefront are
+// the compaction kernel's. The flag array must be 16-byte aligned.
+constexpr int kFlagLoads = 8;                                     // 128-bit loads per lane
+constexpr int kFlagChunk = kWave * 16 * kFlagLoads;               // 8192 flags per data wavefront
+constexpr int64_t kFlagTile = static_cast<int64_t>(kDataWaves) * kFlagChunk;  // 122,880
+
+// The nonzero bytes of a 32-bit word as a 4-bit mask (bit i = byte i). Bit 7
+// of each byte of ((w & 0x7F7F7F7F) + 0x7F7F7F7F) | w is set iff that byte
+// is nonzero (no carry leaves a byte); multiplying the four bits, moved to
+// bits 0, 8, 16, 24, by 2^24 + 2^17 + 2^10 + 2^3 puts byte i's bit at
+// bit 24 + i, with no other product term at or above bit 24 below bit 32.
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t w) {
+    const uint32_t hi = (((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u;
+    return ((hi >> 7) * 0x01020408u) >> 24;
+}
+
+__global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_flags_kernel(
+    const uint8_t *__restrict__ flags, int32_t *__restrict__ idx, int64_t n, void *scratch,
+    uint32_t num_tiles, uint32_t capacity, int32_t *__restrict__ count) {
+    // one staging region per data wavefront, plus one of padding for run reads
+    __shared__ __attribute__((aligned(16))) uint32_t s_stage[kDataWaves + 1][kStageWords];
+    __shared__ uint32_t s_tot[kDataWaves];
+    __shared__ uint32_t s_pre[3][kDataWaves + 1];  // chunk prefixes + aggregate, by tile mod 3
+    __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
+    __shared__ uint32_t s_first[3], s_epoch, s_arrive;
+    static_assert(kFlagChunk / 4 == kStageWords, "a round of two loads fills one staging region");
+
+    const ScratchView sv = view(scratch);
+    const int lane = lane_id();
+    const int w = static_cast<int>(uniform(threadIdx.x / kWave));
+    if (threadIdx.x == 0) {
+        const uint64_t c = claim_tiles(sv, 1);
+        s_first[0] = static_cast<uint32_t>(c);
+        s_epoch = static_cast<uint32_t>(c >> 32);
+        s_arrive = 0;
+    }
+    __syncthreads();  // B0: the first tile
+    uint32_t tile = uniform(s_first[0]);
+    const uint32_t epoch = uniform(s_epoch);
+    const uint32_t tag = epoch & kTagMask;
+    if (tile >= num_tiles) {
+        if (w == kCtrlWave && lane == 0) finish_claims(sv, epoch, gridDim.x, num_tiles, capacity);
+        return;
+    }
+    bool last_claim = false;
+    if (w == kCtrlWave && lane == 0) last_claim = claim_second_third(sv, num_tiles, s_first);
+    uint32_t par = 0;
+    uint32_t tri = 0;
+
+    if (w == kCtrlWave) {
+        __syncthreads();  // B0b: the second and third tiles
+        uint32_t nxt = uniform(s_first[1]);
+        uint32_t nxt2 = uniform(s_first[2]);
+        __syncthreads();  // B0': the first tile's arrivals are in
+        while (true) {
+            uint32_t nxt3 = kNoTile;
+            if (lane == 0 && nxt2 < num_tiles) {
+                nxt3 = static_cast<uint32_t>(claim_tiles(sv, 1));
+                last_claim = nxt3 >= num_tiles;
+            }
+            uint32_t prefix = 0;
+            if (tile != 0) prefix = look_back<SumU32, 16, true>(sv.desc, tile, tag, sv.timed_out);
+            if (lane == 0) {
+                s_base[par] = prefix;
+                s_next[par] = nxt3;
+            }
+            __syncthreads();  // B1
+            const uint32_t agg = uniform(s_pre[tri][kDataWaves]);
+            if (lane == 0) {
+                // {inclusive} at least one barrier after this tile's {aggregate}
+                if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, prefix + agg);
+                if (tile == num_tiles - 1) *count = static_cast<int32_t>(prefix + agg);
+                if (last_claim) finish_claims(sv, epoch, gridDim.x, num_tiles, capacity);
+                last_claim = false;
+            }
+            if (nxt >= num_tiles) return;
+            tile = nxt;
+            nxt = nxt2;
+            nxt2 = uniform(nxt3);
+            par ^= 1u;
+            tri = tri == 2u ? 0u : tri + 1u;
+        }
+    }
+
+    const auto chunk_of = [&](uint32_t t) {
+        return static_cast<int64_t>(t) * kFlagTile + static_cast<int64_t>(w) * kFlagChunk;
+    };
+    const auto rem_of = [&](uint32_t t) {
+        return t < num_tiles ? chunk_rem<kFlagChunk>(n, chunk_of(t)) : 0u;
+    };
+    // Eight 128-bit words of flags per lane: byte b of load j is flag
+    // chunk + j*1024 + lane*16 + b. The resource covers the valid flags
+    // rounded up to whole dwords (the dword holding the last flag is read
+    // whole: 4-byte aligned, it never crosses a page); the rest read as 0.
+    const auto load = [&](uint32_t t, int ln, u32x4(&v)[kFlagLoads]) {
+        const __amdgpu_buffer_rsrc_t r = buffer_rsrc(flags + chunk_of(t), (rem_of(t) + 3u) & ~3u);
+#pragma unroll
+        for (int j = 0; j < kFlagLoads; ++j)
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(r, j * (kWave * 16) + ln * 16, 0, kNT);
+    };
+    // m[q] = the flags of loads 2q (bits 0-15) and 2q+1 (bits 16-31), those
+    // past rem cleared. Returns the chunk's total.
+    const auto masks = [&](const u32x4(&v)[kFlagLoads], uint32_t rem, int ln, uint32_t(&m)[4]) {
+        uint32_t tot = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t x = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) x |= nonzero_bytes(v[2 * q + h][k]) << (16 * h + 4 * k);
+            if (rem < static_cast<uint32_t>(kFlagChunk)) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int32_t lim = static_cast<int32_t>(rem) - ((2 * q + h) * (kWave * 16) + ln * 16);
+                    const uint32_t keep =
+                        lim >= 16 ? 0xFFFFu : (lim <= 0 ? 0u : (1u << static_cast<uint32_t>(lim)) - 1u);
+                    x &= ~(0xFFFFu << (16 * h)) | (keep << (16 * h));
+                }
+            }
+            m[q] = x;
+            tot += static_cast<uint32_t>(__builtin_popcount(x));
+        }
+        return tot;
+    };
+    // The last data wavefront to arrive scans the 15 totals into s_pre[TRI]
+    // and publishes tile T's {aggregate} ({inclusive} for tile 0).
+    const auto arrive = [&](uint32_t lane_tot, uint32_t t, uint32_t tri_, int ln) {
+        const uint32_t a = static_cast<uint32_t>(
+            __builtin_amdgcn_readlane(static_cast<int>(wave_inclusive_scan<SumU32>(lane_tot)), kWave - 1));
+        if (ln == 0) s_tot[w] = a;
+        perturb(t * 16u + w, 11);
+        uint32_t before = 0;
+        if (ln == 0)
+            before = __hip_atomic_fetch_add(&s_arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (uniform(before) == kDataWaves - 1) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const uint32_t mine = ln < kDataWaves ? s_tot[ln] : 0u;
+            const uint32_t incl = wave_inclusive_scan<SumU32>(mine);
+            if (ln < kDataWaves) s_pre[tri_][ln] = incl - mine;
+            const uint32_t agg =
+                static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kDataWaves - 1));
+            if (ln == 0) {
+                s_arrive = 0;
+                s_pre[tri_][kDataWaves] = agg;
+                if (t < num_tiles) publish(sv.desc + t, tag, t == 0 ? kStatusInclusive : kStatusAggregate, agg);
+            }
+        }
+    };
+    // The survivors' positions of the current chunk, in four rounds of two
+    // loads: ranks by one packed DPP scan of the two loads' counts (16-bit
+    // fields: at most 1024 each), positions staged at their ranks, then one
+    // run to idx[seg + done ..).
+    const auto write = [&](const uint32_t(&m)[4], int64_t chunk, uint32_t seg, int ln) {
+        uint32_t done = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t mq = m[q];
+            const uint32_t c = static_cast<uint32_t>(__builtin_popcount(mq & 0xFFFFu)) |
+                               (static_cast<uint32_t>(__builtin_popcount(mq >> 16)) << 16);
+            const uint32_t incl = wave_inclusive_scan<SumU32>(c);
+            const uint32_t ex = incl - c;
+            const uint32_t last = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), kWave - 1));
+            const uint32_t t0 = last & 0xFFFFu;
+            uint32_t r0 = ex & 0xFFFFu;
+            uint32_t r1 = t0 + (ex >> 16);
+            // positions of flags past n are formed but never staged: unsigned
+            const uint32_t p0 = static_cast<uint32_t>(chunk) + static_cast<uint32_t>(2 * q * (kWave * 16) + ln * 16);
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const uint32_t f0 = (mq >> b) & 1u;
+                const uint32_t f1 = (mq >> (16 + b)) & 1u;
+                if (f0) s_stage[w][r0] = p0 + static_cast<uint32_t>(b);
+                if (f1) s_stage[w][r1] = p0 + static_cast<uint32_t>(kWave * 16 + b);
+                r0 += f0;
+                r1 += f1;
+            }
+            const uint32_t len = t0 + (last >> 16);
+            stream_run<kStageWords>(s_stage[w], reinterpret_cast<uint32_t *>(idx), seg + done, len, n, ln);
+            done += len;
+        }
+    };
+
+    u32x4 ra[kFlagLoads], rb[kFlagLoads];  // raw flags of the two tiles in flight
+    uint32_t mc[4], mn[4];                 // masks of the current and the next tile
+
+    // One tile: X holds the next tile's flags, Y the tile after next's (in
+    // flight); once X's masks are taken, X takes the loads of the tile the
+    // control wavefront claimed during this one.
+#define SSC_FLAG_TILE(X)                                                                      \
+    {                                                                                         \
+        int ln = lane;                                                                        \
+        asm volatile("" : "+v"(ln));                                                          \
+        const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                     \
+        arrive(masks(X, rem_of(nxt), ln, mn), nxt, tri_n, ln);                                \
+        __syncthreads(); /* B1: this tile's base is known */                                  \
+        const uint32_t nxt3 = uniform(s_next[par]);                                           \
+        load(nxt3, ln, X);                                                                    \
+        write(mc, chunk_of(tile), uniform(s_base[par]) + uniform(s_pre[tri][w]), ln);         \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) mc[q] = mn[q];                          \
+        tile = nxt;                                                                           \
+        nxt = nxt2;                                                                           \
+        nxt2 = nxt3;                                                                          \
+        par ^= 1u;                                                                            \
+        tri = tri_n;                                                                          \
+    }
+
+    load(tile, lane, ra);
+    __syncthreads();  // B0b: the second and third tiles
+    uint32_t nxt = uniform(s_first[1]);
+    uint32_t nxt2 = uniform(s_first[2]);
+    load(nxt, lane, rb);
+    arrive(masks(ra, rem_of(tile), lane, mc), tile, tri, lane);
+    load(nxt2, lane, ra);
+    __syncthreads();  // B0': every wavefront has arrived for the first tile
+    while (true) {
+        SSC_FLAG_TILE(rb)
+        if (tile >= num_tiles) break;
+        SSC_FLAG_TILE(ra)
+        if (tile >= num_tiles) break;
+    }
+#undef SSC_FLAG_TILE
+}
+
 // =========================================================== scan kernel ---
 constexpr int kScanPollSleep = 127;  // look-back poll interval, s_sleep units (measured)
 // Exclusive (or, INCL, inclusive) scan of 32-bit values: one tile per
@@ -2575,6 +2809,14 @@ int flags_impl(const void *in, const uint8_t *flags, void *out, int64_t n, int32
     const SelArgs a{in, flags, out, nullptr};
     const PredArgs pr{0, 0, 0u, 0u, 0u, 0u};
     const uint32_t cap = capacity_of(scratch_bytes);
+    if (!values && aligned(flags, 16)) {
+        const uint32_t tiles = static_cast<uint32_t>((n + kFlagTile - 1) / kFlagTile);
+        uint32_t slots = 0;
+        SSC_TRY(compute_units(&slots));
+        hipLaunchKernelGGL(select_flags_kernel, dim3(tiles < slots ? tiles : slots), dim3(kLbBlock), 0, s,
+                           flags, static_cast<int32_t *>(out), n, scratch, tiles, cap, count);
+        return launched();
+    }
     if (!values)
         return launch_select<FmtFlags<true, false>, 0, kSelectIndex>(a, n, pr, scratch, cap, count,
                                                                      nullptr, nullptr, s);

@@ -116,6 +116,43 @@ def test_flag_bytes_full_size():
     say(f"  kept {m} of {n}")
 
 
+# Selection by flag bytes from a 16-byte aligned array takes its own kernel:
+# 8192 flags per data wavefront (eight 128-bit loads per lane), 122,880 per
+# tile. Sizes around its chunk and tile, byte counts that end inside a dword,
+# and tile counts on both sides of the claim paths (256 compute units; the
+# second and third tiles are claimed together from 768 tiles).
+TS = 15 * 8192
+SEL_FLAG_N = [8191, 8192, 8193, 8195, 16 * 1024 + 7, TS - 1, TS, TS + 1, TS + 3, 3 * TS + 611,
+              257 * TS + 13, 800 * TS + 5]
+
+
+@pytest.mark.parametrize("n", SEL_FLAG_N)
+def test_selection_by_flag_bytes_large_tiles(n):
+    say(f"  selection by flags n={n}")
+    for keep in (0, 1, 50, 100):
+        f = wl.flag_bytes(500 + n + keep, n, keep)
+        want, m = oracle.select_flags(f)
+        fd = dev(f)
+        assert fd.data_ptr() % 16 == 0
+        idx = torch.full((n,), SENTINEL, dtype=torch.int32, device=DEV)
+        _, cnt = ssc.select_flags(fd, out=idx)
+        assert int(host(cnt)[0]) == m, (n, keep)
+        o = host(idx)
+        assert checks.first_mismatch(o[:m], want) == -1, (n, keep)
+        assert np.all(o[m:] == SENTINEL), "selection wrote past count"
+        if n <= 3 * TS + 611:
+            # 4-byte but not 16-byte aligned flags keep the compaction kernel's format
+            big = torch.zeros(n + 4, dtype=torch.uint8, device=DEV)
+            fu = big[4:]
+            fu.copy_(fd)
+            assert fu.data_ptr() % 16 == 4
+            idx.fill_(SENTINEL)
+            _, cnt = ssc.select_flags(fu, out=idx)
+            assert int(host(cnt)[0]) == m
+            o = host(idx)
+            assert checks.first_mismatch(o[:m], want) == -1 and np.all(o[m:] == SENTINEL)
+
+
 def check_kv(keys: np.ndarray, vals: np.ndarray, pred, a=0, b=0, kd=None, vd=None):
     p = ssc.PRED[pred] if isinstance(pred, str) else pred
     wk, wv, m = oracle.compact_kv(keys, vals, p, a, b)

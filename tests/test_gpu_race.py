@@ -69,6 +69,10 @@ def test_compaction_family_under_perturbation(perturbed, tiles):
     iw, mi = oracle.select_index_i32(x, oracle.PRED_ODD)
     idx, icnt = ssc.select_index(xd, "odd", scratch=scratch)
     assert int(host(icnt)[0]) == mi and checks.first_mismatch(host(idx)[:mi], iw) == -1
+    f = wl.flag_bytes(0x7AC4 + tiles, n, 50)
+    fw, mf = oracle.select_flags(f)
+    fidx, fcnt = ssc.select_flags(dev(f), scratch=scratch)
+    assert int(host(fcnt)[0]) == mf and checks.first_mismatch(host(fidx)[:mf], fw) == -1
     assert not ssc.timed_out(scratch)
 
 
