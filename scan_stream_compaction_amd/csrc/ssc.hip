@@ -1044,6 +1044,10 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         rem_nxt = rem_of(nxt);                                                                \
         SSC_FLAG_AND_ARRIVE(NX, nxt, rem_nxt, fm_nxt, a_nxt, tri_n, ln)                       \
         __syncthreads(); /* B1: this tile's base is known */                                  \
+        /* the ranks' leads come from fm_cur after the barrier: computed before  */           \
+        /* it, they stayed live across the next chunk's flags and the kernel     */           \
+        /* spilled (MOD_LT 24 dwords per lane; 485 -> 465 us at 2^28)            */           \
+        if constexpr (KIND == kCompactRanks) asm volatile("" : "+v"(fm_cur));                 \
         const uint32_t base = uniform(s_base[par]);                                           \
         const uint32_t nxt3 = uniform(s_next[par]);                                           \
         const int64_t chunk_now = chunk_of(tile);                                             \
