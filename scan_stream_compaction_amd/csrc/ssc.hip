@@ -860,20 +860,23 @@ enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3, kParti
 // reuse the current chunk's registers, so they leave only once that chunk is
 // staged; with three they leave before the staging. Which one a kernel takes
 // is measured (2^28 elements, microseconds per launch, two sets -> three):
-//   three: odd 50% kept 285.4 -> 274.4, odd 1% 210.9 -> 206.8, odd
-//     selection 283.6 -> 275.4, int64 279.1 -> 275.8, key-value pairs
-//     283.7 -> 270.7, flag-byte compaction 327.4 -> 317.0;
-//   two: MOD_LT(100, s) s = 1 / 10 / 99 (216 -> 233 / 231 -> 240 / 367 ->
-//     372; 50%: 289 -> 281), ranks 463 -> 476, partitions 537 -> 540, the
-//     radix driver's chained splits (2^24 keys, 1,176 -> 1,210 a sort), and
-//     selection by flag bytes 181 -> 192.
-template <class F, int P, int KIND>
+//   three: odd 50% kept 286.4 -> 267.1, odd 1% 210.4 -> 201.7, odd
+//     selection 284.2 -> 267.0, key-value pairs 284.8 -> 268.4, int64
+//     279.6 -> 273.1, flag-byte compaction 327.2 -> 310.2;
+//   two: ranks 463 -> 476, partitions 537 -> 540, the radix driver's
+//     chained splits (2^24 keys, 1,176 -> 1,210 a sort);
+//   MOD_LT(100, s) by the fraction it is expected to keep (DEEP, chosen
+//     on the host): three from s >= m/4 (50%: 289.5 -> 269.5, 99%: 366.3 ->
+//     365.8), two below (1%: 216 -> 226, 10%: 230.5 -> 233.6). Either
+//     is correct for any input; only the speed depends on the fraction kept.
+template <class F, int P, int KIND, bool DEEP = false>
 constexpr bool three_sets() {
-    return (KIND == kCompact || KIND == kSelectIndex) && P != 5 && F::kValues;
+    return (KIND == kCompact || KIND == kSelectIndex) && (P != 5 || DEEP) && F::kValues;
 }
-// The look-back with three sets goes straight to its window and polls at
-// s_sleep 32; with two it first waits on its predecessor and polls at s_sleep
-// 16 (each measured best for its pipeline).
+// The look-back with three sets (MOD_LT aside) goes straight to its window and
+// polls at s_sleep 32; with two it first waits on its predecessor and polls
+// at s_sleep 16 (each measured best for its pipeline; MOD_LT with three sets
+// polls as with two: 50% kept 273.5 -> 269.5, 1% 229.4 -> 225.9).
 template <bool THREE>
 constexpr int sel_poll_sleep() {
     return THREE ? 32 : 16;
@@ -881,7 +884,7 @@ constexpr int sel_poll_sleep() {
 
 // F is the element format (what a chunk holds and how survivors are staged
 // and written); partition and ranks are defined for 32-bit elements.
-template <class F, int P, int KIND>
+template <class F, int P, int KIND, bool DEEP = false>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(
     SelArgs a, int64_t n, PredArgs pr, void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
@@ -899,7 +902,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
     __shared__ uint32_t s_first[3], s_epoch, s_arrive;
 
-    constexpr bool kThree = three_sets<F, P, KIND>();
+    constexpr bool kThree = three_sets<F, P, KIND, DEEP>();
+    constexpr bool kLbFast = kThree && P != 5;  // look-back without the predecessor poll
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
@@ -935,8 +939,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             }
             uint32_t prefix = 0;
             if (tile != 0)
-                prefix = look_back<SumU32, sel_poll_sleep<kThree>(), !kThree>(sv.desc, tile, tag,
-                                                                              sv.timed_out);
+                prefix = look_back<SumU32, sel_poll_sleep<kLbFast>(), !kLbFast>(sv.desc, tile, tag,
+                                                                                sv.timed_out);
             if (lane == 0) {
                 s_base[par] = prefix;
                 s_next[par] = nxt3;
@@ -2463,9 +2467,19 @@ int dispatch_pred(int pred, bool vec, A... a) {
     }
 }
 
+// Or-ed into a kind: a MOD_LT(m, s) compaction or selection expected to keep
+// at least a quarter of uniform input (4s >= m) takes three register sets
+// (see three_sets). Only the speed depends on it.
+constexpr int kDeep = 0x100;
+inline int with_depth(int kind, int pred, int32_t pa, int32_t pb) {
+    const bool deep = pred == SSC_PRED_MOD_LT && (kind == kCompact || kind == kSelectIndex) &&
+                      4 * static_cast<int64_t>(pb) >= static_cast<int64_t>(pa);
+    return deep ? (kind | kDeep) : kind;
+}
+
 // One launch of the persistent kernel for element format F and kind KIND:
 // one workgroup per compute unit, at most one per tile.
-template <class F, int P, int KIND>
+template <class F, int P, int KIND, bool DEEP = false>
 int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint32_t capacity,
                   int32_t *count, int32_t *ranks, const int32_t *kept, hipStream_t s) {
     constexpr int64_t kTileElems = F::Shape::kTileElems;
@@ -2473,7 +2487,7 @@ int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint3
     uint32_t slots = 0;
     SSC_TRY(compute_units(&slots));
     const dim3 grid(tiles < slots ? tiles : slots);
-    hipLaunchKernelGGL((select_kernel<F, P, KIND>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
+    hipLaunchKernelGGL((select_kernel<F, P, KIND, DEEP>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
                        tiles, capacity, count, ranks, kept);
     return launched();
 }
@@ -2486,16 +2500,25 @@ struct LaunchSelect {
                    const int32_t *kept, hipStream_t s) {
         using F = FmtB32<VEC>;
         const SelArgs a{in, nullptr, out, nullptr};
-        switch (kind) {
+        const bool deep = (kind & kDeep) != 0;
+        switch (kind & ~kDeep) {
         case kPartition:
             return launch_select<F, P, kPartition>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         case kCompactRanks:
             return launch_select<F, P, kCompactRanks>(a, n, pr, scratch, capacity, count, ranks,
                                                       kept, s);
         case kSelectIndex:
+            if constexpr (P == 5)
+                if (deep)
+                    return launch_select<F, P, kSelectIndex, true>(a, n, pr, scratch, capacity, count,
+                                                                   ranks, kept, s);
             return launch_select<F, P, kSelectIndex>(a, n, pr, scratch, capacity, count, ranks,
                                                      kept, s);
         default:
+            if constexpr (P == 5)
+                if (deep)
+                    return launch_select<F, P, kCompact, true>(a, n, pr, scratch, capacity, count,
+                                                               ranks, kept, s);
             return launch_select<F, P, kCompact>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         }
     }
@@ -2711,7 +2734,7 @@ int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t p
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect, F32>(pred, vec, ranks ? kCompactRanks : kCompact, in, out, n,
+    return dispatch_pred<LaunchSelect, F32>(pred, vec, with_depth(ranks ? kCompactRanks : kCompact, pred, pa, pb), in, out, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count, ranks,
                                        static_cast<const int32_t *>(nullptr), s);
@@ -2735,7 +2758,7 @@ int select_index_impl(const int32_t *in, int32_t *idx, int64_t n, int pred, int3
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
-    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), kSelectIndex, in, idx, n,
+    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), with_depth(kSelectIndex, pred, pa, pb), in, idx, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count,
                                        static_cast<int32_t *>(nullptr),
