@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published peak
+WARM_MS = 20.0  # GPU time each extra row runs before its timed region
 METRIC = "ordered compaction GB/s and % HBM peak, 2^28 int32, 50% selectivity"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "compact_odd_2p28_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "scan_stream_compaction_amd", "csrc", f)
@@ -71,14 +72,37 @@ def measured_traffic():
         return None
 
 
-def timed_calls(fn, steps: int, stream):
+def warm_up(fn, stream, ms: float = WARM_MS, cap: int = 100):
+    """Run fn() back to back for at least `ms` of GPU time (at least three
+    calls, at most `cap`). After an idle gap this GPU runs launches 11-40 of
+    a load up to a quarter slower than the sustained state it settles into by
+    launch 50-70 (2^28 MOD_LT(100, 50) compaction: 347 us per launch at
+    launches 11-20, 269-272 from launch 90 on), so every row is timed
+    sustained."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(3):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    per = max(start.elapsed_time(end) / 3, 1e-3)
+    for _ in range(min(cap, int(ms / per))):
+        fn()
+
+
+def timed_calls(fn, steps: int, stream, warm: bool = True):
     """Run fn() `steps` times back to back between two synchronizations, with
     one HIP event pair around the whole region on `stream` (the stream the
-    kernels run on). Returns (region ms, ms per call, wall seconds). Events
-    between the calls are avoided: on this GPU each recorded event writes the
-    caches back, which puts about 10 us between launches that run back to
-    back otherwise."""
+    kernels run on), after warm_up() unless `warm` is False. Returns (region
+    ms, ms per call, wall seconds). Events between the calls are avoided: on
+    this GPU each recorded event writes the caches back, which puts about
+    10 us between launches that run back to back otherwise."""
     import torch
+    if warm:
+        warm_up(fn, stream)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -480,7 +504,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 60 launches (about 16 ms): the timed launches then fall after the
+    # power-state dip of launches 11-40 (see warm_up)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extra", choices=("all", "copy", "none"), default="all",
                     help="extra rows: copy ceiling, selectivity sweep and atomic comparison")
@@ -528,14 +554,13 @@ def main():
     log(f"parity ok: kept {m} of {n} ({m / n:.5f})")
     alg_bytes = 4 * n + 4 * m  # input read + survivors written
 
-    # The headline is timed after the other rows have run: on this part the
-    # memory clocks settle some milliseconds into sustained streaming, and
-    # launches 11-40 after an idle period run about 4% slower than the
-    # sustained rate (per-launch kernel traces: launches 1-10 after 0.5 s idle
-    # 268 us, 11-30 277-279 us, 51-100 266 us; after 40 copy launches a flat
-    # 266 us). The first timed launches after the parity check are kept
-    # below as cold_us for the record.
-    _, cold_ms, _ = timed_calls(step, args.steps, stream)
+    # The headline is timed after the other rows have run and after its W
+    # warm-up launches: on this part launches 11-40 after an idle period run
+    # slower than the sustained rate (per-launch kernel traces: launches 1-10
+    # after 0.5 s idle 268 us, 11-30 277-279 us, 51-100 266 us; after 40 copy
+    # launches a flat 266 us). The first launches after the parity check are
+    # kept below as cold_us for the record.
+    _, cold_ms, _ = timed_calls(step, args.steps, stream, warm=False)
     extra = {}
     if args.extra in ("all", "copy"):
         cp = torch.empty_like(x)
@@ -587,7 +612,7 @@ def main():
         extra["other_formats"] = format_rows(x, out, dev, max(5, args.steps // 2), stream)
     for _ in range(args.warmup):
         step()
-    region_ms, ms_per_step, wall = timed_calls(step, args.steps, stream)
+    region_ms, ms_per_step, wall = timed_calls(step, args.steps, stream, warm=False)
     mask = (x & 1).bool()
     recheck("headline", scratch, lambda: int(count.item()) == m and torch.equal(out[:m], torch.masked_select(x, mask)))
     del mask
