@@ -1506,10 +1506,10 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 // WIDE (fp32): carries between tiles are fp64 (wide descriptors, fp64
 // look-back) and each output is rounded to fp32 once from the fp64 sum of
 // base, chunk prefix and in-chunk prefix. Forward progress as for
-// select_kernel. Measured at 2^28 int32 (exclusive): 369.7 us against 377.1
-// for one workgroup per tile; fp32 376 against 405; 2^24: 29.8 against 36.1;
-// without the look-back wait (results wrong, timing only) 368 -> 378 us
-// before the per-load resources, i.e. the look-back costs about 10 us.
+// select_kernel. Measured (interleaved A/B, exclusive int32): 2^28 369.7 us
+// against 377.1 for one workgroup per tile, fp32 376 against 405, 2^24 29.8
+// against 36.1; a timing-only build without the look-back wait ran about
+// 10 us faster at 2^28.
 constexpr int kScanPSleep = 32;  // look-back poll interval, s_sleep units
 
 template <class Op, bool VEC, bool INCL, bool WIDE>

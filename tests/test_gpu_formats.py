@@ -153,6 +153,23 @@ def test_selection_by_flag_bytes_large_tiles(n):
             assert checks.first_mismatch(o[:m], want) == -1 and np.all(o[m:] == SENTINEL)
 
 
+def test_selection_by_flag_bytes_every_byte_value():
+    """Every byte value 0..255 at every byte offset within the 16-byte words
+    the large-tile kernel loads (block b of 256 flags is 0..255 rotated by b),
+    repeated past one chunk; nonzero means kept, whatever the bits."""
+    i = np.arange(256 * 16 * 3, dtype=np.int64)
+    f = ((i % 256 + (i // 256) % 16) % 256).astype(np.uint8)
+    want, m = oracle.select_flags(f)
+    assert m == f.size - f.size // 256
+    fd = dev(f)
+    assert fd.data_ptr() % 16 == 0
+    idx, cnt = ssc.select_flags(fd)
+    assert int(host(cnt)[0]) == m
+    assert checks.first_mismatch(host(idx)[:m], want) == -1
+    x = wl.full_int32(0xB17E, f.size)
+    check_flags(x, f)
+
+
 def check_kv(keys: np.ndarray, vals: np.ndarray, pred, a=0, b=0, kd=None, vd=None):
     p = ssc.PRED[pred] if isinstance(pred, str) else pred
     wk, wv, m = oracle.compact_kv(keys, vals, p, a, b)
