@@ -96,10 +96,13 @@ def load_library(path: str) -> ctypes.CDLL:
 
 
 def lib() -> ctypes.CDLL:
-    """Load libssc.so (built in-tree by ``python -m scan_stream_compaction_amd.build``)."""
+    """Load libssc.so (built in-tree by ``python -m scan_stream_compaction_amd.build``),
+    or the build of the same sources that the environment variable
+    SSC_LIBRARY names (the race checks run the whole suite through
+    libssc_perturb.so that way)."""
     global _lib
     if _lib is None:
-        _lib = load_library(LIB_PATH)
+        _lib = load_library(os.environ.get("SSC_LIBRARY") or LIB_PATH)
     return _lib
 
 
