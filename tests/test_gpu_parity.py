@@ -260,7 +260,8 @@ def test_headline_odd_selection_full_size(headline):
 
 
 def test_maximum_size_compaction_and_selection():
-    """n = 2^31 - 1, the largest n the C ABI takes (8 GiB in and out): byte
+    """n = 2^31 - 1, the largest n the C ABI takes (8 GiB in and out), for
+    compaction, selection (by predicate and by flag bytes) and the scan: byte
     offsets past 4 GiB, tile numbers near the descriptor capacity, and a
     count near 2^30; compared element by element with the full oracle."""
     n = 2**31 - 1
@@ -282,6 +283,20 @@ def test_maximum_size_compaction_and_selection():
     wi, mi = oracle.select_index_i32(x, oracle.PRED_ODD)
     assert mi == m and checks.first_mismatch(host(idx)[:m], wi) == -1
     say(f"  kept {m} of {n}")
+    # the same positions by flag bytes (x & 1, 2 GiB): the large-tile kernel,
+    # positions up to 2^31 - 2
+    fd = (xd & 1).to(torch.uint8)
+    assert fd.data_ptr() % 16 == 0
+    idx.fill_(SENTINEL)
+    _, cnt = ssc.select_flags(fd, out=idx)
+    assert int(host(cnt)[0]) == m
+    assert checks.first_mismatch(host(idx)[:m], wi) == -1
+    del fd, wi
+    # exclusive scan (the persistent kernel, 69,906 tiles), wrapping sums
+    sw, total = oracle.exclusive_scan_i32(x)
+    _, tot = ssc.exclusive_scan(xd, out=out)
+    assert int(host(tot)[0]) == total
+    assert checks.first_mismatch(host(out), sw) == -1
 
 
 @pytest.mark.parametrize("keep", wl.SWEEP_KEEP)
