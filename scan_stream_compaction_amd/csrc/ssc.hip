@@ -1924,7 +1924,7 @@ __global__ __launch_bounds__(kBlock) void bit_clear_count_kernel(const uint32_t 
 // done as three steps over tiles of 8192 keys (one 512-thread workgroup, 16
 // keys per lane):
 //   digit_count_kernel: cnt[d * tiles + t] = keys of tile t with digit d;
-//   one exclusive scan of that digit-major table (scan_kernel) turns it
+//   one exclusive scan of that digit-major table (scan_impl) turns it
 //     into off[d * tiles + t] = number of keys that precede, in the output,
 //     the first digit-d key of tile t (all keys of smaller digits, plus the
 //     digit-d keys of earlier tiles);
