@@ -123,7 +123,7 @@ def test_flag_bytes_full_size():
 # second and third tiles are claimed together from 768 tiles).
 TS = 15 * 8192
 SEL_FLAG_N = [8191, 8192, 8193, 8195, 16 * 1024 + 7, TS - 1, TS, TS + 1, TS + 3, 3 * TS + 611,
-              257 * TS + 13, 800 * TS + 5]
+              256 * TS, 256 * TS + 1, 257 * TS + 13, 767 * TS + 9, 768 * TS, 800 * TS + 5]
 
 
 @pytest.mark.parametrize("n", SEL_FLAG_N)

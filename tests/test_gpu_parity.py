@@ -578,12 +578,12 @@ def test_scan_i32_wraps_and_in_place():
     assert int(host(tot)[0]) == total
 
 
-# Tile counts that take each scan launch: at most one tile per compute unit
-# (persistent, one tile each), one to two (one workgroup per tile), two to
-# three (persistent, later tiles claimed one at a time) and three or more
-# (persistent, second and third tiles claimed together). MI355X has 256
-# compute units.
-SCAN_TILE_COUNTS = [33, 326, 700, 1500]
+# Tile counts that take each scan launch, and the counts on both sides of
+# each switch: at most one tile per compute unit (persistent, one tile each),
+# one to two (one workgroup per tile), two to three (persistent, later tiles
+# claimed one at a time) and three or more (persistent, second and third
+# tiles claimed together). MI355X has 256 compute units.
+SCAN_TILE_COUNTS = [33, 256, 257, 326, 512, 513, 700, 767, 768, 1500]
 
 
 @pytest.mark.parametrize("tiles", SCAN_TILE_COUNTS)
