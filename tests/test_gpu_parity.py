@@ -611,6 +611,21 @@ def test_scan_paths_by_tile_count(tiles):
     check_scan_f32(wl.unit_float32(0x5CAF + tiles, n))
 
 
+@pytest.mark.parametrize("tiles", [256, 257, 767, 768])
+def test_compaction_paths_by_tile_count(tiles):
+    """The persistent compaction kernel on both sides of its switches: one
+    tile per workgroup or more, and the second and third tiles claimed one at
+    a time (below three per workgroup) or together. Compaction with ranks,
+    partition and selection, with a ragged last tile."""
+    n = (tiles - 1) * T + 611
+    x = wl.full_int32(0xC0A7 + tiles, n)
+    xd = dev(x)
+    check_compact(x, "odd", xd=xd)
+    check_compact(x, "mod_lt", 100, 50, xd=xd, ranks=False)
+    check_partition(x, "even", xd=xd)
+    check_select_index(x, "mod_lt", 100, 1, xd=xd)
+
+
 def test_repeated_runs_are_identical():
     """The look-back must give the same answer whatever order tiles finish in:
     100 compactions and 100 scans of 1,500 tiles (several per workgroup, every
