@@ -1492,10 +1492,12 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 // compute unit loops over tiles of 30720 values claimed three ahead, each data
 // wavefront holding three chunks of 2048 values (eight 128-bit loads per
 // lane) in registers. Per tile it
-//   1. issues the loads of the tile after next into the chunk written last;
-//   2. sums the next tile's chunk once it has landed and arrives with the
+//   1. sums the next tile's chunk once it has landed and arrives with the
 //      total; the last of the 15 to arrive scans the chunk totals and
 //      publishes the next tile's {aggregate} at once;
+//   2. issues the loads of the tile after next into the chunk written last
+//      (issued after the next tile's have landed, not before: fewer reads
+//      waiting, 2^28 371.4 -> 367.4 us, fp32 377.4 -> 374.8);
 //   3. waits at the tile's barrier for its base from the control wavefront;
 //   4. scans the current chunk load by load (per load a DPP wavefront scan of
 //      the lanes' 4-value sums) and stores base + chunk prefix + the value's
@@ -1739,9 +1741,10 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     {                                                                                        \
         int ln = lane;                                                                       \
         asm volatile("" : "+v"(ln));                                                         \
-        load(nxt2, ln, FREE);                                                                \
         const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                    \
-        arrive(chunk_sum(NX), nxt, tri_n, ln);                                          \
+        arrive(chunk_sum(NX), nxt, tri_n, ln);                                               \
+        /* the tile after next's loads leave once the next tile's have landed */             \
+        load(nxt2, ln, FREE);                                                                \
         __syncthreads(); /* B1: this tile's base is known */                                 \
         const uint32_t nxt3 = uniform(s_next[par]);                                          \
         write(CUR, tile, par, tri, ln);                                                      \
