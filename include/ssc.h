@@ -238,8 +238,8 @@ int ssc_compact_flags_b32(const void *in, const uint8_t *flags, void *out, int64
 /* Positions of the nonzero flag bytes: idx[0 .. count) = the i, increasing,
  * with flags[i] != 0; *count = their number (the flag-byte form of
  * ssc_select_index_i32; same alignment rule for flags). A 16-byte aligned
- * flag array is read in 128-bit words by a kernel with 122,880-flag tiles
- * (faster: each tile carries four times the bytes per look-back); it too
+ * flag array is read in 128-bit words by a kernel with 61,440-flag tiles
+ * (faster: each tile carries twice the bytes per look-back); it too
  * reads nothing past the 32-bit word that holds flags[n - 1]. No overlap
  * between flags, idx and count is allowed. Source: as ssc_compact_flags_b32. */
 int ssc_select_flags(const uint8_t *flags, int32_t *idx, int64_t n, int32_t *count,

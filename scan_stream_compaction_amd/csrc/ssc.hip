@@ -1116,19 +1116,27 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 
 // ================================================== flag-byte selection ---
 // Selection by flag bytes (idx[k] = position of the k-th nonzero flag) with
-// tiles four times the compaction kernel's. A flag is one byte, so a
-// 30720-flag tile is too little data to hide the look-back and the barrier
-// each tile costs. Here each data lane loads eight 128-bit words of flags
-// (8192 per data wavefront, 122,880 per tile) and turns them into four
-// 32-bit masks as soon as they land. The bytes are then dead, so two raw
-// register sets keep two tiles of loads in flight. After the tile's barrier a
-// wavefront writes its survivors' positions in four rounds of two loads
-// (2048 flags each), every round staged in its 8 KiB LDS region and streamed
-// out as one run. The claims, arrivals, look-back and control wavefront are
-// the compaction kernel's. The flag array must be 16-byte aligned.
-constexpr int kFlagLoads = 8;                                     // 128-bit loads per lane
-constexpr int kFlagChunk = kWave * 16 * kFlagLoads;               // 8192 flags per data wavefront
-constexpr int64_t kFlagTile = static_cast<int64_t>(kDataWaves) * kFlagChunk;  // 122,880
+// tiles twice the compaction kernel's. A flag is one byte, so a 30720-flag
+// tile is too little data to hide the look-back and the barrier each tile
+// costs. Here each data lane loads four 128-bit words of flags (4096 per data
+// wavefront, 61,440 per tile) and turns them into two 32-bit masks as soon
+// as they land. The bytes are then dead, so two raw register sets keep two
+// tiles of loads in flight. After the tile's barrier a wavefront writes its
+// survivors' positions in two rounds of two loads (2048 flags each), every
+// round staged in its 8 KiB LDS region and streamed out as one run. The
+// claims, arrivals, look-back and control wavefront are the compaction
+// kernel's. The flag array must be 16-byte aligned.
+//
+// Tile size, 2^28 flags, 50% kept (us per launch): 30,720 flags 158.4,
+// 61,440 143.7, 92,160 151.3, 122,880 155.4. Larger tiles cost fewer
+// look-backs, but each tile's look-back then waits longer on predecessors
+// whose workgroups have fallen behind: at 122,880 flags a tile took 10-20 us,
+// and in one tile of six the look-back polled its predecessor more than six
+// times (90th percentile 11.5 us).
+constexpr int kFlagLoads = 4;                                     // 128-bit loads per lane
+constexpr int kFlagMasks = kFlagLoads / 2;                        // 32-bit masks per lane
+constexpr int kFlagChunk = kWave * 16 * kFlagLoads;               // 4096 flags per data wavefront
+constexpr int64_t kFlagTile = static_cast<int64_t>(kDataWaves) * kFlagChunk;  // 61,440
 
 // The nonzero bytes of a 32-bit word as a 4-bit mask (bit i = byte i). Bit 7
 // of each byte of ((w & 0x7F7F7F7F) + 0x7F7F7F7F) | w is set iff that byte
@@ -1149,7 +1157,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     __shared__ uint32_t s_pre[3][kDataWaves + 1];  // chunk prefixes + aggregate, by tile mod 3
     __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
     __shared__ uint32_t s_first[3], s_epoch, s_arrive;
-    static_assert(kFlagChunk / 4 == kStageWords, "a round of two loads fills one staging region");
+    static_assert(kWave * 16 * 2 == kStageWords, "a round of two loads fills one staging region");
 
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
@@ -1214,7 +1222,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     const auto rem_of = [&](uint32_t t) {
         return t < num_tiles ? chunk_rem<kFlagChunk>(n, chunk_of(t)) : 0u;
     };
-    // Eight 128-bit words of flags per lane: byte b of load j is flag
+    // Four 128-bit words of flags per lane: byte b of load j is flag
     // chunk + j*1024 + lane*16 + b. The resource covers the valid flags
     // rounded up to whole dwords (the dword holding the last flag is read
     // whole: 4-byte aligned, it never crosses a page); the rest read as 0.
@@ -1226,10 +1234,10 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     };
     // m[q] = the flags of loads 2q (bits 0-15) and 2q+1 (bits 16-31), those
     // past rem cleared. Returns the chunk's total.
-    const auto masks = [&](const u32x4(&v)[kFlagLoads], uint32_t rem, int ln, uint32_t(&m)[4]) {
+    const auto masks = [&](const u32x4(&v)[kFlagLoads], uint32_t rem, int ln, uint32_t(&m)[kFlagMasks]) {
         uint32_t tot = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kFlagMasks; ++q) {
             uint32_t x = 0;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -1273,14 +1281,14 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             }
         }
     };
-    // The survivors' positions of the current chunk, in four rounds of two
+    // The survivors' positions of the current chunk, in two rounds of two
     // loads: ranks by one packed DPP scan of the two loads' counts (16-bit
     // fields: at most 1024 each), positions staged at their ranks, then one
     // run to idx[seg + done ..).
-    const auto write = [&](const uint32_t(&m)[4], int64_t chunk, uint32_t seg, int ln) {
+    const auto write = [&](const uint32_t(&m)[kFlagMasks], int64_t chunk, uint32_t seg, int ln) {
         uint32_t done = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kFlagMasks; ++q) {
             const uint32_t mq = m[q];
             const uint32_t c = static_cast<uint32_t>(__builtin_popcount(mq & 0xFFFFu)) |
                                (static_cast<uint32_t>(__builtin_popcount(mq >> 16)) << 16);
@@ -1308,7 +1316,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     };
 
     u32x4 ra[kFlagLoads], rb[kFlagLoads];  // raw flags of the two tiles in flight
-    uint32_t mc[4], mn[4];                 // masks of the current and the next tile
+    uint32_t mc[kFlagMasks], mn[kFlagMasks];  // masks of the current and the next tile
 
     // One tile: X holds the next tile's flags, Y the tile after next's (in
     // flight); once X's masks are taken, X takes the loads of the tile the
@@ -1323,7 +1331,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         const uint32_t nxt3 = uniform(s_next[par]);                                           \
         load(nxt3, ln, X);                                                                    \
         write(mc, chunk_of(tile), uniform(s_base[par]) + uniform(s_pre[tri][w]), ln);         \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) mc[q] = mn[q];                          \
+        _Pragma("unroll") for (int q = 0; q < kFlagMasks; ++q) mc[q] = mn[q];                          \
         tile = nxt;                                                                           \
         nxt = nxt2;                                                                           \
         nxt2 = nxt3;                                                                          \

@@ -117,13 +117,16 @@ def test_flag_bytes_full_size():
 
 
 # Selection by flag bytes from a 16-byte aligned array takes its own kernel:
-# 8192 flags per data wavefront (eight 128-bit loads per lane), 122,880 per
-# tile. Sizes around its chunk and tile, byte counts that end inside a dword,
-# and tile counts on both sides of the claim paths (256 compute units; the
-# second and third tiles are claimed together from 768 tiles).
-TS = 15 * 8192
-SEL_FLAG_N = [8191, 8192, 8193, 8195, 16 * 1024 + 7, TS - 1, TS, TS + 1, TS + 3, 3 * TS + 611,
-              256 * TS, 256 * TS + 1, 257 * TS + 13, 767 * TS + 9, 768 * TS, 800 * TS + 5]
+# 4096 flags per data wavefront (four 128-bit loads per lane), 61,440 per
+# tile, written in rounds of 2048. Sizes around a round, its chunk and tile,
+# byte counts that end inside a dword, and tile counts on both sides of the
+# claim paths (256 compute units; the second and third tiles are claimed
+# together from 768 tiles).
+CH = 4096
+TS = 15 * CH
+SEL_FLAG_N = [2047, 2048, 2049, CH - 1, CH, CH + 1, CH + 3, 2 * CH + 7, TS - 1, TS, TS + 1, TS + 3,
+              3 * TS + 611, 256 * TS, 256 * TS + 1, 257 * TS + 13, 767 * TS + 9, 768 * TS,
+              800 * TS + 5]
 
 
 @pytest.mark.parametrize("n", SEL_FLAG_N)
