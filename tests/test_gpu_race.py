@@ -101,6 +101,20 @@ def test_scans_under_perturbation(perturbed, tiles):
     assert not ssc.timed_out(scratch)
 
 
+def test_flag_selection_claim_paths_under_perturbation(perturbed):
+    """Selection by flag bytes at 800 of its 61,440-flag tiles: the second and
+    third tiles come from one claim (768 tiles or more on 256 compute units)."""
+    n = 800 * 61440 + 5
+    f = wl.flag_bytes(0x7AC5, n, 37)
+    fw, mf = oracle.select_flags(f)
+    fd = dev(f)
+    scratch = ssc.new_scratch(n, fd.device)
+    for rep in range(2):
+        fidx, fcnt = ssc.select_flags(fd, scratch=scratch)
+        assert int(host(fcnt)[0]) == mf and checks.first_mismatch(host(fidx)[:mf], fw) == -1, rep
+    assert not ssc.timed_out(scratch)
+
+
 def test_radix_sort_under_perturbation(perturbed):
     keys = wl.full_uint32(0x5EED7, 1 << 20)
     got = ssc.radix_sort4(dev(keys.view(np.int32)))
