@@ -59,7 +59,7 @@ extern "C" {
 typedef enum ssc_status {
     SSC_OK = 0,
     SSC_ERR_ARG = 1,     /* null pointer, n < 0, bad predicate or predicate argument, misalignment */
-    SSC_ERR_SIZE = 2,    /* n > INT32_MAX */
+    SSC_ERR_SIZE = 2,    /* n > INT32_MAX (the small-tile test build: n > 2^17 x 3840) */
     SSC_ERR_ALIAS = 3,   /* buffers overlap where they must not */
     SSC_ERR_SCRATCH = 4, /* scratch too small or not 8-byte aligned */
     SSC_ERR_HIP = 5,     /* a HIP call or kernel launch failed */
@@ -97,7 +97,9 @@ typedef enum ssc_pred {
 
 /* Elements per tile: the share of the single pass behind one tile number
  * claimed from the atomic counter and one look-back descriptor (a workgroup
- * of the compaction kernel processes several tiles in turn). */
+ * of the compaction kernel processes several tiles in turn). 30720; 3840 in
+ * the library's small-tile test build (libssc_stress.so), which otherwise
+ * has the same calls and results. */
 int64_t ssc_tile_elems(void);
 
 /* Scratch bytes needed by the scan, compaction, partition and counting calls

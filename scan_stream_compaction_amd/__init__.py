@@ -20,6 +20,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssc.so")
 PERTURB_LIB_PATH = os.path.join(_PKG, "libssc_perturb.so")  # race-test build
+STRESS_LIB_PATH = os.path.join(_PKG, "libssc_stress.so")    # race-test build, 3840-element tiles
 
 PRED = {"nonzero": 0, "odd": 1, "even": 2, "bit_set": 3, "bit_clear": 4, "mod_lt": 5,
         "f32_nonzero": 6, "f32_gt": 7, "f32_lt": 8, "f32_in": 9}

@@ -1,11 +1,15 @@
 """Build libssc.so (HIP, gfx950) in-tree with hipcc.
 
-Also builds libssc_perturb.so, the same sources with -DSSC_PERTURB: every
-tile claim, descriptor publication, arrival and look-back poll pauses for a
-hashed number of clocks, so the race tests see tiles finish in other orders.
-The library proper never contains that code.
+Also builds two test builds of the same sources for the race tests:
+- libssc_perturb.so (-DSSC_PERTURB): every tile claim, descriptor
+  publication, arrival and look-back poll pauses for a hashed number of
+  clocks, so tiles finish in other orders;
+- libssc_stress.so (-DSSC_STRESS_TILES): the persistent kernels' tiles are
+  eight times smaller, so a call makes eight times the claims, descriptors
+  and look-backs.
+The library proper contains neither.
 
-Usage: python -m scan_stream_compaction_amd.build [--asm DIR] [--only lib|perturb]
+Usage: python -m scan_stream_compaction_amd.build [--asm DIR] [--only lib|perturb|stress]
 """
 from __future__ import annotations
 
@@ -20,6 +24,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "ssc.hip")
 LIB = os.path.join(PKG, "libssc.so")
 PERTURB_LIB = os.path.join(PKG, "libssc_perturb.so")
+STRESS_LIB = os.path.join(PKG, "libssc_stress.so")
+
 ARCH = "gfx950"
 
 
@@ -40,8 +46,8 @@ def flags() -> list[str]:
     ]
 
 
-def _command(out: str, perturb: bool, asm_dir: str | None) -> tuple[list[str], str]:
-    cmd = [hipcc(), *flags(), *(["-DSSC_PERTURB=1"] if perturb else []), "-shared", SRC, "-o", out]
+def _command(out: str, defines: list[str], asm_dir: str | None) -> tuple[list[str], str]:
+    cmd = [hipcc(), *flags(), *defines, "-shared", SRC, "-o", out]
     cwd = ROOT
     if asm_dir:
         # intermediate files (device ISA included) go next to the output
@@ -52,13 +58,14 @@ def _command(out: str, perturb: bool, asm_dir: str | None) -> tuple[list[str], s
 
 
 def build(asm_dir: str | None = None, only: str | None = None) -> list[str]:
-    """Compile the library (and, unless only == "lib", the perturbed test
-    build) in parallel; each output is replaced only once it is complete."""
+    """Compile the library and the two test builds (or only the one named)
+    in parallel; each output is replaced only once it is complete."""
     jobs = []
-    for name, out, perturb in (("lib", LIB, False), ("perturb", PERTURB_LIB, True)):
+    for name, out, defines in (("lib", LIB, []), ("perturb", PERTURB_LIB, ["-DSSC_PERTURB=1"]),
+                               ("stress", STRESS_LIB, ["-DSSC_STRESS_TILES=1"])):
         if only and only != name:
             continue
-        cmd, cwd = _command(out + ".tmp", perturb, asm_dir if name == "lib" else None)
+        cmd, cwd = _command(out + ".tmp", defines, asm_dir if name == "lib" else None)
         jobs.append((out, subprocess.Popen(cmd, cwd=cwd)))
     failed = [out for out, p in jobs if p.wait() != 0]
     if failed:
@@ -71,7 +78,7 @@ def build(asm_dir: str | None = None, only: str | None = None) -> list[str]:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--asm", default=None, help="keep intermediate files (ISA) of libssc.so in this directory")
-    ap.add_argument("--only", choices=("lib", "perturb"), default=None)
+    ap.add_argument("--only", choices=("lib", "perturb", "stress"), default=None)
     a = ap.parse_args()
     print("\n".join(build(a.asm, a.only)))
     sys.exit(0)

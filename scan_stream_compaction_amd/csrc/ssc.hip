@@ -66,6 +66,17 @@ constexpr int kLbRounds = 2;                   // chunks per data wavefront per 
 constexpr int kLbSub = kDataWaves * kChunk;    // 15360 elements per round
 constexpr int kTile = kLbSub * kLbRounds;      // 30720 elements per tile
 constexpr uint32_t kMaxTiles = 1u << 18;       // power of two >= descriptor words of the largest n
+// 128-bit loads per lane of the persistent kernels' 32-bit chunks (2048
+// elements per data wavefront, a 30720-element tile). A build with
+// SSC_STRESS_TILES defined takes one (3840-element tiles: eight times the
+// tiles, claims and look-backs per call) to stress the descriptor protocol in
+// the tests; it accepts n up to 2^17 tiles and is no faster.
+#ifdef SSC_STRESS_TILES
+constexpr int kTileLoads = 1;
+#else
+constexpr int kTileLoads = 8;
+#endif
+constexpr int kSelTile = kDataWaves * kWave * kTileLoads * 4;  // elements per compaction tile
 // Workgroups of the grid-stride counting kernels: one per compute unit. The
 // memory system delivers more with fewer reads waiting (2^28 int32, count of
 // the even elements: 1024 / 512 / 256 / 128 workgroups 197 / 176 / 167 /
@@ -75,8 +86,12 @@ constexpr int kReduceGrid = 256;
 constexpr int kSpread = 16;                    // accumulators a counting pass spreads over
 
 static_assert(kLbBlock == (kDataWaves + 1) * kWave, "one control wavefront");
-// two words per tile for the wide descriptors of the fp32 scans
-static_assert(static_cast<int64_t>(kMaxTiles) * kTile >= 2LL * 2147483647LL, "kMaxTiles");
+// two words per compaction tile: the wide descriptors of the fp32 scans, and
+// the tiles of half the size of the key-value and 64-bit formats
+static_assert(kTile % kSelTile == 0, "compaction tiles divide the scan tile");
+#ifndef SSC_STRESS_TILES
+static_assert(static_cast<int64_t>(kMaxTiles) * kSelTile >= 2LL * 2147483647LL, "kMaxTiles");
+#endif
 
 // Scratch header (bytes). Descriptors follow it, one 64-bit word per tile.
 constexpr size_t kHeaderBytes = 512;
@@ -89,6 +104,8 @@ constexpr size_t kOffAcc32 = 128;    // uint32[32] per-bit clear counts being su
 constexpr size_t kOffKept32 = 256;   // uint32[32] per-bit clear counts of the current sort
 
 __host__ __device__ constexpr int64_t tiles_for(int64_t n) { return (n + kTile - 1) / kTile; }
+// Descriptor words for n elements: two per compaction tile.
+__host__ __device__ constexpr int64_t desc_words(int64_t n) { return 2 * ((n + kSelTile - 1) / kSelTile); }
 
 // Four 32-bit lanes moved by one 128-bit global load or store.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -643,18 +660,19 @@ struct SelArgs {
 // Eight 128-bit loads per lane: 2048 elements per data wavefront.
 template <bool VEC>
 struct FmtB32 {
-    using Shape = ChunkShape<8, 4>;
+    using Shape = ChunkShape<kTileLoads, 4>;
+    static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;  // element values are loaded
     struct Regs {
-        int32_t v[8][4];
+        int32_t v[L][4];
     };
     __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
-        load_b32x4<8, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.v);
+        load_b32x4<L, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.v);
     }
     template <int P>
     __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &pr) {
-        return mask_b32<P, 8>(r.v, lane, rem, pr);
+        return mask_b32<P, L>(r.v, lane, rem, pr);
     }
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
         region[slot] = static_cast<uint32_t>(r.v[j][k]);
@@ -673,31 +691,32 @@ struct FmtB32 {
 // holds the last flag is read whole (never anything past that word).
 template <bool VEC, bool VALUES>
 struct FmtFlags {
-    using Shape = ChunkShape<8, 4>;
+    using Shape = ChunkShape<kTileLoads, 4>;
+    static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = VALUES;
     struct Regs {
-        int32_t v[8][4];
-        uint32_t f[8];
+        int32_t v[L][4];
+        uint32_t f[L];
     };
     __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
         if constexpr (VALUES)
-            load_b32x4<8, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.v);
+            load_b32x4<L, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.v);
         const __amdgpu_buffer_rsrc_t fr =
             buffer_rsrc(static_cast<const uint8_t *>(a.aux) + chunk, (rem + 3u) & ~3u);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < L; ++j)
             r.f[j] = __builtin_amdgcn_raw_buffer_load_b32(fr, j * (kWave * 4) + lane * 4, 0, kNT);
     }
     template <int P>
     __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &) {
         uint32_t mask = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < L; ++j)
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 mask |= static_cast<uint32_t>(((r.f[j] >> (8 * k)) & 0xFFu) != 0u) << (j * 4 + k);
-        if (rem < static_cast<uint32_t>(Shape::kChunk)) mask &= valid_mask<8, 4>(lane, rem);
+        if (rem < static_cast<uint32_t>(Shape::kChunk)) mask &= valid_mask<L, 4>(lane, rem);
         return mask;
     }
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
@@ -716,20 +735,21 @@ struct FmtFlags {
 // values in the second.
 template <bool VEC>
 struct FmtPairs {
-    using Shape = ChunkShape<4, 4>;
+    using Shape = ChunkShape<(kTileLoads + 1) / 2, 4>;
+    static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;
     struct Regs {
-        int32_t k[4][4];
-        int32_t v[4][4];
+        int32_t k[L][4];
+        int32_t v[L][4];
     };
     __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
-        load_b32x4<4, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.k);
-        load_b32x4<4, VEC>(static_cast<const int32_t *>(a.aux), chunk, rem, lane, r.v);
+        load_b32x4<L, VEC>(static_cast<const int32_t *>(a.in), chunk, rem, lane, r.k);
+        load_b32x4<L, VEC>(static_cast<const int32_t *>(a.aux), chunk, rem, lane, r.v);
     }
     template <int P>
     __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &pr) {
-        return mask_b32<P, 4>(r.k, lane, rem, pr);
+        return mask_b32<P, L>(r.k, lane, rem, pr);
     }
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
         region[slot] = static_cast<uint32_t>(r.k[j][k]);
@@ -766,17 +786,18 @@ __device__ __forceinline__ bool pred_eval64(uint64_t u, const PredArgs &pr) {
 // elements per data wavefront (8-byte aligned arrays take 64-bit loads).
 template <bool VEC>
 struct FmtB64 {
-    using Shape = ChunkShape<8, 2>;
+    using Shape = ChunkShape<kTileLoads, 2>;
+    static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;
     struct Regs {
-        uint64_t v[8][2];
+        uint64_t v[L][2];
     };
     __device__ static void load(const SelArgs &a, int64_t chunk, uint32_t rem, int lane, Regs &r) {
         const __amdgpu_buffer_rsrc_t rs =
             buffer_rsrc(static_cast<const uint64_t *>(a.in) + chunk, rem * 8u);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < L; ++j) {
             const int off = j * (kWave * 16) + lane * 16;
             if constexpr (VEC) {
                 const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNT);
@@ -795,11 +816,11 @@ struct FmtB64 {
     __device__ static uint32_t flags(const Regs &r, int lane, uint32_t rem, const PredArgs &pr) {
         uint32_t mask = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < L; ++j)
 #pragma unroll
             for (int k = 0; k < 2; ++k)
                 mask |= static_cast<uint32_t>(pred_eval64<P>(r.v[j][k], pr)) << (j * 2 + k);
-        if (rem < static_cast<uint32_t>(Shape::kChunk)) mask &= valid_mask<8, 2>(lane, rem);
+        if (rem < static_cast<uint32_t>(Shape::kChunk)) mask &= valid_mask<L, 2>(lane, rem);
         return mask;
     }
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
@@ -1133,10 +1154,11 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 // whose workgroups have fallen behind: at 122,880 flags a tile took 10-20 us,
 // and in one tile of six the look-back polled its predecessor more than six
 // times (90th percentile 11.5 us).
-constexpr int kFlagLoads = 4;                                     // 128-bit loads per lane
+constexpr int kFlagLoads = kTileLoads == 8 ? 4 : 2;              // 128-bit loads per lane
 constexpr int kFlagMasks = kFlagLoads / 2;                        // 32-bit masks per lane
 constexpr int kFlagChunk = kWave * 16 * kFlagLoads;               // 4096 flags per data wavefront
 constexpr int64_t kFlagTile = static_cast<int64_t>(kDataWaves) * kFlagChunk;  // 61,440
+static_assert(kFlagTile >= kSelTile, "at most one descriptor per compaction tile");
 
 // The nonzero bytes of a 32-bit word as a 4-bit mask (bit i = byte i). Bit 7
 // of each byte of ((w & 0x7F7F7F7F) + 0x7F7F7F7F) | w is set iff that byte
@@ -1527,8 +1549,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     const typename Op::T *in, typename Op::T *out, int64_t n, void *scratch, uint32_t num_tiles,
     uint32_t capacity, typename Op::T *total) {
     using T = typename Op::T;
-    using S = ChunkShape<8, 4>;
-    static_assert(S::kTileElems == kTile, "one descriptor per kTile values");
+    using S = ChunkShape<kTileLoads, 4>;
+    static_assert(S::kTileElems == kSelTile, "the compaction kernel's tile");
     static_assert(!WIDE || sizeof(T) == 4, "wide carries are for fp32 values");
     __shared__ uint32_t s_tot[kDataWaves];
     __shared__ uint32_t s_pre[3][kDataWaves + 1];  // chunk prefixes + aggregate, by tile mod 3
@@ -1614,7 +1636,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
 
     uint32_t va[S::kLoads][4], vb[S::kLoads][4], vc[S::kLoads][4];
     const auto chunk_of = [&](uint32_t t) {
-        return static_cast<int64_t>(t) * kTile + static_cast<int64_t>(w) * S::kChunk;
+        return static_cast<int64_t>(t) * S::kTileElems + static_cast<int64_t>(w) * S::kChunk;
     };
     const auto rem_of = [&](uint32_t t) {
         return t < num_tiles ? chunk_rem<S::kChunk>(n, chunk_of(t)) : 0u;
@@ -2321,7 +2343,7 @@ __global__ __launch_bounds__(kBlock) void clear_kernel(uint32_t *__restrict__ p,
 // this name stands for the symbol only: its device address comes from
 // hipGetSymbolAddress (noalloc_scratch below), once per device.
 constexpr size_t kNoAllocScratchBytes =
-    (ssc::kHeaderBytes + static_cast<size_t>(ssc::tiles_for(INT32_MAX)) * 2 * sizeof(uint64_t) + 255) &
+    (ssc::kHeaderBytes + static_cast<size_t>(ssc::desc_words(INT32_MAX)) * sizeof(uint64_t) + 255) &
     ~static_cast<size_t>(255);
 static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
@@ -2433,14 +2455,15 @@ PredArgs make_pred_args(int pred, int32_t pa, int32_t pb) {
 int check_n(int64_t n) {
     if (n < 0) return SSC_ERR_ARG;
     if (n > INT32_MAX) return SSC_ERR_SIZE;
+    // only the stress build's small tiles can need more descriptor words
+    if (desc_words(n) > static_cast<int64_t>(kMaxTiles)) return SSC_ERR_SIZE;
     return SSC_OK;
 }
 
 // Header plus two 64-bit descriptor words per tile (the fp32 scans' wide
 // descriptors; the other kernels use the first half of the array).
 size_t scratch_need(int64_t n) {
-    const int64_t t = n > 0 ? tiles_for(n) : 0;
-    return kHeaderBytes + static_cast<size_t>(t) * 2 * sizeof(uint64_t);
+    return kHeaderBytes + static_cast<size_t>(n > 0 ? desc_words(n) : 0) * sizeof(uint64_t);
 }
 
 int check_scratch(const void *scratch, size_t bytes, size_t need) {
@@ -2710,13 +2733,16 @@ int scan_impl(const typename Op::T *in, typename Op::T *out, int64_t n, typename
                                out, n, scratch, tiles, cap, total);
         return launched();
     }
-    const dim3 grid(tiles < slots ? tiles : slots);  // persistent: one workgroup per compute unit
+    // persistent: one workgroup per compute unit, tiles of the compaction
+    // kernel's size (the same as kTile but in the stress build)
+    const uint32_t ptiles = static_cast<uint32_t>((n + kSelTile - 1) / kSelTile);
+    const dim3 grid(ptiles < slots ? ptiles : slots);
     if (vec)
         hipLaunchKernelGGL((scan_persistent_kernel<Op, true, INCL, kWide>), grid, dim3(kLbBlock), 0, s, in,
-                           out, n, scratch, tiles, cap, total);
+                           out, n, scratch, ptiles, cap, total);
     else
         hipLaunchKernelGGL((scan_persistent_kernel<Op, false, INCL, kWide>), grid, dim3(kLbBlock), 0, s, in,
-                           out, n, scratch, tiles, cap, total);
+                           out, n, scratch, ptiles, cap, total);
     return launched();
 }
 
@@ -2980,7 +3006,7 @@ int noalloc_scratch(void **ptr, hipStream_t s) {
 // ======================================================================
 extern "C" {
 
-int64_t ssc_tile_elems(void) { return kTile; }
+int64_t ssc_tile_elems(void) { return kSelTile; }
 
 size_t ssc_scratch_bytes(int64_t n) { return scratch_need(n < 0 ? 0 : n); }
 
@@ -3364,7 +3390,11 @@ const char *ssc_status_str(int status) {
     switch (status) {
     case SSC_OK: return "ok";
     case SSC_ERR_ARG: return "invalid argument";
+#ifdef SSC_STRESS_TILES
+    case SSC_ERR_SIZE: return "n exceeds 2^17 tiles of 3840 elements (the small-tile test build's limit)";
+#else
     case SSC_ERR_SIZE: return "n exceeds INT32_MAX";
+#endif
     case SSC_ERR_ALIAS: return "buffers overlap";
     case SSC_ERR_SCRATCH: return "scratch too small or misaligned";
     case SSC_ERR_HIP: return "HIP error";

@@ -51,6 +51,27 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+@pytest.mark.parametrize("path", [ssc.PERTURB_LIB_PATH, ssc.STRESS_LIB_PATH])
+def test_test_builds_export_every_symbol_and_size_their_scratch(path):
+    """The race tests' builds: the same C ABI; the stress build's tiles are
+    3840 elements, so its scratch holds 16 bytes of descriptors per 3840
+    elements and it refuses n beyond 2^17 of its tiles."""
+    if not os.path.exists(path):
+        pytest.skip(f"{os.path.basename(path)} not built (python -m scan_stream_compaction_amd.build)")
+    L = ssc.load_library(path)
+    for name in _declared():
+        assert hasattr(L, name), name
+    stress = path == ssc.STRESS_LIB_PATH
+    T = L.ssc_tile_elems()
+    assert T == (3840 if stress else 30720)
+    for n in (1, T, T + 1, 2**28):
+        assert L.ssc_scratch_bytes(n) == 512 + 16 * ((n + T - 1) // T)
+    big = (1 << 17) * 3840 + 1
+    rc = L.ssc_compact_i32(None, None, big, 1, 0, 0, None, None, None, 0, None)
+    code = {v: k for k, v in ssc.STATUS.items()}
+    assert rc == (code["SSC_ERR_SIZE"] if stress else code["SSC_ERR_ARG"])
+
+
 def test_enum_numbering_agrees_with_oracle_and_binding():
     preds = _enum("ssc_pred")
     assert preds == {"SSC_PRED_NONZERO": 0, "SSC_PRED_ODD": 1, "SSC_PRED_EVEN": 2,

@@ -1,11 +1,16 @@
-"""Parity under perturbed timing: the same calls through libssc_perturb.so.
+"""Parity under stress: the same calls through the library's two test builds.
 
-That build (the library's sources compiled with -DSSC_PERTURB) pauses every
-tile claim, descriptor publication, data-wavefront arrival and look-back poll
-for 0 to 7 x 1024 clocks chosen by a hash of the tile, workgroup or poll
-count, so workgroups claim, publish and finish in orders the library proper
-rarely shows. Every result must still match the oracle exactly (fp32 scans
-within 1e-5), repeated calls must agree, and no look-back wait may give up.
+- libssc_perturb.so (the sources compiled with -DSSC_PERTURB) pauses every
+  tile claim, descriptor publication, data-wavefront arrival and look-back
+  poll for 0 to 7 x 1024 clocks chosen by a hash of the tile, workgroup or
+  poll count, so workgroups claim, publish and finish in orders the library
+  proper rarely shows.
+- libssc_stress.so (-DSSC_STRESS_TILES) gives the persistent kernels tiles
+  eight times smaller (3840 elements), so every call makes eight times the
+  claims, descriptors and look-backs, and look-backs walk longer windows.
+
+Every result must still match the oracle exactly (fp32 scans within 1e-5),
+repeated calls must agree, and no look-back wait may give up.
 """
 from __future__ import annotations
 
@@ -20,11 +25,7 @@ import scan_stream_compaction_amd as ssc
 from scan_stream_compaction_amd import workloads as wl
 from tests import checks
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skipif(not os.path.exists(ssc.PERTURB_LIB_PATH),
-                       reason="libssc_perturb.so not built (python -m scan_stream_compaction_amd.build)"),
-]
+pytestmark = [pytest.mark.gpu]
 
 T = 30720
 SENTINEL = -123456789
@@ -39,10 +40,25 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-@pytest.fixture(scope="module")
-def perturbed():
-    with ssc.using_library(ssc.PERTURB_LIB_PATH) as L:
+@pytest.fixture(scope="module", params=[ssc.PERTURB_LIB_PATH, ssc.STRESS_LIB_PATH],
+                ids=["perturbed", "small_tiles"])
+def perturbed(request):
+    if not os.path.exists(request.param):
+        pytest.skip(f"{os.path.basename(request.param)} not built (python -m scan_stream_compaction_amd.build)")
+    with ssc.using_library(request.param) as L:
         yield L
+
+
+def test_stress_build_has_small_tiles():
+    if not os.path.exists(ssc.STRESS_LIB_PATH):
+        pytest.skip("libssc_stress.so not built")
+    with ssc.using_library(ssc.STRESS_LIB_PATH):
+        assert ssc.tile_elems() == 3840
+        n = 5 * 3840 + 17
+        x = wl.full_int32(0x7AC6, n)
+        want, m = oracle.compact_i32(x, oracle.PRED_ODD, 0, 0)
+        out, cnt = ssc.compact(dev(x), "odd")
+        assert int(host(cnt)[0]) == m and checks.first_mismatch(host(out)[:m], want) == -1
 
 
 @pytest.mark.parametrize("tiles", [33, 700, 1500])
