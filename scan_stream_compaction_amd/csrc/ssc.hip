@@ -657,7 +657,7 @@ struct SelArgs {
 };
 
 // 32-bit elements (int32, or fp32 bits); the predicate reads the element.
-// Eight 128-bit loads per lane: 2048 elements per data wavefront.
+// Eight 128-bit loads per lane (kTileLoads): 2048 elements per data wavefront.
 template <bool VEC>
 struct FmtB32 {
     using Shape = ChunkShape<kTileLoads, 4>;
@@ -730,9 +730,9 @@ struct FmtFlags {
 };
 
 // Key-value pairs: 32-bit keys (the predicate reads them) and 32-bit values
-// that travel with them. Four 128-bit loads per lane of each array: 1024
-// pairs per data wavefront, keys staged in the first half of the region and
-// values in the second.
+// that travel with them. Four 128-bit loads per lane of each array (half of
+// kTileLoads, rounded up): 1024 pairs per data wavefront, keys staged in the
+// first half of the region and values in the second.
 template <bool VEC>
 struct FmtPairs {
     using Shape = ChunkShape<(kTileLoads + 1) / 2, 4>;
@@ -782,8 +782,9 @@ __device__ __forceinline__ bool pred_eval64(uint64_t u, const PredArgs &pr) {
     }
 }
 
-// 64-bit elements: eight 128-bit loads per lane of two elements each, 1024
-// elements per data wavefront (8-byte aligned arrays take 64-bit loads).
+// 64-bit elements: eight 128-bit loads per lane (kTileLoads) of two elements
+// each, 1024 elements per data wavefront (8-byte aligned arrays take 64-bit
+// loads).
 template <bool VEC>
 struct FmtB64 {
     using Shape = ChunkShape<kTileLoads, 2>;
