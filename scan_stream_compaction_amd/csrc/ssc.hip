@@ -524,16 +524,57 @@ __device__ __forceinline__ uint32_t valid_mask(int lane, uint32_t rem) {
 // Flags of L x 4 32-bit elements as a per-lane mask: bit j*4 + k is the
 // predicate of element (j, lane, k), evaluated once; elements past rem are
 // not flagged.
+//
+// The mask is assembled with v_alignbit_b32, which shifts a 64-bit pair
+// right and keeps the low word: alignbit(x, m, 1) is m >> 1 with bit 0 of x
+// entering at bit 31, so after the 32 elements in order, element e sits at
+// bit e. That is one instruction per element for the parity predicates and
+// two for NONZERO (min(x, 1) is 1 iff x != 0) and the bit tests, where a
+// shift and a mask, or a compare and a select, cost three or four. MOD_LT
+// subtracts the threshold from the residue's fraction (both in [0, 1], so
+// the difference is negative, its sign bit set, exactly when the element is
+// kept) and shifts that sign bit in from the bottom instead: alignbit(m,
+// hi, 31) is m << 1 with bit 31 of hi entering at bit 0, and a bit reversal
+// at the end puts element e at bit e.
 template <int P, int L>
 __device__ __forceinline__ uint32_t mask_b32(const int32_t (&v)[L][4], int lane, uint32_t rem,
                                              const PredArgs &pr) {
+    constexpr int kN = L * 4;
     uint32_t mask = 0;
+    if constexpr (P <= 5) {
 #pragma unroll
-    for (int j = 0; j < L; ++j)
+        for (int j = 0; j < L; ++j)
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            mask |= static_cast<uint32_t>(pred_eval<P>(v[j][k], pr)) << (j * 4 + k);
-    if (rem < static_cast<uint32_t>(kWave * L * 4)) mask &= valid_mask<L, 4>(lane, rem);
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t u = static_cast<uint32_t>(v[j][k]);
+                if constexpr (P == 0) {
+                    // min(u, 1) written as the instruction: the compiler would
+                    // turn it into a compare and a select
+                    uint32_t nz;
+                    asm("v_min_u32 %0, %1, 1" : "=v"(nz) : "v"(u));
+                    mask = __builtin_amdgcn_alignbit(nz, mask, 1);
+                } else if constexpr (P == 1 || P == 2) {
+                    mask = __builtin_amdgcn_alignbit(u, mask, 1);
+                } else if constexpr (P == 3 || P == 4) {
+                    mask = __builtin_amdgcn_alignbit(u >> pr.a, mask, 1);
+                } else {
+                    const double t = __builtin_fma(static_cast<double>(v[j][k]), pr.inv, pr.half);
+                    const double d = __builtin_amdgcn_fract(t) - pr.thr;
+                    const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint64_t, d) >> 32);
+                    mask = __builtin_amdgcn_alignbit(mask, hi, 31);
+                }
+            }
+        if constexpr (P == 5) mask = __builtin_bitreverse32(mask);
+        if constexpr (kN < 32) mask >>= 32 - kN;  // the first element at bit 0
+        if constexpr (P == 2 || P == 4) mask = ~mask & (kN < 32 ? (1u << kN) - 1u : ~0u);
+    } else {
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                mask |= static_cast<uint32_t>(pred_eval<P>(v[j][k], pr)) << (j * 4 + k);
+    }
+    if (rem < static_cast<uint32_t>(kN * kWave)) mask &= valid_mask<L, 4>(lane, rem);
     return mask;
 }
 
@@ -629,6 +670,7 @@ struct FmtB32 {
     static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;  // element values are loaded
+    static constexpr int kSlotWords = 1;  // 32-bit words per staged survivor
     struct Regs {
         int32_t v[L][4];
     };
@@ -660,6 +702,7 @@ struct FmtFlags {
     static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = VALUES;
+    static constexpr int kSlotWords = 1;  // 32-bit words per staged survivor
     struct Regs {
         int32_t v[L][4];
         uint32_t f[L];
@@ -704,6 +747,7 @@ struct FmtPairs {
     static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;
+    static constexpr int kSlotWords = 1;  // 32-bit words per staged survivor
     struct Regs {
         int32_t k[L][4];
         int32_t v[L][4];
@@ -756,6 +800,7 @@ struct FmtB64 {
     static constexpr int L = Shape::kLoads;
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;
+    static constexpr int kSlotWords = 2;  // 32-bit words per staged survivor
     struct Regs {
         uint64_t v[L][2];
     };
@@ -862,13 +907,13 @@ enum { kCompact = 0, kCompactRanks = 1, kPartition = 2, kSelectIndex = 3, kParti
 //     279.6 -> 273.1, flag-byte compaction 327.2 -> 310.2;
 //   two: ranks 463 -> 476, partitions 537 -> 540, the radix driver's
 //     chained splits (2^24 keys, 1,176 -> 1,210 a sort);
-//   MOD_LT(100, s) by the fraction it is expected to keep (DEEP, chosen
-//     on the host): three from s >= m/4 (50%: 289.5 -> 269.5, 99%: 366.3 ->
-//     365.8), two below (1%: 216 -> 226, 10%: 230.5 -> 233.6). Either
-//     is correct for any input; only the speed depends on the fraction kept.
-template <class F, int P, int KIND, bool DEEP = false>
+//   MOD_LT(100, s) with the residue read off a fraction (four fp64
+//     operations per element): 1% kept 211.9 -> 206.7, 10% 229.6 -> 219.1,
+//     50% 268.3 -> 268.0. (With the earlier seven-operation residue, three
+//     sets lost below a quarter kept: 1% 216 -> 226.)
+template <class F, int P, int KIND>
 constexpr bool three_sets() {
-    return (KIND == kCompact || KIND == kSelectIndex) && (P != 5 || DEEP) && F::kValues;
+    return (KIND == kCompact || KIND == kSelectIndex) && F::kValues;
 }
 // The look-back with three sets (MOD_LT aside) goes straight to its window and
 // polls at s_sleep 32; with two it first waits on its predecessor and polls
@@ -881,7 +926,7 @@ constexpr int sel_poll_sleep() {
 
 // F is the element format (what a chunk holds and how survivors are staged
 // and written); partition and ranks are defined for 32-bit elements.
-template <class F, int P, int KIND, bool DEEP = false>
+template <class F, int P, int KIND>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(
     SelArgs a, int64_t n, PredArgs pr, void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
@@ -899,7 +944,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
     __shared__ uint32_t s_first[3], s_epoch, s_arrive;
 
-    constexpr bool kThree = three_sets<F, P, KIND, DEEP>();
+    constexpr bool kThree = three_sets<F, P, KIND>();
     constexpr bool kLbFast = kThree && P != 5;  // look-back without the predecessor poll
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
@@ -1023,20 +1068,33 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             /* (a selection stages each element's index instead of its value)    */            \
             const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * S::kPer;        \
             _Pragma("unroll") for (int j = 0; j < S::kLoads; ++j) {                           \
-                uint32_t r = lead[j];                                                         \
-                const uint32_t rej =                                                          \
-                    a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);      \
-                _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                         \
-                    const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                    \
-                    if constexpr (kPart) {                                                    \
+                if constexpr (kPart) {                                                        \
+                    uint32_t r = lead[j];                                                     \
+                    const uint32_t rej =                                                      \
+                        a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);  \
+                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
+                        const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                \
                         F::stage(s_stage[w], f ? r : rej + k - r, CUR, j, k);                 \
-                    } else if (f) {                                                           \
-                        if constexpr (KIND == kSelectIndex)                                   \
-                            s_stage[w][r] = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
-                        else                                                                  \
-                            F::stage(s_stage[w], r, CUR, j, k);                               \
+                        r += f;                                                               \
                     }                                                                         \
-                    r += f;                                                                   \
+                } else {                                                                      \
+                    /* a running LDS pointer that each element's flag advances; */           \
+                    /* the flag is opaque so that the test reuses the extracted */           \
+                    /* bit (else it is taken from the mask a second time)       */           \
+                    /* (a selection stages one 32-bit position per survivor)    */           \
+                    constexpr int kSlot = KIND == kSelectIndex ? 1 : F::kSlotWords;           \
+                    uint32_t *p = s_stage[w] + lead[j] * kSlot;                               \
+                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
+                        uint32_t f = __builtin_amdgcn_ubfe(fm_cur, j * S::kPer + k, 1);       \
+                        asm volatile("" : "+v"(f));                                           \
+                        if (f) {                                                              \
+                            if constexpr (KIND == kSelectIndex)                               \
+                                *p = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
+                            else                                                              \
+                                F::stage(p, 0, CUR, j, k);                                    \
+                        }                                                                     \
+                        p += f * kSlot;                                                       \
+                    }                                                                         \
                 }                                                                             \
             }                                                                                 \
         }                                                                                     \
@@ -2411,14 +2469,13 @@ int32_t f32_bits(float f) {
 }
 
 // Arguments of a predicate as the kernels take them (see PredArgs); for
-// MOD_LT the fp64 constants of the division by the invariant modulus a >= 1.
+// MOD_LT the fp64 constants of the residue test for the modulus a >= 1.
 PredArgs make_pred_args(int pred, int32_t pa, int32_t pb) {
-    PredArgs p{pa, pb, 0.0, 0.0, 0.0, 0.0};
+    PredArgs p{pa, pb, 0.0, 0.0, 0.0};
     if (pred == SSC_PRED_MOD_LT) {
         p.inv = 1.0 / static_cast<double>(pa);
-        p.ad = static_cast<double>(pa);
-        p.bd = static_cast<double>(pb);
-        p.bma = static_cast<double>(pb) - static_cast<double>(pa);
+        p.half = 0.5 * p.inv;
+        p.thr = static_cast<double>(pb) / static_cast<double>(pa);
     }
     return p;
 }
@@ -2493,19 +2550,9 @@ int dispatch_pred(int pred, bool vec, A... a) {
     }
 }
 
-// Or-ed into a kind: a MOD_LT(m, s) compaction or selection expected to keep
-// at least a quarter of uniform input (4s >= m) takes three register sets
-// (see three_sets). Only the speed depends on it.
-constexpr int kDeep = 0x100;
-inline int with_depth(int kind, int pred, int32_t pa, int32_t pb) {
-    const bool deep = pred == SSC_PRED_MOD_LT && (kind == kCompact || kind == kSelectIndex) &&
-                      4 * static_cast<int64_t>(pb) >= static_cast<int64_t>(pa);
-    return deep ? (kind | kDeep) : kind;
-}
-
 // One launch of the persistent kernel for element format F and kind KIND:
 // one workgroup per compute unit, at most one per tile.
-template <class F, int P, int KIND, bool DEEP = false>
+template <class F, int P, int KIND>
 int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint32_t capacity,
                   int32_t *count, int32_t *ranks, const int32_t *kept, hipStream_t s) {
     constexpr int64_t kTileElems = F::Shape::kTileElems;
@@ -2513,7 +2560,7 @@ int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint3
     uint32_t slots = 0;
     SSC_TRY(compute_units(&slots));
     const dim3 grid(tiles < slots ? tiles : slots);
-    hipLaunchKernelGGL((select_kernel<F, P, KIND, DEEP>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
+    hipLaunchKernelGGL((select_kernel<F, P, KIND>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
                        tiles, capacity, count, ranks, kept);
     return launched();
 }
@@ -2526,25 +2573,16 @@ struct LaunchSelect {
                    const int32_t *kept, hipStream_t s) {
         using F = FmtB32<VEC>;
         const SelArgs a{in, nullptr, out, nullptr};
-        const bool deep = (kind & kDeep) != 0;
-        switch (kind & ~kDeep) {
+        switch (kind) {
         case kPartition:
             return launch_select<F, P, kPartition>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         case kCompactRanks:
             return launch_select<F, P, kCompactRanks>(a, n, pr, scratch, capacity, count, ranks,
                                                       kept, s);
         case kSelectIndex:
-            if constexpr (P == 5)
-                if (deep)
-                    return launch_select<F, P, kSelectIndex, true>(a, n, pr, scratch, capacity, count,
-                                                                   ranks, kept, s);
             return launch_select<F, P, kSelectIndex>(a, n, pr, scratch, capacity, count, ranks,
                                                      kept, s);
         default:
-            if constexpr (P == 5)
-                if (deep)
-                    return launch_select<F, P, kCompact, true>(a, n, pr, scratch, capacity, count,
-                                                               ranks, kept, s);
             return launch_select<F, P, kCompact>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         }
     }
@@ -2763,7 +2801,7 @@ int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t p
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect, F32>(pred, vec, with_depth(ranks ? kCompactRanks : kCompact, pred, pa, pb), in, out, n,
+    return dispatch_pred<LaunchSelect, F32>(pred, vec, ranks ? kCompactRanks : kCompact, in, out, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count, ranks,
                                        static_cast<const int32_t *>(nullptr), s);
@@ -2787,7 +2825,7 @@ int select_index_impl(const int32_t *in, int32_t *idx, int64_t n, int pred, int3
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
-    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), with_depth(kSelectIndex, pred, pa, pb), in, idx, n,
+    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), kSelectIndex, in, idx, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count,
                                        static_cast<int32_t *>(nullptr),
@@ -2863,7 +2901,7 @@ int flags_impl(const void *in, const uint8_t *flags, void *out, int64_t n, int32
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const SelArgs a{in, flags, out, nullptr};
-    const PredArgs pr{0, 0, 0u, 0u, 0u, 0u};
+    const PredArgs pr{0, 0, 0.0, 0.0, 0.0};
     const uint32_t cap = capacity_of(scratch_bytes);
     if (!values && aligned(flags, 16)) {
         const uint32_t tiles = static_cast<uint32_t>((n + kFlagTile - 1) / kFlagTile);

@@ -87,17 +87,19 @@ __device__ __forceinline__ typename Op::T wave_sum(typename Op::T v) {
 // F32 predicates (6..9) read the 32-bit element and a, b as fp32 bits and
 // compare with IEEE semantics (NaN compares false, -0.0 == 0.0).
 //
-// MOD_LT divides in fp64 with constants the host computes once per call
-// (make_pred_args): inv = 1/a rounded once, then q = floor(fma(x, inv,
-// 2^-20)) and r = fma(-q, a, x) = x - q*a exactly (all integers below 2^33).
-// fma(x, inv, 2^-20) is within 2^-21 of x/a + 2^-20 for |x| <= 2^31, so q is
-// floor(x/a) or one more and r lies in [-a, a); the non-negative residue is
-// below b iff 0 <= r < b, or r < b - a (a negative r stands for r + a). Four
-// full-rate fp64 operations and three compares, where an integer division by
-// multiplication needs two quarter-rate 32-bit multiplies and corrections.
+// MOD_LT reads the residue off a fractional part, with constants the host
+// computes once per call (make_pred_args): inv = 1/a rounded once, half =
+// inv/2 and thr = b/a rounded once. t = fma(x, inv, half) is (x + 1/2)/a to
+// within 2^-21/a for every int32 x, and (x + 1/2)/a = floor(x/a) + (r + 1/2)/a
+// with r the non-negative residue, whose fractional part lies in [1/(2a),
+// 1 - 1/(2a)]. The error is far inside that margin, so floor(t) = floor(x/a)
+// and t - floor(t) (v_fract_f64, exact) is (r + 1/2)/a to within 2^-21/a,
+// which is below b/a iff r < b, with 1/(2a) to spare on either side (b <= 0
+// keeps nothing, b >= a everything). Four full-rate fp64 operations: convert,
+// fma, fract, compare.
 struct PredArgs {
     int32_t a, b;
-    double inv, ad, bd, bma;  // MOD_LT: 1/a, a, b, b - a
+    double inv, half, thr;  // MOD_LT: 1/a, 1/(2a), b/a
 };
 
 template <int P>
@@ -124,10 +126,8 @@ __device__ __forceinline__ bool pred_eval(int32_t x, const PredArgs &pr) {
         return __int_as_float(pr.a) <= f && f < __int_as_float(pr.b);
     } else {
         static_assert(P == 5, "predicate numbering");
-        const double xd = static_cast<double>(x);
-        const double q = __builtin_floor(__builtin_fma(xd, pr.inv, 0x1p-20));
-        const double r = __builtin_fma(-q, pr.ad, xd);
-        return (r >= 0.0 && r < pr.bd) || r < pr.bma;
+        const double t = __builtin_fma(static_cast<double>(x), pr.inv, pr.half);
+        return __builtin_amdgcn_fract(t) < pr.thr;
     }
 }
 

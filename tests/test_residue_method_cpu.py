@@ -1,8 +1,9 @@
-"""The MOD_LT predicate's fp64 residue method, checked on the host against
-64-bit integer residues (tests/residue_fp64.c): the ends and the middle of
-the int32 range for moduli on both sides of the bound where the quotient
-estimate can run one high, the extreme moduli, and 5e7 random (x, m, s)
-triples with s from -1 to m + 1. `residue_fp64 full` sweeps all 2^32 x."""
+"""The MOD_LT predicate's fp64 residue method (the fraction of
+fma(x, 1/m, 1/(2m)) against s/m), checked on the host against 64-bit integer
+residues (tests/residue_fp64.c): the ends and the middle of the int32 range
+for small, prime and the largest moduli with bounds inside and outside
+[1, m - 1], and 5e7 random (x, m, s) triples with s from -1 to m + 1.
+`residue_fp64 full` sweeps all 2^32 x."""
 from __future__ import annotations
 
 import os
