@@ -671,6 +671,7 @@ struct FmtB32 {
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;  // element values are loaded
     static constexpr int kSlotWords = 1;  // 32-bit words per staged survivor
+    static constexpr bool kFlagFirst = true;  // stage after the next chunk's arrival
     struct Regs {
         int32_t v[L][4];
     };
@@ -703,6 +704,7 @@ struct FmtFlags {
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = VALUES;
     static constexpr int kSlotWords = 1;  // 32-bit words per staged survivor
+    static constexpr bool kFlagFirst = false;  // stage after the next chunk's arrival
     struct Regs {
         int32_t v[L][4];
         uint32_t f[L];
@@ -748,6 +750,7 @@ struct FmtPairs {
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;
     static constexpr int kSlotWords = 1;  // 32-bit words per staged survivor
+    static constexpr bool kFlagFirst = true;  // stage after the next chunk's arrival
     struct Regs {
         int32_t k[L][4];
         int32_t v[L][4];
@@ -801,6 +804,7 @@ struct FmtB64 {
     static constexpr bool kVec = VEC;
     static constexpr bool kValues = true;
     static constexpr int kSlotWords = 2;  // 32-bit words per staged survivor
+    static constexpr bool kFlagFirst = false;  // stage after the next chunk's arrival
     struct Regs {
         uint64_t v[L][2];
     };
@@ -866,7 +870,9 @@ struct FmtB64 {
 //      freed up (with a third register set, before step 1: see three_sets);
 //   3. flags the next tile's chunk (waiting only for those loads), writes
 //      its total to LDS and arrives; the last of the 15 to arrive scans the
-//      totals and publishes the next tile's {aggregate} at once;
+//      totals and publishes the next tile's {aggregate} at once (with three
+//      sets the 32-bit and key-value formats take this step before step 1:
+//      see kFlagFirst);
 //   4. waits at the tile's one workgroup barrier for the base (the survivors
 //      of all earlier tiles) that the control wavefront found;
 //   5. writes its region out to out[base + chunk prefix].
@@ -945,6 +951,14 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     __shared__ uint32_t s_first[3], s_epoch, s_arrive;
 
     constexpr bool kThree = three_sets<F, P, KIND>();
+    // With three sets, the 32-bit and key-value formats flag the next chunk
+    // and arrive before staging the current one, so the next tile's
+    // aggregate goes out as soon as its data has landed and the staging
+    // fills the wait at the barrier (2^28 MOD_LT(100, 1): 200.1 -> 197.9 us,
+    // key-value pairs 263.3 -> 261.6; MOD_LT(100, 99) 349.1 -> 349.8, int64
+    // 261.4 -> 262.0, and flag-byte compaction, at the register cap, 309 ->
+    // 361, keep the other order).
+    constexpr bool kFlagFirst = kThree && F::kFlagFirst;
     constexpr bool kLbFast = kThree && P != 5;  // look-back without the predecessor poll
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
@@ -1058,7 +1072,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         int ln = lane;                                                                        \
         asm volatile("" : "+v"(ln));                                                          \
         if constexpr (kThree) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, FREE);             \
-        {                                                                                     \
+        if constexpr (!kFlagFirst) {                                                          \
             /* a partition gives every element a slot of its own, no branches:   */            \
             /* survivors at their rank, the others after all survivors at a_cur + */            \
             /* (index - rank), elements past rem included (they land past the     */            \
@@ -1102,6 +1116,46 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                     \
         rem_nxt = rem_of(nxt);                                                                \
         SSC_FLAG_AND_ARRIVE(NX, nxt, rem_nxt, fm_nxt, a_nxt, tri_n, ln)                       \
+        if constexpr (kFlagFirst) {                                                           \
+            /* a partition gives every element a slot of its own, no branches:   */            \
+            /* survivors at their rank, the others after all survivors at a_cur + */            \
+            /* (index - rank), elements past rem included (they land past the     */            \
+            /* runs); compaction and selection stage the survivors only           */            \
+            uint32_t lead[S::kLoads];                                                         \
+            chunk_leads<S::kLoads, S::kPer>(fm_cur, lead);                                    \
+            /* (a selection stages each element's index instead of its value)    */            \
+            const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * S::kPer;        \
+            _Pragma("unroll") for (int j = 0; j < S::kLoads; ++j) {                           \
+                if constexpr (kPart) {                                                        \
+                    uint32_t r = lead[j];                                                     \
+                    const uint32_t rej =                                                      \
+                        a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);  \
+                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
+                        const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                \
+                        F::stage(s_stage[w], f ? r : rej + k - r, CUR, j, k);                 \
+                        r += f;                                                               \
+                    }                                                                         \
+                } else {                                                                      \
+                    /* a running LDS pointer that each element's flag advances; */           \
+                    /* the flag is opaque so that the test reuses the extracted */           \
+                    /* bit (else it is taken from the mask a second time)       */           \
+                    /* (a selection stages one 32-bit position per survivor)    */           \
+                    constexpr int kSlot = KIND == kSelectIndex ? 1 : F::kSlotWords;           \
+                    uint32_t *p = s_stage[w] + lead[j] * kSlot;                               \
+                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
+                        uint32_t f = __builtin_amdgcn_ubfe(fm_cur, j * S::kPer + k, 1);       \
+                        asm volatile("" : "+v"(f));                                           \
+                        if (f) {                                                              \
+                            if constexpr (KIND == kSelectIndex)                               \
+                                *p = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
+                            else                                                              \
+                                F::stage(p, 0, CUR, j, k);                                    \
+                        }                                                                     \
+                        p += f * kSlot;                                                       \
+                    }                                                                         \
+                }                                                                             \
+            }                                                                                 \
+        }                                                                                     \
         __syncthreads(); /* B1: this tile's base is known */                                  \
         /* the ranks' leads come from fm_cur after the barrier: computed before  */           \
         /* it, they stayed live across the next chunk's flags and the kernel     */           \
