@@ -530,7 +530,8 @@ __device__ __forceinline__ uint32_t valid_mask(int lane, uint32_t rem) {
 // entering at bit 31, so after the 32 elements in order, element e sits at
 // bit e. That is one instruction per element for the parity predicates and
 // two for NONZERO (min(x, 1) is 1 iff x != 0) and the bit tests, where a
-// shift and a mask, or a compare and a select, cost three or four. MOD_LT
+// shift and a mask, or a compare and a select, cost three or four; the fp32
+// comparisons enter their 0/1 the same way. MOD_LT
 // subtracts the threshold from the residue's fraction (both in [0, 1], so
 // the difference is negative, its sign bit set, exactly when the element is
 // kept) and shifts that sign bit in from the bottom instead: alignbit(m,
@@ -541,39 +542,35 @@ __device__ __forceinline__ uint32_t mask_b32(const int32_t (&v)[L][4], int lane,
                                              const PredArgs &pr) {
     constexpr int kN = L * 4;
     uint32_t mask = 0;
-    if constexpr (P <= 5) {
 #pragma unroll
-        for (int j = 0; j < L; ++j)
+    for (int j = 0; j < L; ++j)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t u = static_cast<uint32_t>(v[j][k]);
-                if constexpr (P == 0) {
-                    // min(u, 1) written as the instruction: the compiler would
-                    // turn it into a compare and a select
-                    uint32_t nz;
-                    asm("v_min_u32 %0, %1, 1" : "=v"(nz) : "v"(u));
-                    mask = __builtin_amdgcn_alignbit(nz, mask, 1);
-                } else if constexpr (P == 1 || P == 2) {
-                    mask = __builtin_amdgcn_alignbit(u, mask, 1);
-                } else if constexpr (P == 3 || P == 4) {
-                    mask = __builtin_amdgcn_alignbit(u >> pr.a, mask, 1);
-                } else {
-                    const double t = __builtin_fma(static_cast<double>(v[j][k]), pr.inv, pr.half);
-                    const double d = __builtin_amdgcn_fract(t) - pr.thr;
-                    const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint64_t, d) >> 32);
-                    mask = __builtin_amdgcn_alignbit(mask, hi, 31);
-                }
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t u = static_cast<uint32_t>(v[j][k]);
+            if constexpr (P == 0 || P == 6) {
+                // min(u, 1) written as the instruction (the compiler would
+                // turn it into a compare and a select); an fp32 is nonzero
+                // iff its bits without the sign are
+                const uint32_t b = P == 0 ? u : u << 1;
+                uint32_t nz;
+                asm("v_min_u32 %0, %1, 1" : "=v"(nz) : "v"(b));
+                mask = __builtin_amdgcn_alignbit(nz, mask, 1);
+            } else if constexpr (P == 1 || P == 2) {
+                mask = __builtin_amdgcn_alignbit(u, mask, 1);
+            } else if constexpr (P == 3 || P == 4) {
+                mask = __builtin_amdgcn_alignbit(u >> pr.a, mask, 1);
+            } else if constexpr (P == 5) {
+                const double t = __builtin_fma(static_cast<double>(v[j][k]), pr.inv, pr.half);
+                const double d = __builtin_amdgcn_fract(t) - pr.thr;
+                const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint64_t, d) >> 32);
+                mask = __builtin_amdgcn_alignbit(mask, hi, 31);
+            } else {
+                mask = __builtin_amdgcn_alignbit(pred_eval<P>(v[j][k], pr) ? 1u : 0u, mask, 1);
             }
-        if constexpr (P == 5) mask = __builtin_bitreverse32(mask);
-        if constexpr (kN < 32) mask >>= 32 - kN;  // the first element at bit 0
-        if constexpr (P == 2 || P == 4) mask = ~mask & (kN < 32 ? (1u << kN) - 1u : ~0u);
-    } else {
-#pragma unroll
-        for (int j = 0; j < L; ++j)
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                mask |= static_cast<uint32_t>(pred_eval<P>(v[j][k], pr)) << (j * 4 + k);
-    }
+        }
+    if constexpr (P == 5) mask = __builtin_bitreverse32(mask);
+    if constexpr (kN < 32) mask >>= 32 - kN;  // the first element at bit 0
+    if constexpr (P == 2 || P == 4) mask = ~mask & (kN < 32 ? (1u << kN) - 1u : ~0u);
     if (rem < static_cast<uint32_t>(kN * kWave)) mask &= valid_mask<L, 4>(lane, rem);
     return mask;
 }
