@@ -1601,27 +1601,36 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(8, 8))
 // The scan in the compaction kernel's pipeline: one 1024-thread workgroup per
 // compute unit loops over tiles of 30720 values claimed three ahead, each data
 // wavefront holding three chunks of 2048 values (eight 128-bit loads per
-// lane) in registers. Per tile it
+// lane) in registers and parking one more in its 8 KiB LDS region. Per tile
+// it
 //   1. sums the next tile's chunk once it has landed and arrives with the
 //      total; the last of the 15 to arrive scans the chunk totals and
 //      publishes the next tile's {aggregate} at once;
-//   2. issues the loads of the tile after next into the chunk written last
+//   2. issues the loads of the tile after next into the chunk parked last
 //      (issued after the next tile's have landed, not before: fewer reads
 //      waiting, 2^28 371.4 -> 367.4 us, fp32 377.4 -> 374.8);
-//   3. waits at the tile's barrier for its base from the control wavefront;
-//   4. scans the current chunk load by load (per load a DPP wavefront scan of
-//      the lanes' 4-value sums) and stores base + chunk prefix + the value's
-//      prefix at once, in the layout it was read with.
-// No LDS staging is needed: the output of a chunk is its input's positions.
-// Scanning at the store instead of on arrival keeps one chunk's prefixes
-// live instead of two, which is what lets three chunks fit in 128 VGPRs.
+//   3. waits at the tile's barrier, which hands over the base of the tile
+//      before it (not of this one);
+//   4. scans the previous tile's parked chunk load by load (per load a DPP
+//      wavefront scan of the lanes' 4-value sums), stores base + chunk
+//      prefix + the value's prefix in the layout it was read with, and parks
+//      the current chunk in the same LDS bytes.
+// So each look-back has a whole tile period: the control wavefront walks
+// the look-back of the previous tile while the data wavefronts arrive for
+// the next one, and publishes that tile's {inclusive} before the barrier.
+// A workgroup passes one more barrier than it has tiles, for the base of its
+// last one. Writing each chunk one barrier later took 2^28 from 367.0 to
+// 358.9 us (fp32 372.2 -> 370.1); before it, the control wavefront was last
+// at the barrier in 90% of the tiles and the data wavefronts waited there
+// 3-5 us per tile. Scanning a chunk in place on arrival instead (its
+// prefixes then live beside three register sets) spilled 8-39 dwords.
 // WIDE (fp32): carries between tiles are fp64 (wide descriptors, fp64
 // look-back) and each output is rounded to fp32 once from the fp64 sum of
 // base, chunk prefix and in-chunk prefix. Forward progress as for
-// select_kernel. Measured (interleaved A/B, exclusive int32): 2^28 369.7 us
-// against 377.1 for one workgroup per tile, fp32 376 against 405, 2^24 29.8
-// against 36.1; a timing-only build without the look-back wait ran about
-// 10 us faster at 2^28.
+// select_kernel: a tile's aggregate waits only on its own data, and a
+// look-back only on lower tiles. Earlier measurements (interleaved A/B,
+// exclusive int32, before the parked chunk): 2^28 369.7 us against 377.1 for
+// one workgroup per tile, fp32 376 against 405, 2^24 29.8 against 36.1.
 constexpr int kScanPSleep = 32;  // look-back poll interval, s_sleep units
 
 template <class Op, bool VEC, bool INCL, bool WIDE>
@@ -1637,6 +1646,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     __shared__ uint32_t s_base[2], s_next[2];      // by tile parity
     __shared__ double s_base64[2];
     __shared__ uint32_t s_first[3], s_epoch, s_arrive;
+    __shared__ __attribute__((aligned(16))) uint32_t s_park[kDataWaves][S::kChunk];
 
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
@@ -1667,45 +1677,48 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         uint32_t nxt = uniform(s_first[1]);
         uint32_t nxt2 = uniform(s_first[2]);
         __syncthreads();  // B0': the first tile's arrivals are in
+        uint32_t prev = kNoTile;  // the tile whose base this iteration's barrier hands over
         while (true) {
             uint32_t nxt3 = kNoTile;
             if (lane == 0 && nxt2 < num_tiles) {
                 nxt3 = static_cast<uint32_t>(claim_tiles(sv, 1));
                 last_claim = nxt3 >= num_tiles;
             }
-            T prefix = Op::zero();
-            double prefix64 = 0.0;
-            if (tile != 0) {
-                if constexpr (WIDE)
-                    prefix64 = look_back_wide<kScanPSleep>(sv.desc, tile, tag, sv.timed_out);
-                else
-                    prefix = look_back<Op, kScanPSleep, false>(sv.desc, tile, tag, sv.timed_out);
-            }
-            if (lane == 0) {
-                if constexpr (WIDE)
-                    s_base64[par] = prefix64;
-                else
-                    s_base[par] = Op::bits(prefix);
-                s_next[par] = nxt3;
-            }
-            __syncthreads();  // B1
-            const T agg = Op::from_bits(uniform(s_pre[tri][kDataWaves]));
-            if (lane == 0) {
-                // {inclusive} at least one barrier after this tile's
-                // {aggregate}: from one compute unit, in issue order
-                if constexpr (WIDE) {
-                    const double incl = prefix64 + static_cast<double>(agg);
-                    if (tile != 0) publish_wide(sv.desc, tile, tag, kStatusInclusive, incl);
-                    if (total != nullptr && tile == num_tiles - 1) *total = static_cast<T>(incl);
-                } else {
-                    const T incl = Op::add(prefix, agg);
-                    if (tile != 0) publish(sv.desc + tile, tag, kStatusInclusive, Op::bits(incl));
-                    if (total != nullptr && tile == num_tiles - 1) *total = incl;
+            if (prev != kNoTile) {
+                T prefix = Op::zero();
+                double prefix64 = 0.0;
+                if (prev != 0) {
+                    if constexpr (WIDE)
+                        prefix64 = look_back_wide<kScanPSleep>(sv.desc, prev, tag, sv.timed_out);
+                    else
+                        prefix = look_back<Op, kScanPSleep, false>(sv.desc, prev, tag, sv.timed_out);
                 }
+                // prev's aggregate is read before the barrier: the arrivals of
+                // the next iteration rewrite its slot
+                const T agg = Op::from_bits(uniform(s_pre[tri == 0u ? 2u : tri - 1u][kDataWaves]));
+                if (lane == 0) {
+                    // {inclusive} two barriers after this tile's {aggregate}
+                    if constexpr (WIDE) {
+                        s_base64[par ^ 1u] = prefix64;
+                        const double incl = prefix64 + static_cast<double>(agg);
+                        if (prev != 0) publish_wide(sv.desc, prev, tag, kStatusInclusive, incl);
+                        if (total != nullptr && prev == num_tiles - 1) *total = static_cast<T>(incl);
+                    } else {
+                        s_base[par ^ 1u] = Op::bits(prefix);
+                        const T incl = Op::add(prefix, agg);
+                        if (prev != 0) publish(sv.desc + prev, tag, kStatusInclusive, Op::bits(incl));
+                        if (total != nullptr && prev == num_tiles - 1) *total = incl;
+                    }
+                }
+            }
+            if (lane == 0) s_next[par] = nxt3;
+            __syncthreads();  // B1
+            if (lane == 0) {
                 if (last_claim) finish_claims(sv, epoch, gridDim.x, words_used, capacity);
                 last_claim = false;
             }
-            if (nxt >= num_tiles) return;
+            if (tile >= num_tiles) return;  // that barrier handed over this workgroup's last base
+            prev = tile;
             tile = nxt;
             nxt = nxt2;
             nxt2 = uniform(nxt3);
@@ -1726,9 +1739,14 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // offset register, and the range check still covers the whole access
     // (the instruction's scalar offset is outside that check, so it cannot
     // carry j).
+    // The byte count goes through readfirstlane: the compiler computes the
+    // saturating subtraction in a VGPR, and a resource it cannot prove
+    // wave-uniform wraps every load and store in a one-pass waterfall loop
+    // (readfirstlane x4, two compares, exec juggling: 57 such loops in the
+    // int32 kernel, 226 in the 32-bit-access form).
     const auto part_rsrc = [&](const void *chunk, uint32_t bytes, int j) {
         const uint32_t skip = static_cast<uint32_t>(j) * (kWave * 16);
-        return buffer_rsrc(static_cast<const char *>(chunk) + skip, bytes > skip ? bytes - skip : 0u);
+        return buffer_rsrc(static_cast<const char *>(chunk) + skip, uniform(bytes > skip ? bytes - skip : 0u));
     };
     const auto load = [&](uint32_t t, int ln, uint32_t(&v)[S::kLoads][4]) {
         const T *c = in + chunk_of(t);
@@ -1787,67 +1805,91 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
             }
         }
     };
-    // Scans the chunk load by load (exclusive, or with INCL inclusive) and
-    // stores base + chunk prefix + in-chunk prefix in the load layout.
-    const auto write = [&](const uint32_t(&v)[S::kLoads][4], uint32_t t, uint32_t par_, uint32_t tri_,
-                           int ln) {
-        const T *c = out + chunk_of(t);
-        const uint32_t bytes = rem_of(t) * 4u;
-        const T cb = Op::from_bits(uniform(s_pre[tri_][w]));
+    // A tile's chunk is parked in the wavefront's LDS region from the barrier
+    // of its own iteration to the next one, which hands over its base.
+    // write_park scans the parked chunk of tile tp load by load (exclusive,
+    // or with INCL inclusive) and stores base + chunk prefix + in-chunk
+    // prefix in the load layout, and parks cur in its place: each load's 16
+    // bytes per lane are read back, scanned and stored before the same bytes
+    // take cur's values. The tags leave out either half.
+    const auto write_park = [&](auto write_tag, auto park_tag, const uint32_t(&cur)[S::kLoads][4],
+                                uint32_t tp, uint32_t par_p, uint32_t tri_p, int ln) {
+        constexpr bool kWrite = decltype(write_tag)::value;
+        constexpr bool kPark = decltype(park_tag)::value;
+        u32x4 *slot = reinterpret_cast<u32x4 *>(&s_park[w][0]) + ln;
+        const T *c = out + chunk_of(tp);
+        const uint32_t bytes = kWrite ? rem_of(tp) * 4u : 0u;
         double b64 = 0.0;
         T base = Op::zero();
-        if constexpr (WIDE)
-            b64 = s_base64[par_] + static_cast<double>(cb);
-        else
-            base = Op::add(Op::from_bits(uniform(s_base[par_])), cb);
+        if constexpr (kWrite) {
+            const T cb = Op::from_bits(uniform(s_pre[tri_p][w]));
+            if constexpr (WIDE)
+                b64 = s_base64[par_p] + static_cast<double>(cb);
+            else
+                base = Op::add(Op::from_bits(uniform(s_base[par_p])), cb);
+        }
         T running = Op::zero();
 #pragma unroll
         for (int j = 0; j < S::kLoads; ++j) {
-            T p[4];
-            T s = Op::zero();
+            if constexpr (kWrite) {
+                const u32x4 xv = slot[j * kWave];
+                T p[4];
+                T s = Op::zero();
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const T x = Op::from_bits(v[j][k]);
-                if constexpr (INCL) {
-                    s = Op::add(s, x);
-                    p[k] = s;
+                for (int k = 0; k < 4; ++k) {
+                    const T x = Op::from_bits(xv[k]);
+                    if constexpr (INCL) {
+                        s = Op::add(s, x);
+                        p[k] = s;
+                    } else {
+                        p[k] = s;
+                        s = Op::add(s, x);
+                    }
+                }
+                const T incl = wave_inclusive_scan<Op>(s);
+                const uint32_t up = static_cast<uint32_t>(__shfl_up(static_cast<int>(Op::bits(incl)), 1));
+                const T lead = Op::add(running, ln == 0 ? Op::zero() : Op::from_bits(up));
+                running = Op::add(running, Op::from_bits(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                                               static_cast<int>(Op::bits(incl)), kWave - 1))));
+                uint32_t q[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const T pre = Op::add(lead, p[k]);
+                    if constexpr (WIDE)
+                        q[k] = Op::bits(static_cast<T>(b64 + static_cast<double>(pre)));
+                    else
+                        q[k] = Op::bits(Op::add(base, pre));
+                }
+                const __amdgpu_buffer_rsrc_t r = part_rsrc(c, bytes, j);
+                if constexpr (VEC) {
+                    u32x4 o;
+                    o[0] = q[0];
+                    o[1] = q[1];
+                    o[2] = q[2];
+                    o[3] = q[3];
+                    __builtin_amdgcn_raw_buffer_store_b128(o, r, ln * 16, 0, kNT);
                 } else {
-                    p[k] = s;
-                    s = Op::add(s, x);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        __builtin_amdgcn_raw_buffer_store_b32(q[k], r, ln * 16 + 4 * k, 0, kNT);
                 }
             }
-            const T incl = wave_inclusive_scan<Op>(s);
-            const uint32_t up = static_cast<uint32_t>(__shfl_up(static_cast<int>(Op::bits(incl)), 1));
-            const T lead = Op::add(running, ln == 0 ? Op::zero() : Op::from_bits(up));
-            running = Op::add(running, Op::from_bits(static_cast<uint32_t>(__builtin_amdgcn_readlane(
-                                           static_cast<int>(Op::bits(incl)), kWave - 1))));
-            uint32_t q[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const T pre = Op::add(lead, p[k]);
-                if constexpr (WIDE)
-                    q[k] = Op::bits(static_cast<T>(b64 + static_cast<double>(pre)));
-                else
-                    q[k] = Op::bits(Op::add(base, pre));
-            }
-            const __amdgpu_buffer_rsrc_t r = part_rsrc(c, bytes, j);
-            if constexpr (VEC) {
+            if constexpr (kPark) {
                 u32x4 o;
-                o[0] = q[0];
-                o[1] = q[1];
-                o[2] = q[2];
-                o[3] = q[3];
-                __builtin_amdgcn_raw_buffer_store_b128(o, r, ln * 16, 0, kNT);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) __builtin_amdgcn_raw_buffer_store_b32(q[k], r, ln * 16 + 4 * k, 0, kNT);
+                o[0] = cur[j][0];
+                o[1] = cur[j][1];
+                o[2] = cur[j][2];
+                o[3] = cur[j][3];
+                slot[j * kWave] = o;
             }
         }
     };
 
-    // One tile: CUR holds the current tile's scanned chunk, NX the next one in
-    // flight, FREE the chunk written one tile ago.
-#define SSC_SCAN_TILE(CUR, NX, FREE)                                                         \
+    // One tile: CUR holds the current tile's chunk (arrived, parked after the
+    // barrier), NX the next one in flight, FREE the chunk parked one tile
+    // ago. The barrier hands over the previous tile's base, whose parked
+    // chunk goes out before CUR takes its place.
+#define SSC_SCAN_TILE(CUR, NX, FREE, WRITE)                                                  \
     {                                                                                        \
         int ln = lane;                                                                       \
         asm volatile("" : "+v"(ln));                                                         \
@@ -1855,9 +1897,11 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         arrive(chunk_sum(NX), nxt, tri_n, ln);                                               \
         /* the tile after next's loads leave once the next tile's have landed */             \
         load(nxt2, ln, FREE);                                                                \
-        __syncthreads(); /* B1: this tile's base is known */                                 \
+        __syncthreads(); /* B1: the previous tile's base is known */                         \
         const uint32_t nxt3 = uniform(s_next[par]);                                          \
-        write(CUR, tile, par, tri, ln);                                                      \
+        write_park(std::integral_constant<bool, WRITE>{}, std::true_type{}, CUR, prev,       \
+                   par ^ 1u, tri == 0u ? 2u : tri - 1u, ln);                                 \
+        prev = tile;                                                                         \
         tile = nxt;                                                                          \
         nxt = nxt2;                                                                          \
         nxt2 = nxt3;                                                                         \
@@ -1872,14 +1916,20 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     load(nxt, lane, vb);
     arrive(chunk_sum(va), tile, tri, lane);
     __syncthreads();  // B0': every wavefront has arrived for the first tile
-    while (true) {
-        SSC_SCAN_TILE(va, vb, vc)
-        if (tile >= num_tiles) break;
-        SSC_SCAN_TILE(vb, vc, va)
-        if (tile >= num_tiles) break;
-        SSC_SCAN_TILE(vc, va, vb)
-        if (tile >= num_tiles) break;
+    uint32_t prev = kNoTile;
+    SSC_SCAN_TILE(va, vb, vc, false)  // the first tile: nothing parked yet
+    if (tile < num_tiles) {
+        while (true) {
+            SSC_SCAN_TILE(vb, vc, va, true)
+            if (tile >= num_tiles) break;
+            SSC_SCAN_TILE(vc, va, vb, true)
+            if (tile >= num_tiles) break;
+            SSC_SCAN_TILE(va, vb, vc, true)
+            if (tile >= num_tiles) break;
+        }
     }
+    __syncthreads();  // B1 once more: the base of this workgroup's last tile
+    write_park(std::true_type{}, std::false_type{}, va, prev, par ^ 1u, tri == 0u ? 2u : tri - 1u, lane);
 #undef SSC_SCAN_TILE
 }
 
