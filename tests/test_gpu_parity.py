@@ -426,8 +426,8 @@ PRED_CASES = [("nonzero", 0, 0), ("odd", 0, 0), ("even", 0, 0), ("bit_set", 0, 0
               ("bit_set", 13, 0), ("bit_set", 31, 0), ("bit_clear", 0, 0),
               ("bit_clear", 31, 0), ("mod_lt", 100, 50), ("mod_lt", 7, 3), ("mod_lt", 1, 1),
               ("mod_lt", 2147483647, 5), ("mod_lt", 3, 0),
-              # moduli that exercise every shape of the division by an invariant
-              # modulus: powers of two, 2^30 + 1, large primes, bounds <= 0 or >= m
+              # moduli from 2 to 2^31 - 2 for the residue test read off a
+              # fraction: powers of two, 2^30 + 1, large primes, bounds <= 0 or >= m
               ("mod_lt", 2, 1), ("mod_lt", 16, 5), ("mod_lt", 641, 320), ("mod_lt", 65535, 100),
               ("mod_lt", 1 << 30, 7), ("mod_lt", (1 << 30) + 1, 1 << 29),
               ("mod_lt", 1000000007, 123456789), ("mod_lt", 2147483646, 1073741823),
@@ -445,6 +445,30 @@ def test_every_predicate_full_range(pred, pa, pb):
     out, cnt = ssc.compact_atomic(dev(x), pred, pa, pb, variant=1)
     assert int(host(cnt)[0]) == m
     assert checks.same_multiset(host(out)[:m], want)
+
+
+MOD_EDGE_CASES = [(1, 1), (3, 2), (100, 1), (100, 99), ((1 << 20) + 1, 1 << 19), (1000000007, 3),
+                  (2147483647, 2147483646), (2147483647, 1)]
+
+
+@pytest.mark.parametrize("m,s", MOD_EDGE_CASES)
+def test_mod_lt_at_residue_edges(m, s):
+    """MOD_LT where the residue test is tightest: every value has residue 0,
+    s - 1, s or m - 1 (the fractions nearest the threshold s/m and nearest 0
+    and 1), with quotients at both ends of the int32 range and around 0,
+    where the rounding error of the fraction is largest or the sign flips."""
+    lo, hi = -(1 << 31), (1 << 31) - 1
+    qs = set()
+    for q0 in (lo // m, 0, hi // m):
+        qs.update(range(q0 - 40, q0 + 41))
+    rs = sorted({0, max(s - 1, 0), min(s, m - 1), m - 1})
+    vals = [q * m + r for q in sorted(qs) for r in rs]
+    x = np.array([v for v in vals if lo <= v <= hi], dtype=np.int64).astype(np.int32)
+    x = np.concatenate([x, np.array([lo, hi, 0, -1, 1], np.int32)])
+    reps = -(-(T + 97) // x.size)  # several tiles, a ragged tail
+    x = np.tile(x, reps)[: T + 97 + x.size]
+    check_compact(x, "mod_lt", m, s)
+    check_select_index(x, "mod_lt", m, s)
 
 
 def f32_input(seed: int, n: int) -> np.ndarray:
