@@ -1689,7 +1689,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
                 double prefix64 = 0.0;
                 if (prev != 0) {
                     if constexpr (WIDE)
-                        prefix64 = look_back_wide<kScanPSleep>(sv.desc, prev, tag, sv.timed_out);
+                        prefix64 = look_back_wide<kScanPSleep, false>(sv.desc, prev, tag, sv.timed_out);
                     else
                         prefix = look_back<Op, kScanPSleep, false>(sv.desc, prev, tag, sv.timed_out);
                 }

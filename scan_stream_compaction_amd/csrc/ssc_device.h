@@ -378,14 +378,16 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 // The look-back of `look_back` over wide descriptors: the same waiting,
 // windows, stopping rule and time-out, summing the values in fp64. Returns
-// the exclusive prefix of `tile` in every lane.
-template <int SLEEP>
+// the exclusive prefix of `tile` in every lane. PRED_FIRST as for
+// look_back (the persistent scan, whose look-back has a whole tile period,
+// goes straight to the window: 2^28 fp32 370.1 -> 362.7 us).
+template <int SLEEP, bool PRED_FIRST = true>
 __device__ double look_back_wide(uint64_t *desc, uint32_t tile, uint32_t tag,
                                  uint32_t *timed_out) {
     const int lane = lane_id();
     double prefix = 0.0;
     uint32_t spins = 0;
-    while (true) {
+    while (PRED_FIRST) {
         uint32_t st = 0;
         if (lane == 0) {
             double unused;
