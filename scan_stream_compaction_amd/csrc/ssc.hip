@@ -22,9 +22,11 @@
 // staged in LDS. Ranks inside a wavefront come from packed DPP scans of the
 // lanes' per-load flag counts. The kernel is a template over element formats
 // (32-bit values, a caller's flag bytes, key-value pairs, 64-bit values) that
-// share this pipeline. The scan kernel keeps one tile per workgroup: two
-// rounds of 15 chunks, the last data wavefront to finish scanning the 30
-// chunk totals.
+// share this pipeline. The scan of values runs in the same pipeline
+// (scan_persistent_kernel), each chunk parked in LDS until the next tile's
+// barrier hands over its base; between one and two tiles per compute unit a
+// one-tile-per-workgroup kernel (scan_kernel: two rounds of 15 chunks, the
+// last data wavefront to finish scanning the 30 chunk totals) is faster.
 //
 // Scratch needs no clearing between calls: tile numbers and an epoch come
 // from one 64-bit atomic word {epoch:32 | next tile:32}, reset and advanced
