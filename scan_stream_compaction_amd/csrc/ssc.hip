@@ -1066,95 +1066,61 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // One tile (steps 1-5 above) with CUR holding the current chunk, NX the
     // next one in flight and, with three sets, FREE the registers of the chunk
     // staged one tile ago; the loop below rotates the register sets.
+    // Stages chunk CUR's survivors at their rank in this wavefront's LDS region
+    // (a partition: every element, the rejected ones after the survivors).
+#define SSC_STAGE(CUR)                                                                        \
+    {                                                                                         \
+            /* a partition gives every element a slot of its own, no branches:   */            \
+            /* survivors at their rank, the others after all survivors at a_cur + */            \
+            /* (index - rank), elements past rem included (they land past the     */            \
+            /* runs); compaction and selection stage the survivors only           */            \
+            uint32_t lead[S::kLoads];                                                         \
+            chunk_leads<S::kLoads, S::kPer>(fm_cur, lead);                                    \
+            /* (a selection stages each element's index instead of its value)    */            \
+            const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * S::kPer;        \
+            _Pragma("unroll") for (int j = 0; j < S::kLoads; ++j) {                           \
+                if constexpr (kPart) {                                                        \
+                    uint32_t r = lead[j];                                                     \
+                    const uint32_t rej =                                                      \
+                        a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);  \
+                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
+                        const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                \
+                        F::stage(s_stage[w], f ? r : rej + k - r, CUR, j, k);                 \
+                        r += f;                                                               \
+                    }                                                                         \
+                } else {                                                                      \
+                    /* a running LDS pointer that each element's flag advances; */           \
+                    /* the flag is opaque so that the test reuses the extracted */           \
+                    /* bit (else it is taken from the mask a second time)       */           \
+                    /* (a selection stages one 32-bit position per survivor)    */           \
+                    constexpr int kSlot = KIND == kSelectIndex ? 1 : F::kSlotWords;           \
+                    uint32_t *p = s_stage[w] + lead[j] * kSlot;                               \
+                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
+                        uint32_t f = __builtin_amdgcn_ubfe(fm_cur, j * S::kPer + k, 1);       \
+                        asm volatile("" : "+v"(f));                                           \
+                        if (f) {                                                              \
+                            if constexpr (KIND == kSelectIndex)                               \
+                                *p = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
+                            else                                                              \
+                                F::stage(p, 0, CUR, j, k);                                    \
+                        }                                                                     \
+                        p += f * kSlot;                                                       \
+                    }                                                                         \
+                }                                                                             \
+            }                                                                                 \
+    }
+
 #define SSC_TILE(CUR, NX, FREE)                                                               \
     {                                                                                         \
         int ln = lane;                                                                        \
         asm volatile("" : "+v"(ln));                                                          \
         if constexpr (kThree) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, FREE);             \
-        if constexpr (!kFlagFirst) {                                                          \
-            /* a partition gives every element a slot of its own, no branches:   */            \
-            /* survivors at their rank, the others after all survivors at a_cur + */            \
-            /* (index - rank), elements past rem included (they land past the     */            \
-            /* runs); compaction and selection stage the survivors only           */            \
-            uint32_t lead[S::kLoads];                                                         \
-            chunk_leads<S::kLoads, S::kPer>(fm_cur, lead);                                    \
-            /* (a selection stages each element's index instead of its value)    */            \
-            const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * S::kPer;        \
-            _Pragma("unroll") for (int j = 0; j < S::kLoads; ++j) {                           \
-                if constexpr (kPart) {                                                        \
-                    uint32_t r = lead[j];                                                     \
-                    const uint32_t rej =                                                      \
-                        a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);  \
-                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
-                        const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                \
-                        F::stage(s_stage[w], f ? r : rej + k - r, CUR, j, k);                 \
-                        r += f;                                                               \
-                    }                                                                         \
-                } else {                                                                      \
-                    /* a running LDS pointer that each element's flag advances; */           \
-                    /* the flag is opaque so that the test reuses the extracted */           \
-                    /* bit (else it is taken from the mask a second time)       */           \
-                    /* (a selection stages one 32-bit position per survivor)    */           \
-                    constexpr int kSlot = KIND == kSelectIndex ? 1 : F::kSlotWords;           \
-                    uint32_t *p = s_stage[w] + lead[j] * kSlot;                               \
-                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
-                        uint32_t f = __builtin_amdgcn_ubfe(fm_cur, j * S::kPer + k, 1);       \
-                        asm volatile("" : "+v"(f));                                           \
-                        if (f) {                                                              \
-                            if constexpr (KIND == kSelectIndex)                               \
-                                *p = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
-                            else                                                              \
-                                F::stage(p, 0, CUR, j, k);                                    \
-                        }                                                                     \
-                        p += f * kSlot;                                                       \
-                    }                                                                         \
-                }                                                                             \
-            }                                                                                 \
-        }                                                                                     \
+        if constexpr (!kFlagFirst) SSC_STAGE(CUR)                                             \
         if constexpr (!kThree) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, CUR);             \
         const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                     \
         rem_nxt = rem_of(nxt);                                                                \
         SSC_FLAG_AND_ARRIVE(NX, nxt, rem_nxt, fm_nxt, a_nxt, tri_n, ln)                       \
-        if constexpr (kFlagFirst) {                                                           \
-            /* a partition gives every element a slot of its own, no branches:   */            \
-            /* survivors at their rank, the others after all survivors at a_cur + */            \
-            /* (index - rank), elements past rem included (they land past the     */            \
-            /* runs); compaction and selection stage the survivors only           */            \
-            uint32_t lead[S::kLoads];                                                         \
-            chunk_leads<S::kLoads, S::kPer>(fm_cur, lead);                                    \
-            /* (a selection stages each element's index instead of its value)    */            \
-            const int32_t first = static_cast<int32_t>(chunk_of(tile)) + ln * S::kPer;        \
-            _Pragma("unroll") for (int j = 0; j < S::kLoads; ++j) {                           \
-                if constexpr (kPart) {                                                        \
-                    uint32_t r = lead[j];                                                     \
-                    const uint32_t rej =                                                      \
-                        a_cur + static_cast<uint32_t>(j * (kWave * S::kPer) + ln * S::kPer);  \
-                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
-                        const uint32_t f = (fm_cur >> (j * S::kPer + k)) & 1u;                \
-                        F::stage(s_stage[w], f ? r : rej + k - r, CUR, j, k);                 \
-                        r += f;                                                               \
-                    }                                                                         \
-                } else {                                                                      \
-                    /* a running LDS pointer that each element's flag advances; */           \
-                    /* the flag is opaque so that the test reuses the extracted */           \
-                    /* bit (else it is taken from the mask a second time)       */           \
-                    /* (a selection stages one 32-bit position per survivor)    */           \
-                    constexpr int kSlot = KIND == kSelectIndex ? 1 : F::kSlotWords;           \
-                    uint32_t *p = s_stage[w] + lead[j] * kSlot;                               \
-                    _Pragma("unroll") for (int k = 0; k < S::kPer; ++k) {                     \
-                        uint32_t f = __builtin_amdgcn_ubfe(fm_cur, j * S::kPer + k, 1);       \
-                        asm volatile("" : "+v"(f));                                           \
-                        if (f) {                                                              \
-                            if constexpr (KIND == kSelectIndex)                               \
-                                *p = static_cast<uint32_t>(first + (j * (kWave * S::kPer) + k)); \
-                            else                                                              \
-                                F::stage(p, 0, CUR, j, k);                                    \
-                        }                                                                     \
-                        p += f * kSlot;                                                       \
-                    }                                                                         \
-                }                                                                             \
-            }                                                                                 \
-        }                                                                                     \
+        if constexpr (kFlagFirst) SSC_STAGE(CUR)                                              \
         __syncthreads(); /* B1: this tile's base is known */                                  \
         /* the ranks' leads come from fm_cur after the barrier: computed before  */           \
         /* it, they stayed live across the next chunk's flags and the kernel     */           \
@@ -1214,6 +1180,7 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         }
     }
 #undef SSC_TILE
+#undef SSC_STAGE
 #undef SSC_FLAG_AND_ARRIVE
 }
 
