@@ -2620,6 +2620,21 @@ int dispatch_pred(int pred, bool vec, A... a) {
     }
 }
 
+// Workgroups for the radix driver's chained splits: the fewest that still
+// take the tiles in as many rounds as one per compute unit would, when that
+// is a few rounds. At 2^24 keys a split has 547 tiles, 2.1 rounds on 256
+// compute units; 183 workgroups of 3 tiles each leave no near-empty last
+// round (a 32-pass sort 1,105 -> 1,060 us). Other kinds and sizes keep one
+// workgroup per compute unit: the same grid measured mixed elsewhere (2^25
+// odd compaction 45.2 -> 42.8 us but the 2^25 int32 scan 49.3 -> 50.6, at
+// two rounds the 8,387,997-element partition 32.0 -> 34.9, at 35 rounds
+// selection by flag bytes 145.3 -> 147.6).
+uint32_t split_grid(uint32_t tiles, uint32_t slots) {
+    if (tiles <= slots) return tiles;
+    const uint32_t rounds = (tiles + slots - 1) / slots;
+    return rounds <= 8 ? (tiles + rounds - 1) / rounds : slots;
+}
+
 // One launch of the persistent kernel for element format F and kind KIND:
 // one workgroup per compute unit, at most one per tile.
 template <class F, int P, int KIND>
@@ -2629,7 +2644,7 @@ int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint3
     const uint32_t tiles = static_cast<uint32_t>((n + kTileElems - 1) / kTileElems);
     uint32_t slots = 0;
     SSC_TRY(compute_units(&slots));
-    const dim3 grid(tiles < slots ? tiles : slots);
+    const dim3 grid(KIND == kPartitionCached ? split_grid(tiles, slots) : (tiles < slots ? tiles : slots));
     hipLaunchKernelGGL((select_kernel<F, P, KIND>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
                        tiles, capacity, count, ranks, kept);
     return launched();
