@@ -273,9 +273,9 @@ def pipeline_rows(x, m: int, stream, steps: int, copy_us: float) -> dict:
 
 def hbm_rows(x, dev, steps: int, stream) -> dict:
     """The other 2^28 operations of the path, HBM-bound like the headline:
-    stable partition (a counting read, then the single pass) and the
-    exclusive scans of int32 and fp32 values, each checked before and after
-    its timed calls."""
+    stable partition (a counting read, then the single pass), the headline's
+    compaction with its ranks output, and the exclusive scans of int32 and
+    fp32 values, each checked before and after its timed calls."""
     import torch
 
     import scan_stream_compaction_amd as ssc
@@ -307,6 +307,20 @@ def hbm_rows(x, dev, steps: int, stream) -> dict:
     timed("partition_even_2p28", fn, 8 * n, ok, kept=k,
           note="algorithmic 8N; the counting pass before the single pass reads another 4N (12N moved)")
     del pwant
+    od = (x & 1) == 1
+    km = int(od.sum())
+    cwant = x[od]
+    f32 = od.to(torch.int32)
+    rwant = torch.cumsum(f32, 0, dtype=torch.int32) - f32  # the exclusive scan of the flags
+    del od, f32
+    rk = torch.empty_like(x)
+    fn = ssc.prepared(ssc.compact, x, "odd", out=out, count=cnt, ranks=rk, scratch=sc)
+    torch.cuda.synchronize()
+    ok = lambda: int(cnt.item()) == km and torch.equal(out[:km], cwant) and torch.equal(rk, rwant)
+    assert ok()
+    timed("compact_ranks_odd_2p28", fn, 8 * n + 4 * km, ok, kept=km,
+          note="the survivors and the ranks (the exclusive scan of the flags) written: 4N + 4K + 4N")
+    del cwant, rwant, rk
     c = torch.cumsum(x.to(torch.int64), 0)
     swant = ((c - x.to(torch.int64)) & 0xFFFFFFFF).to(torch.int64)
     del c
