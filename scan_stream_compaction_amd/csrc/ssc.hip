@@ -931,7 +931,7 @@ constexpr int sel_poll_sleep() {
 
 // F is the element format (what a chunk holds and how survivors are staged
 // and written); partition and ranks are defined for 32-bit elements.
-template <class F, int P, int KIND>
+template <class F, int P, int KIND, bool DENSE = false>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(
     SelArgs a, int64_t n, PredArgs pr, void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
@@ -958,7 +958,15 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // 261.4 -> 262.0, and flag-byte compaction, at the register cap, 309 ->
     // 361, keep the other order).
     constexpr bool kFlagFirst = kThree && F::kFlagFirst;
-    constexpr bool kLbFast = kThree && P != 5;  // look-back without the predecessor poll
+    // DENSE (chosen on the host for MOD_LT(m, s) expected to keep at least
+    // three quarters of uniform input, 4s >= 3m): the look-back goes straight
+    // to its window and the tile after next's loads leave after the next
+    // chunk's arrival. At 99% kept the write stream dominates and both help
+    // (365.6 -> 359.3 us at 2^28); at 50% the late loads cost 11.5 us, and
+    // below about half kept the predecessor poll pays off. Either form is
+    // correct for any input; only the speed depends on the fraction kept.
+    constexpr bool kDense = DENSE && kThree && kFlagFirst;
+    constexpr bool kLbFast = kThree && (P != 5 || kDense);  // look-back without the predecessor poll
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
     const int w = static_cast<int>(uniform(threadIdx.x / kWave));
@@ -1114,12 +1122,13 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     {                                                                                         \
         int ln = lane;                                                                        \
         asm volatile("" : "+v"(ln));                                                          \
-        if constexpr (kThree) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, FREE);             \
+        if constexpr (kThree && !kDense) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, FREE);  \
         if constexpr (!kFlagFirst) SSC_STAGE(CUR)                                             \
         if constexpr (!kThree) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, CUR);             \
         const uint32_t tri_n = tri == 2u ? 0u : tri + 1u;                                     \
         rem_nxt = rem_of(nxt);                                                                \
         SSC_FLAG_AND_ARRIVE(NX, nxt, rem_nxt, fm_nxt, a_nxt, tri_n, ln)                       \
+        if constexpr (kDense) F::load(a, chunk_of(nxt2), rem_of(nxt2), ln, FREE);             \
         if constexpr (kFlagFirst) SSC_STAGE(CUR)                                              \
         __syncthreads(); /* B1: this tile's base is known */                                  \
         /* the ranks' leads come from fm_cur after the barrier: computed before  */           \
@@ -2637,7 +2646,7 @@ uint32_t split_grid(uint32_t tiles, uint32_t slots) {
 
 // One launch of the persistent kernel for element format F and kind KIND:
 // one workgroup per compute unit, at most one per tile.
-template <class F, int P, int KIND>
+template <class F, int P, int KIND, bool DENSE = false>
 int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint32_t capacity,
                   int32_t *count, int32_t *ranks, const int32_t *kept, hipStream_t s) {
     constexpr int64_t kTileElems = F::Shape::kTileElems;
@@ -2645,9 +2654,19 @@ int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint3
     uint32_t slots = 0;
     SSC_TRY(compute_units(&slots));
     const dim3 grid(KIND == kPartitionCached ? split_grid(tiles, slots) : (tiles < slots ? tiles : slots));
-    hipLaunchKernelGGL((select_kernel<F, P, KIND>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
+    hipLaunchKernelGGL((select_kernel<F, P, KIND, DENSE>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
                        tiles, capacity, count, ranks, kept);
     return launched();
+}
+
+// Or-ed into a kind: a MOD_LT(m, s) compaction or selection expected to keep
+// at least three quarters of uniform input (4s >= 3m) takes the dense form of
+// the kernel (see DENSE in select_kernel). Only the speed depends on it.
+constexpr int kDense = 0x100;
+inline int with_density(int kind, int pred, int32_t pa, int32_t pb) {
+    const bool dense = pred == SSC_PRED_MOD_LT && (kind == kCompact || kind == kSelectIndex) &&
+                       4 * static_cast<int64_t>(pb) >= 3 * static_cast<int64_t>(pa);
+    return dense ? (kind | kDense) : kind;
 }
 
 // 32-bit elements, predicate P on the element.
@@ -2658,16 +2677,25 @@ struct LaunchSelect {
                    const int32_t *kept, hipStream_t s) {
         using F = FmtB32<VEC>;
         const SelArgs a{in, nullptr, out, nullptr};
-        switch (kind) {
+        const bool dense = (kind & kDense) != 0;
+        switch (kind & ~kDense) {
         case kPartition:
             return launch_select<F, P, kPartition>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         case kCompactRanks:
             return launch_select<F, P, kCompactRanks>(a, n, pr, scratch, capacity, count, ranks,
                                                       kept, s);
         case kSelectIndex:
+            if constexpr (P == 5)
+                if (dense)
+                    return launch_select<F, P, kSelectIndex, true>(a, n, pr, scratch, capacity, count,
+                                                                   ranks, kept, s);
             return launch_select<F, P, kSelectIndex>(a, n, pr, scratch, capacity, count, ranks,
                                                      kept, s);
         default:
+            if constexpr (P == 5)
+                if (dense)
+                    return launch_select<F, P, kCompact, true>(a, n, pr, scratch, capacity, count,
+                                                               ranks, kept, s);
             return launch_select<F, P, kCompact>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         }
     }
@@ -2886,7 +2914,7 @@ int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t p
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect, F32>(pred, vec, ranks ? kCompactRanks : kCompact, in, out, n,
+    return dispatch_pred<LaunchSelect, F32>(pred, vec, with_density(ranks ? kCompactRanks : kCompact, pred, pa, pb), in, out, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count, ranks,
                                        static_cast<const int32_t *>(nullptr), s);
@@ -2910,7 +2938,7 @@ int select_index_impl(const int32_t *in, int32_t *idx, int64_t n, int pred, int3
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
-    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), kSelectIndex, in, idx, n,
+    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), with_density(kSelectIndex, pred, pa, pb), in, idx, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count,
                                        static_cast<int32_t *>(nullptr),
