@@ -468,7 +468,35 @@ def test_mod_lt_at_residue_edges(m, s):
     reps = -(-(T + 97) // x.size)  # several tiles, a ragged tail
     x = np.tile(x, reps)[: T + 97 + x.size]
     check_compact(x, "mod_lt", m, s)
+    check_compact(x, "mod_lt", m, s, ranks=False)
     check_select_index(x, "mod_lt", m, s)
+
+
+# MOD_LT(m, s) takes one of two kernel forms by the fraction s/m it would keep
+# of uniform input; each form must be right whatever the input keeps.
+MOD_FORM_CASES = [(m, s, keep) for m, s in [(100, 1), (100, 50), (100, 75), (100, 99), (4, 3), (1, 1)]
+                  for keep in ("none", "all", "runs") if not (s >= m and keep == "none")]
+
+
+@pytest.mark.parametrize("m,s,keep", MOD_FORM_CASES)
+def test_mod_lt_forms_whatever_the_input_keeps(m, s, keep):
+    n = 3 * T + 4097
+    # values q*m + r have residue r (0 <= r < m) for every quotient q
+    q = wl.full_int32(0x5EED0D00 + m + s, n).astype(np.int64) // max(m, 2)
+    kept_r, dropped_r = 0, min(s, m - 1)  # dropped_r is kept too when s >= m
+    if keep == "none":
+        r = np.full(n, dropped_r)
+    elif keep == "all":
+        r = np.full(n, kept_r)
+    else:  # alternating runs of 1 to 5000 kept and dropped values
+        rng = np.random.default_rng(0x5EED0D80 + m + s)
+        lens = rng.integers(1, 5001, size=n // 2 + 1)
+        sel = np.repeat(np.arange(lens.size) % 2, lens)[:n]
+        r = np.where(sel == 0, kept_r, dropped_r)
+    x = np.clip(q * m + r, -(1 << 31), (1 << 31) - 1).astype(np.int32)
+    kept = check_compact(x, "mod_lt", m, s, ranks=False)
+    check_select_index(x, "mod_lt", m, s)
+    say(f"  MOD_LT({m}, {s}) {keep}: kept {kept} of {n}")
 
 
 def f32_input(seed: int, n: int) -> np.ndarray:
