@@ -677,7 +677,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "ssc::select_kernel<ssc::FmtB32<true>, 1, 0, false> (odd, 128-bit, compaction)",
+            "kernel": "ssc::select_kernel<ssc::FmtB32<true>, 1, 0, 0> (odd, 128-bit, compaction)",
             "kernel_us": round(kernel_ms * 1e3, 2),
         },
         "extra": extra,

@@ -484,7 +484,13 @@ __device__ __forceinline__ void load_b32x4(const int32_t *in, int64_t chunk, uin
 // whole lines' policy: a run the library itself reads next (the radix
 // driver's chained partitions) takes the default policy, which keeps it in
 // the caches (2^24 keys: 1,265 us against 1,360 us with nontemporal lines).
-template <int C, int POL = kNT>
+// DYN: one store per whole 64-word piece of the run instead of the fixed
+// C / 64. The dropped stores of short runs still pass through the memory
+// pipeline (2^28 MOD_LT(100, 1): 199.7 -> 194.2 us, 5% kept 216.8 -> 210.7),
+// but a store count the compiler cannot see makes it wait for the stores
+// before the next chunk's flags (10% kept 215.3 -> 217.5, 25% 225.5 ->
+// 249.4, the headline 266.3 -> 282.3), so only the sparse form takes it.
+template <int C, int POL = kNT, bool DYN = false>
 __device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, uint32_t at,
                                            uint32_t len, int64_t n, int lane) {
     len = uniform(len);
@@ -501,9 +507,14 @@ __device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, u
     const __amdgpu_buffer_rsrc_t rb =
         buffer_rsrc(dst + head, full * static_cast<uint32_t>(kWave) * 4u);
     const uint32_t *src = run + head + lane;
+    if constexpr (DYN) {
+        for (uint32_t i = 0; i < full; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, POL);
+    } else {
 #pragma unroll
-    for (int i = 0; i < C / kWave; ++i)
-        __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, POL);
+        for (int i = 0; i < C / kWave; ++i)
+            __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, POL);
+    }
     __builtin_amdgcn_raw_buffer_store_b32(run[tail_at + lane],
                                           buffer_rsrc(dst + tail_at, (len - tail_at) * 4u), voff,
                                           0, 0);
@@ -684,10 +695,10 @@ struct FmtB32 {
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
         region[slot] = static_cast<uint32_t>(r.v[j][k]);
     }
-    template <int POL = kNT>
+    template <int POL = kNT, bool DYN = false>
     __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
                                  uint32_t len, int64_t n, int lane) {
-        stream_run<Shape::kChunk, POL>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+        stream_run<Shape::kChunk, POL, DYN>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
     }
 };
 
@@ -924,6 +935,11 @@ constexpr bool three_sets() {
 // polls at s_sleep 32; with two it first waits on its predecessor and polls
 // at s_sleep 16 (each measured best for its pipeline; MOD_LT with three sets
 // polls as with two: 50% kept 273.5 -> 269.5, 1% 229.4 -> 225.9).
+// Forms of the persistent compaction kernel (FORM in select_kernel).
+constexpr int kFormDefault = 0;
+constexpr int kFormDense = 1;
+constexpr int kFormSparse = 2;
+
 template <bool THREE>
 constexpr int sel_poll_sleep() {
     return THREE ? 32 : 16;
@@ -931,7 +947,7 @@ constexpr int sel_poll_sleep() {
 
 // F is the element format (what a chunk holds and how survivors are staged
 // and written); partition and ranks are defined for 32-bit elements.
-template <class F, int P, int KIND, bool DENSE = false>
+template <class F, int P, int KIND, int FORM = kFormDefault>
 __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void select_kernel(
     SelArgs a, int64_t n, PredArgs pr, void *scratch, uint32_t num_tiles, uint32_t capacity,
     int32_t *__restrict__ count, int32_t *__restrict__ ranks,
@@ -958,14 +974,18 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // 261.4 -> 262.0, and flag-byte compaction, at the register cap, 309 ->
     // 361, keep the other order).
     constexpr bool kFlagFirst = kThree && F::kFlagFirst;
-    // DENSE (chosen on the host for MOD_LT(m, s) expected to keep at least
-    // three quarters of uniform input, 4s >= 3m): the look-back goes straight
+    // The form, chosen on the host for MOD_LT(m, s) from the fraction s/m it
+    // keeps of uniform input. Dense (4s >= 3m): the look-back goes straight
     // to its window and the tile after next's loads leave after the next
     // chunk's arrival. At 99% kept the write stream dominates and both help
     // (365.6 -> 359.3 us at 2^28); at 50% the late loads cost 11.5 us, and
-    // below about half kept the predecessor poll pays off. Either form is
-    // correct for any input; only the speed depends on the fraction kept.
-    constexpr bool kDense = DENSE && kThree && kFlagFirst;
+    // below about half kept the predecessor poll pays off. Sparse (16s <= m):
+    // runs are written with as many stores as they have 64-word pieces (DYN
+    // in stream_run). Every form is correct for any input; only the speed
+    // depends on the fraction kept.
+    constexpr bool kDense = FORM == kFormDense && kThree && kFlagFirst;
+    constexpr bool kSparse = FORM == kFormSparse && (KIND == kCompact || KIND == kSelectIndex) &&
+                             __is_same(F, FmtB32<F::kVec>);
     constexpr bool kLbFast = kThree && (P != 5 || kDense);  // look-back without the predecessor poll
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
@@ -1140,7 +1160,10 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         const int64_t chunk_now = chunk_of(tile);                                             \
         const uint32_t seg = base + uniform(s_pre[tri][w]); /* kept before this chunk */      \
         if constexpr (KIND == kSelectIndex)                                                   \
-            stream_run<S::kChunk>(s_stage[w], static_cast<uint32_t *>(a.out), seg, a_cur, n, ln); \
+            stream_run<S::kChunk, kNT, kSparse>(s_stage[w], static_cast<uint32_t *>(a.out), seg, \
+                                                a_cur, n, ln);                                \
+        else if constexpr (kSparse)                                                           \
+            F::template write<kRunPol, true>(s_stage[w], a, seg, a_cur, n, ln);               \
         else                                                                                  \
             F::template write<kRunPol>(s_stage[w], a, seg, a_cur, n, ln);                     \
         if constexpr (kPart) {                                                                \
@@ -2646,7 +2669,7 @@ uint32_t split_grid(uint32_t tiles, uint32_t slots) {
 
 // One launch of the persistent kernel for element format F and kind KIND:
 // one workgroup per compute unit, at most one per tile.
-template <class F, int P, int KIND, bool DENSE = false>
+template <class F, int P, int KIND, int FORM = kFormDefault>
 int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint32_t capacity,
                   int32_t *count, int32_t *ranks, const int32_t *kept, hipStream_t s) {
     constexpr int64_t kTileElems = F::Shape::kTileElems;
@@ -2654,19 +2677,22 @@ int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint3
     uint32_t slots = 0;
     SSC_TRY(compute_units(&slots));
     const dim3 grid(KIND == kPartitionCached ? split_grid(tiles, slots) : (tiles < slots ? tiles : slots));
-    hipLaunchKernelGGL((select_kernel<F, P, KIND, DENSE>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
+    hipLaunchKernelGGL((select_kernel<F, P, KIND, FORM>), grid, dim3(kLbBlock), 0, s, a, n, pr, scratch,
                        tiles, capacity, count, ranks, kept);
     return launched();
 }
 
-// Or-ed into a kind: a MOD_LT(m, s) compaction or selection expected to keep
-// at least three quarters of uniform input (4s >= 3m) takes the dense form of
-// the kernel (see DENSE in select_kernel). Only the speed depends on it.
-constexpr int kDense = 0x100;
+// Or-ed into a kind: a MOD_LT(m, s) compaction or selection takes the dense
+// form of the kernel when it is expected to keep at least three quarters of
+// uniform input (4s >= 3m), the sparse form when at most a sixteenth (16s <=
+// m); see FORM in select_kernel. Only the speed depends on it.
+constexpr int kDenseKind = 0x100;
+constexpr int kSparseKind = 0x200;
 inline int with_density(int kind, int pred, int32_t pa, int32_t pb) {
-    const bool dense = pred == SSC_PRED_MOD_LT && (kind == kCompact || kind == kSelectIndex) &&
-                       4 * static_cast<int64_t>(pb) >= 3 * static_cast<int64_t>(pa);
-    return dense ? (kind | kDense) : kind;
+    if (pred != SSC_PRED_MOD_LT || (kind != kCompact && kind != kSelectIndex)) return kind;
+    if (4 * static_cast<int64_t>(pb) >= 3 * static_cast<int64_t>(pa)) return kind | kDenseKind;
+    if (16 * static_cast<int64_t>(pb) <= static_cast<int64_t>(pa)) return kind | kSparseKind;
+    return kind;
 }
 
 // 32-bit elements, predicate P on the element.
@@ -2677,25 +2703,35 @@ struct LaunchSelect {
                    const int32_t *kept, hipStream_t s) {
         using F = FmtB32<VEC>;
         const SelArgs a{in, nullptr, out, nullptr};
-        const bool dense = (kind & kDense) != 0;
-        switch (kind & ~kDense) {
+        const int form = (kind & kDenseKind)    ? kFormDense
+                         : (kind & kSparseKind) ? kFormSparse
+                                                : kFormDefault;
+        switch (kind & ~(kDenseKind | kSparseKind)) {
         case kPartition:
             return launch_select<F, P, kPartition>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         case kCompactRanks:
             return launch_select<F, P, kCompactRanks>(a, n, pr, scratch, capacity, count, ranks,
                                                       kept, s);
         case kSelectIndex:
-            if constexpr (P == 5)
-                if (dense)
-                    return launch_select<F, P, kSelectIndex, true>(a, n, pr, scratch, capacity, count,
-                                                                   ranks, kept, s);
+            if constexpr (P == 5) {
+                if (form == kFormDense)
+                    return launch_select<F, P, kSelectIndex, kFormDense>(a, n, pr, scratch, capacity,
+                                                                         count, ranks, kept, s);
+                if (form == kFormSparse)
+                    return launch_select<F, P, kSelectIndex, kFormSparse>(a, n, pr, scratch, capacity,
+                                                                          count, ranks, kept, s);
+            }
             return launch_select<F, P, kSelectIndex>(a, n, pr, scratch, capacity, count, ranks,
                                                      kept, s);
         default:
-            if constexpr (P == 5)
-                if (dense)
-                    return launch_select<F, P, kCompact, true>(a, n, pr, scratch, capacity, count,
-                                                               ranks, kept, s);
+            if constexpr (P == 5) {
+                if (form == kFormDense)
+                    return launch_select<F, P, kCompact, kFormDense>(a, n, pr, scratch, capacity,
+                                                                     count, ranks, kept, s);
+                if (form == kFormSparse)
+                    return launch_select<F, P, kCompact, kFormSparse>(a, n, pr, scratch, capacity,
+                                                                      count, ranks, kept, s);
+            }
             return launch_select<F, P, kCompact>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         }
     }
@@ -2914,7 +2950,8 @@ int compact_impl(const int32_t *in, int32_t *out, int64_t n, int pred, int32_t p
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
     const bool vec = aligned(in, 16) && (ranks == nullptr || aligned(ranks, 16));
-    return dispatch_pred<LaunchSelect, F32>(pred, vec, with_density(ranks ? kCompactRanks : kCompact, pred, pa, pb), in, out, n,
+    const int kind = with_density(ranks ? kCompactRanks : kCompact, pred, pa, pb);
+    return dispatch_pred<LaunchSelect, F32>(pred, vec, kind, in, out, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count, ranks,
                                        static_cast<const int32_t *>(nullptr), s);
@@ -2938,7 +2975,8 @@ int select_index_impl(const int32_t *in, int32_t *idx, int64_t n, int pred, int3
         return SSC_ERR_ALIAS;
     SSC_TRY(check_device());
     if (n == 0) return clear_words(count, 1, s);
-    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), with_density(kSelectIndex, pred, pa, pb), in, idx, n,
+    const int kind = with_density(kSelectIndex, pred, pa, pb);
+    return dispatch_pred<LaunchSelect, F32>(pred, aligned(in, 16), kind, in, idx, n,
                                        make_pred_args(pred, pa, pb), scratch,
                                        capacity_of(scratch_bytes), count,
                                        static_cast<int32_t *>(nullptr),

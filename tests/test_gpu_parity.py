@@ -472,9 +472,11 @@ def test_mod_lt_at_residue_edges(m, s):
     check_select_index(x, "mod_lt", m, s)
 
 
-# MOD_LT(m, s) takes one of two kernel forms by the fraction s/m it would keep
-# of uniform input; each form must be right whatever the input keeps.
-MOD_FORM_CASES = [(m, s, keep) for m, s in [(100, 1), (100, 50), (100, 75), (100, 99), (4, 3), (1, 1)]
+# MOD_LT(m, s) takes one of three kernel forms by the fraction s/m it would
+# keep of uniform input (sparse up to 1/16, dense from 3/4); each form must be
+# right whatever the input keeps.
+MOD_FORM_CASES = [(m, s, keep) for m, s in [(100, 1), (100, 6), (16, 1), (100, 7), (100, 50),
+                                            (100, 75), (100, 99), (4, 3), (1, 1)]
                   for keep in ("none", "all", "runs") if not (s >= m and keep == "none")]
 
 
