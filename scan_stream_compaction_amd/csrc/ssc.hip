@@ -484,13 +484,19 @@ __device__ __forceinline__ void load_b32x4(const int32_t *in, int64_t chunk, uin
 // whole lines' policy: a run the library itself reads next (the radix
 // driver's chained partitions) takes the default policy, which keeps it in
 // the caches (2^24 keys: 1,265 us against 1,360 us with nontemporal lines).
-// DYN: one store per whole 64-word piece of the run instead of the fixed
-// C / 64. The dropped stores of short runs still pass through the memory
-// pipeline (2^28 MOD_LT(100, 1): 199.7 -> 194.2 us, 5% kept 216.8 -> 210.7),
-// but a store count the compiler cannot see makes it wait for the stores
-// before the next chunk's flags (10% kept 215.3 -> 217.5, 25% 225.5 ->
-// 249.4, the headline 266.3 -> 282.3), so only the sparse form takes it.
-template <int C, int POL = kNT, bool DYN = false>
+// HALF: the second half of the C / 64 piece stores only for a run longer
+// than half a chunk. Stores past the run's end are dropped by the buffer
+// resource, but each still passes through the memory pipeline, and at low
+// selectivity nearly all are such. Skipping all of them (one store per
+// piece the run has) gained 5.5 us at 1% kept, but the compiler cannot
+// count such stores, so its wait for the next chunk's data also waits for
+// them (10% kept 215.3 -> 217.5, 25% 225.5 -> 249.4, the headline 266.3 ->
+// 282.3). With half always issued the wait covers at most half of them
+// (2^28 MOD_LT(100, s): 1% kept 199.7 -> 195.1 us, 5% 216.8 -> 208.8, 10%
+// 215.7 -> 207.8, 50% 267.0 -> 264.1; the headline 265.6 -> 265.3). Key-value
+// pairs (266.3 -> 270.9) and partitions (522.6 -> 525.2), which write two
+// runs a chunk, issue them all.
+template <int C, int POL = kNT, bool HALF = false>
 __device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, uint32_t at,
                                            uint32_t len, int64_t n, int lane) {
     len = uniform(len);
@@ -507,12 +513,13 @@ __device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, u
     const __amdgpu_buffer_rsrc_t rb =
         buffer_rsrc(dst + head, full * static_cast<uint32_t>(kWave) * 4u);
     const uint32_t *src = run + head + lane;
-    if constexpr (DYN) {
-        for (uint32_t i = 0; i < full; ++i)
-            __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, POL);
-    } else {
+    constexpr int kFirst = HALF ? C / kWave / 2 : C / kWave;
 #pragma unroll
-        for (int i = 0; i < C / kWave; ++i)
+    for (int i = 0; i < kFirst; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, POL);
+    if (kFirst < C / kWave && full > static_cast<uint32_t>(kFirst)) {
+#pragma unroll
+        for (int i = kFirst; i < C / kWave; ++i)
             __builtin_amdgcn_raw_buffer_store_b32(src[i * kWave], rb, voff + i * (kWave * 4), 0, POL);
     }
     __builtin_amdgcn_raw_buffer_store_b32(run[tail_at + lane],
@@ -695,10 +702,10 @@ struct FmtB32 {
     __device__ static void stage(uint32_t *region, uint32_t slot, const Regs &r, int j, int k) {
         region[slot] = static_cast<uint32_t>(r.v[j][k]);
     }
-    template <int POL = kNT, bool DYN = false>
+    template <int POL = kNT, bool HALF = false>
     __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
                                  uint32_t len, int64_t n, int lane) {
-        stream_run<Shape::kChunk, POL, DYN>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+        stream_run<Shape::kChunk, POL, HALF>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
     }
 };
 
@@ -938,7 +945,6 @@ constexpr bool three_sets() {
 // Forms of the persistent compaction kernel (FORM in select_kernel).
 constexpr int kFormDefault = 0;
 constexpr int kFormDense = 1;
-constexpr int kFormSparse = 2;
 
 template <bool THREE>
 constexpr int sel_poll_sleep() {
@@ -979,13 +985,11 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
     // to its window and the tile after next's loads leave after the next
     // chunk's arrival. At 99% kept the write stream dominates and both help
     // (365.6 -> 359.3 us at 2^28); at 50% the late loads cost 11.5 us, and
-    // below about half kept the predecessor poll pays off. Sparse (16s <= m):
-    // runs are written with as many stores as they have 64-word pieces (DYN
-    // in stream_run). Every form is correct for any input; only the speed
-    // depends on the fraction kept.
+    // below about half kept the predecessor poll pays off. Either form is
+    // correct for any input; only the speed depends on the fraction kept.
     constexpr bool kDense = FORM == kFormDense && kThree && kFlagFirst;
-    constexpr bool kSparse = FORM == kFormSparse && (KIND == kCompact || KIND == kSelectIndex) &&
-                             __is_same(F, FmtB32<F::kVec>);
+    // one 32-bit run a chunk: its second half of stores only when needed
+    constexpr bool kHalf = (KIND == kCompact || KIND == kSelectIndex) && __is_same(F, FmtB32<F::kVec>);
     constexpr bool kLbFast = kThree && (P != 5 || kDense);  // look-back without the predecessor poll
     const ScratchView sv = view(scratch);
     const int lane = lane_id();
@@ -1160,9 +1164,9 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
         const int64_t chunk_now = chunk_of(tile);                                             \
         const uint32_t seg = base + uniform(s_pre[tri][w]); /* kept before this chunk */      \
         if constexpr (KIND == kSelectIndex)                                                   \
-            stream_run<S::kChunk, kNT, kSparse>(s_stage[w], static_cast<uint32_t *>(a.out), seg, \
-                                                a_cur, n, ln);                                \
-        else if constexpr (kSparse)                                                           \
+            stream_run<S::kChunk, kNT, kHalf>(s_stage[w], static_cast<uint32_t *>(a.out), seg,  \
+                                              a_cur, n, ln);                                  \
+        else if constexpr (kHalf)                                                             \
             F::template write<kRunPol, true>(s_stage[w], a, seg, a_cur, n, ln);               \
         else                                                                                  \
             F::template write<kRunPol>(s_stage[w], a, seg, a_cur, n, ln);                     \
@@ -2684,15 +2688,13 @@ int launch_select(const SelArgs &a, int64_t n, PredArgs pr, void *scratch, uint3
 
 // Or-ed into a kind: a MOD_LT(m, s) compaction or selection takes the dense
 // form of the kernel when it is expected to keep at least three quarters of
-// uniform input (4s >= 3m), the sparse form when at most a sixteenth (16s <=
-// m); see FORM in select_kernel. Only the speed depends on it.
+// uniform input (4s >= 3m); see FORM in select_kernel. Only the speed
+// depends on it.
 constexpr int kDenseKind = 0x100;
-constexpr int kSparseKind = 0x200;
 inline int with_density(int kind, int pred, int32_t pa, int32_t pb) {
-    if (pred != SSC_PRED_MOD_LT || (kind != kCompact && kind != kSelectIndex)) return kind;
-    if (4 * static_cast<int64_t>(pb) >= 3 * static_cast<int64_t>(pa)) return kind | kDenseKind;
-    if (16 * static_cast<int64_t>(pb) <= static_cast<int64_t>(pa)) return kind | kSparseKind;
-    return kind;
+    const bool dense = pred == SSC_PRED_MOD_LT && (kind == kCompact || kind == kSelectIndex) &&
+                       4 * static_cast<int64_t>(pb) >= 3 * static_cast<int64_t>(pa);
+    return dense ? (kind | kDenseKind) : kind;
 }
 
 // 32-bit elements, predicate P on the element.
@@ -2703,35 +2705,25 @@ struct LaunchSelect {
                    const int32_t *kept, hipStream_t s) {
         using F = FmtB32<VEC>;
         const SelArgs a{in, nullptr, out, nullptr};
-        const int form = (kind & kDenseKind)    ? kFormDense
-                         : (kind & kSparseKind) ? kFormSparse
-                                                : kFormDefault;
-        switch (kind & ~(kDenseKind | kSparseKind)) {
+        const bool dense = (kind & kDenseKind) != 0;
+        switch (kind & ~kDenseKind) {
         case kPartition:
             return launch_select<F, P, kPartition>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         case kCompactRanks:
             return launch_select<F, P, kCompactRanks>(a, n, pr, scratch, capacity, count, ranks,
                                                       kept, s);
         case kSelectIndex:
-            if constexpr (P == 5) {
-                if (form == kFormDense)
+            if constexpr (P == 5)
+                if (dense)
                     return launch_select<F, P, kSelectIndex, kFormDense>(a, n, pr, scratch, capacity,
                                                                          count, ranks, kept, s);
-                if (form == kFormSparse)
-                    return launch_select<F, P, kSelectIndex, kFormSparse>(a, n, pr, scratch, capacity,
-                                                                          count, ranks, kept, s);
-            }
             return launch_select<F, P, kSelectIndex>(a, n, pr, scratch, capacity, count, ranks,
                                                      kept, s);
         default:
-            if constexpr (P == 5) {
-                if (form == kFormDense)
+            if constexpr (P == 5)
+                if (dense)
                     return launch_select<F, P, kCompact, kFormDense>(a, n, pr, scratch, capacity,
                                                                      count, ranks, kept, s);
-                if (form == kFormSparse)
-                    return launch_select<F, P, kCompact, kFormSparse>(a, n, pr, scratch, capacity,
-                                                                      count, ranks, kept, s);
-            }
             return launch_select<F, P, kCompact>(a, n, pr, scratch, capacity, count, ranks, kept, s);
         }
     }

@@ -472,9 +472,10 @@ def test_mod_lt_at_residue_edges(m, s):
     check_select_index(x, "mod_lt", m, s)
 
 
-# MOD_LT(m, s) takes one of three kernel forms by the fraction s/m it would
-# keep of uniform input (sparse up to 1/16, dense from 3/4); each form must be
-# right whatever the input keeps.
+# MOD_LT(m, s) takes one of two kernel forms by the fraction s/m it would keep
+# of uniform input (dense from 3/4); each form must be right whatever the
+# input keeps, and so must the run writes, whose second half of stores is
+# issued only for runs longer than half a chunk.
 MOD_FORM_CASES = [(m, s, keep) for m, s in [(100, 1), (100, 6), (16, 1), (100, 7), (100, 50),
                                             (100, 75), (100, 99), (4, 3), (1, 1)]
                   for keep in ("none", "all", "runs") if not (s >= m and keep == "none")]
@@ -499,6 +500,24 @@ def test_mod_lt_forms_whatever_the_input_keeps(m, s, keep):
     kept = check_compact(x, "mod_lt", m, s, ranks=False)
     check_select_index(x, "mod_lt", m, s)
     say(f"  MOD_LT({m}, {s}) {keep}: kept {kept} of {n}")
+
+
+def test_runs_of_every_length_within_a_chunk():
+    """Each 2048-element wavefront chunk keeps its first k elements, k running
+    over 0..2048 in a scattered order, so every run length meets every
+    alignment of its start in the output (the run writes' head, whole 64-word
+    pieces, the optional second half of them and the tail)."""
+    chunks = 160
+    x = wl.full_int32(0x5EED0E00, chunks * C2).astype(np.int64) & ~1  # all even
+    for c in range(chunks):
+        k = (c * 613 + 1000) % (C2 + 1)
+        x[c * C2: c * C2 + k] |= 1
+    x = x.astype(np.int32)
+    for n in (x.size, x.size - 777):
+        kept = check_compact(x[:n], "odd", ranks=False)
+        check_select_index(x[:n], "odd")
+        check_compact(x[:n], "odd")
+        say(f"  n={n}: kept {kept}")
 
 
 def f32_input(seed: int, n: int) -> np.ndarray:
