@@ -493,9 +493,11 @@ __device__ __forceinline__ void load_b32x4(const int32_t *in, int64_t chunk, uin
 // them (10% kept 215.3 -> 217.5, 25% 225.5 -> 249.4, the headline 266.3 ->
 // 282.3). With half always issued the wait covers at most half of them
 // (2^28 MOD_LT(100, s): 1% kept 199.7 -> 195.1 us, 5% 216.8 -> 208.8, 10%
-// 215.7 -> 207.8, 50% 267.0 -> 264.1; the headline 265.6 -> 265.3). Key-value
-// pairs (266.3 -> 270.9) and partitions (522.6 -> 525.2), which write two
-// runs a chunk, issue them all.
+// 215.7 -> 207.8, 50% 267.0 -> 264.1; the headline 265.6 -> 265.3; flag
+// selection 144.3 -> 141.4, flag-byte compaction 310.8 -> 309.0, int64
+// 267.7 -> 266.8). Key-value pairs (266.3 -> 270.9) and partitions (522.6 ->
+// 525.2), which write two runs a chunk, issue them all, and so does
+// compaction with ranks (464.9 -> 464.7, no gain).
 template <int C, int POL = kNT, bool HALF = false>
 __device__ __forceinline__ void stream_run(const uint32_t *run, uint32_t *out, uint32_t at,
                                            uint32_t len, int64_t n, int lane) {
@@ -752,7 +754,8 @@ struct FmtFlags {
     template <int POL = kNT>
     __device__ static void write(const uint32_t *region, const SelArgs &a, uint32_t at,
                                  uint32_t len, int64_t n, int lane) {
-        stream_run<Shape::kChunk, POL>(region, static_cast<uint32_t *>(a.out), at, len, n, lane);
+        stream_run<Shape::kChunk, POL, true>(region, static_cast<uint32_t *>(a.out), at, len, n,
+                                             lane);
     }
 };
 
@@ -866,7 +869,7 @@ struct FmtB64 {
         // (512 bytes per instruction) measured slower at 2^27 int64: 272.9 ->
         // 266.7 us with 50% kept, 374.7 -> 366.6 us with all kept. 2 * at
         // stays below 2^32 for every n the calls accept.
-        stream_run<2 * Shape::kChunk, POL>(region, static_cast<uint32_t *>(a.out), 2u * at,
+        stream_run<2 * Shape::kChunk, POL, true>(region, static_cast<uint32_t *>(a.out), 2u * at,
                                            2u * len, 2 * n, lane);
     }
 };
@@ -1417,7 +1420,8 @@ __global__ __launch_bounds__(kLbBlock) __attribute__((amdgpu_waves_per_eu(4, 4))
                 r1 += f1;
             }
             const uint32_t len = t0 + (last >> 16);
-            stream_run<kStageWords>(s_stage[w], reinterpret_cast<uint32_t *>(idx), seg + done, len, n, ln);
+            stream_run<kStageWords, kNT, true>(s_stage[w], reinterpret_cast<uint32_t *>(idx), seg + done,
+                                               len, n, ln);
             done += len;
         }
     };
